@@ -1,0 +1,187 @@
+"""Ternary-weight linear layer for MI355X (gfx950): thin binding over libternary.so.
+
+    y = x @ (q * s)^T,  q in {-1, 0, +1} packed 4 codes per byte (2 bits each,
+    00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0, first weight in the lowest bits),
+    s an fp16 scale per output channel or per 128 consecutive K weights.
+
+The format is the one stated on trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战"
+(§3.1) and m.nxbn.cn/news/169761 (§2.2); the layer's interface (x, weight,
+scale) -> y follows m.nxbn.cn/news/169761 §5.2.
+
+Everything here only marshals arguments: shapes, dtypes and the current HIP
+stream are read from torch tensors and passed to the C ABI of
+``include/ternary.h``.  Every step of the computation runs in the HIP kernels.
+If the library is not built this module raises on first use; there is no
+CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+__all__ = [
+    "TernaryError", "lib", "pack", "unpack", "linear", "select_path", "gemv_max_m",
+    "PATHS", "BF16", "FP16", "abi_version", "LIB_PATH",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
+
+BF16, FP16 = 0, 1
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3}
+
+# Every symbol include/ternary.h declares.
+EXPORTS = (
+    "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
+    "ternary_select_path", "ternary_gemv_max_m", "ternary_status_string", "ternary_abi_version",
+)
+
+_lib = None
+
+
+class TernaryError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(str(LIB_PATH))
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.ternary_pack.argtypes = [p, i64, i64, p, p, p]
+    L.ternary_unpack.argtypes = [p, i64, i64, p, p]
+    L.ternary_linear.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, p]
+    L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
+    L.ternary_select_path.argtypes = [i64, i64, i64, i64]
+    L.ternary_status_string.argtypes = [i32]
+    L.ternary_status_string.restype = ctypes.c_char_p
+    for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
+               "ternary_select_path", "ternary_gemv_max_m", "ternary_abi_version"):
+        getattr(L, nm).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().ternary_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().ternary_abi_version())
+
+
+def gemv_max_m() -> int:
+    return int(lib().ternary_gemv_max_m())
+
+
+def select_path(M: int, N: int, K: int, group_size: int) -> str:
+    r = int(lib().ternary_select_path(M, N, K, group_size))
+    if r < 0:
+        raise TernaryError(r, "ternary_select_path")
+    return {v: k for k, v in PATHS.items()}[r]
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TernaryError(status, where)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pack(q: torch.Tensor, invalid_count: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 [N, K] in {-1,0,1} -> uint8 [N, K/4].  Values outside {-1,0,1} are
+    written as 0 and, if ``invalid_count`` (int32 device scalar) is given,
+    added to it."""
+    _dev(q, "q")
+    if q.dtype != torch.int8 or q.dim() != 2:
+        raise ValueError("q must be a 2-D int8 tensor")
+    N, K = q.shape
+    out = torch.empty((N, K // 4), dtype=torch.uint8, device=q.device)
+    cnt = None
+    if invalid_count is not None:
+        _dev(invalid_count, "invalid_count")
+        if invalid_count.dtype != torch.int32 or invalid_count.numel() != 1:
+            raise ValueError("invalid_count must be a one-element int32 tensor")
+        cnt = invalid_count.data_ptr()
+    _check(lib().ternary_pack(q.data_ptr(), N, K, out.data_ptr(), cnt, _stream(q)), "ternary_pack")
+    return out
+
+
+def unpack(packed: torch.Tensor, K: int | None = None) -> torch.Tensor:
+    """uint8 (or int8 reinterpreted) [N, K/4] -> int8 [N, K]."""
+    _dev(packed, "packed")
+    if packed.dtype == torch.int8:
+        packed = packed.view(torch.uint8)
+    if packed.dtype != torch.uint8 or packed.dim() != 2:
+        raise ValueError("packed must be a 2-D uint8/int8 tensor")
+    N = packed.shape[0]
+    K = packed.shape[1] * 4 if K is None else K
+    out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check(lib().ternary_unpack(packed.data_ptr(), N, K, out.data_ptr(), _stream(packed)),
+           "ternary_unpack")
+    return out
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+           group_size: int | None = None, path: str = "auto",
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] = x [M, K] @ (q * s)^T in x's dtype (bf16 or fp16).
+
+    ``scale`` is fp16 [N] (per channel) or [N, K/128]; ``group_size`` is
+    inferred from its shape when not given.  ``path`` forces a kernel
+    ("gemv", "gemm", "simple"); "auto" picks by M.
+    """
+    for t, nm in ((x, "x"), (packed, "packed"), (scale, "scale")):
+        _dev(t, nm)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K] (flatten leading dimensions first)")
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float16:
+        dt = FP16
+    else:
+        raise ValueError("x must be bfloat16 or float16")
+    if packed.dtype == torch.int8:
+        packed = packed.view(torch.uint8)
+    if packed.dtype != torch.uint8 or packed.dim() != 2:
+        raise ValueError("packed must be a 2-D uint8/int8 tensor")
+    if scale.dtype != torch.float16:
+        raise ValueError("scale must be float16")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {K // 4}")
+    if group_size is None:
+        group_size = -1 if scale.dim() == 1 else K // scale.shape[1]
+    expect = (N,) if group_size == -1 else (N, K // group_size if group_size > 0 else 0)
+    if tuple(scale.shape) != expect:
+        raise ValueError(f"scale shape {tuple(scale.shape)} does not match {expect}")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out")
+        if out.dtype != x.dtype or tuple(out.shape) != (M, N):
+            raise ValueError("out must match x's dtype and have shape [M, N]")
+    st = lib().ternary_linear_ex(x.data_ptr(), dt, M, N, K, packed.data_ptr(), scale.data_ptr(),
+                                 group_size, out.data_ptr(), PATHS[path], _stream(x))
+    _check(st, "ternary_linear")
+    return out

@@ -1,0 +1,190 @@
+// C ABI of the ternary linear layer (declared in include/ternary.h).
+//
+// Host-side argument validation, then an asynchronous launch on the caller's
+// stream.  Validation never dereferences a pointer and never calls HIP, so an
+// invalid call returns its status without touching the device.
+#include <stdint.h>
+
+#include "../../include/ternary.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges; empty ranges never overlap).
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (na <= 0 || nb <= 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TERNARY_OK : TERNARY_ERR_HIP; }
+
+// Largest M, N or K accepted: kernels index channels, tokens and K with
+// 32-bit ints (element offsets are 64-bit) and grids stay far inside the
+// launch limits.
+constexpr int64_t kMaxDim = (int64_t)1 << 24;
+
+int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+                 const uint16_t *scale, int64_t group_size, const void *y)
+{
+    if (dtype != TERNARY_BF16 && dtype != TERNARY_FP16)
+        return TERNARY_ERR_DTYPE;
+    if (group_size != -1 && group_size != 128)
+        return TERNARY_ERR_GROUP;
+    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return TERNARY_ERR_SHAPE;
+    if (group_size == 128 && K % 128 != 0)
+        return TERNARY_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return TERNARY_OK;
+    if (!x || !packed || !scale || !y)
+        return TERNARY_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(packed, 16) || !aligned(scale, 2))
+        return TERNARY_ERR_ALIGN;
+    const int64_t ybytes = 2 * M * N;
+    const int64_t sbytes = 2 * (group_size == -1 ? N : N * (K / 128));
+    if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, packed, N * (K / 4)) ||
+        overlap(y, ybytes, scale, sbytes))
+        return TERNARY_ERR_ALIAS;
+    return TERNARY_OK;
+}
+
+int select_path(int64_t M, int64_t K)
+{
+    if (ternary::gemv_takes(M, K))
+        return TERNARY_PATH_GEMV;
+    if (ternary::gemm_takes(M, K))
+        return TERNARY_PATH_GEMM;
+    return TERNARY_PATH_SIMPLE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ternary_abi_version(void) { return kAbiVersion; }
+
+int ternary_gemv_max_m(void) { return ternary::kGemvMaxM; }
+
+const char *ternary_status_string(int status)
+{
+    switch (status) {
+    case TERNARY_OK: return "ok";
+    case TERNARY_ERR_NULL: return "null pointer argument";
+    case TERNARY_ERR_SHAPE: return "invalid shape (negative size, K % 4 != 0, or K % 128 != 0 in group mode)";
+    case TERNARY_ERR_GROUP: return "group_size must be -1 (per channel) or 128";
+    case TERNARY_ERR_DTYPE: return "activation dtype must be TERNARY_BF16 or TERNARY_FP16";
+    case TERNARY_ERR_ALIGN: return "pointer not aligned (data 16 bytes, scale 2 bytes)";
+    case TERNARY_ERR_ALIAS: return "output overlaps an input";
+    case TERNARY_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case TERNARY_ERR_PATH: return "forced kernel path cannot take this shape";
+    default: return "unknown status";
+    }
+}
+
+int ternary_pack(const int8_t *q, int64_t N, int64_t K, uint8_t *packed, int32_t *invalid_count,
+                 hipStream_t stream)
+{
+    if (N < 0 || K < 0 || K % 4 != 0)
+        return TERNARY_ERR_SHAPE;
+    if (N == 0 || K == 0)
+        return TERNARY_OK;
+    if (N > INT64_MAX / K)
+        return TERNARY_ERR_SHAPE;
+    if (!q || !packed)
+        return TERNARY_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(packed, 16) || !aligned(invalid_count, 4))
+        return TERNARY_ERR_ALIGN;
+    const int64_t nbytes = N * (K / 4);
+    if (overlap(packed, nbytes, q, N * K) || overlap(invalid_count, 4, q, N * K) ||
+        overlap(invalid_count, 4, packed, nbytes))
+        return TERNARY_ERR_ALIAS;
+    return hip_status(ternary::launch_pack(q, nbytes, packed, invalid_count, stream));
+}
+
+int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipStream_t stream)
+{
+    if (N < 0 || K < 0 || K % 4 != 0)
+        return TERNARY_ERR_SHAPE;
+    if (N == 0 || K == 0)
+        return TERNARY_OK;
+    if (N > INT64_MAX / K)
+        return TERNARY_ERR_SHAPE;
+    if (!q || !packed)
+        return TERNARY_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(packed, 16))
+        return TERNARY_ERR_ALIGN;
+    const int64_t nbytes = N * (K / 4);
+    if (overlap(packed, nbytes, q, N * K))
+        return TERNARY_ERR_ALIAS;
+    return hip_status(ternary::launch_unpack(packed, nbytes, q, stream));
+}
+
+int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size)
+{
+    if (group_size != -1 && group_size != 128)
+        return TERNARY_ERR_GROUP;
+    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+        (group_size == 128 && K % 128 != 0))
+        return TERNARY_ERR_SHAPE;
+    return select_path(M, K);
+}
+
+int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                      const uint8_t *packed, const uint16_t *scale, int64_t group_size, void *y,
+                      int path, hipStream_t stream)
+{
+    const int st = check_linear(x, dtype, M, N, K, packed, scale, group_size, y);
+    if (st != TERNARY_OK)
+        return st;
+    if (path == TERNARY_PATH_AUTO)
+        path = select_path(M, K);
+    switch (path) {
+    case TERNARY_PATH_GEMV:
+        if (!(M == 0 || N == 0 || ternary::gemv_takes(M, K)))
+            return TERNARY_ERR_PATH;
+        break;
+    case TERNARY_PATH_GEMM:
+        if (!(M == 0 || N == 0 || ternary::gemm_takes(M, K)))
+            return TERNARY_ERR_PATH;
+        break;
+    case TERNARY_PATH_SIMPLE: break;
+    default: return TERNARY_ERR_PATH;
+    }
+    if (M == 0 || N == 0)
+        return TERNARY_OK;
+    const bool fp16 = dtype == TERNARY_FP16;
+    const bool grouped = group_size == 128;
+    const uint16_t *xv = static_cast<const uint16_t *>(x);
+    uint16_t *yv = static_cast<uint16_t *>(y);
+    hipError_t e;
+    switch (path) {
+    case TERNARY_PATH_GEMV:
+        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv, stream);
+        break;
+    case TERNARY_PATH_GEMM:
+        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv, stream);
+        break;
+    default:
+        e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv,
+                                   stream);
+        break;
+    }
+    return hip_status(e);
+}
+
+int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                   const uint8_t *packed, const uint16_t *scale, int64_t group_size, void *y,
+                   hipStream_t stream)
+{
+    return ternary_linear_ex(x, dtype, M, N, K, packed, scale, group_size, y, TERNARY_PATH_AUTO,
+                             stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ternary {
+
+// Largest M the decode GEMV takes (two MFMA B columns per token, 16 columns).
+constexpr int kGemvMaxM = 8;
+
+hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,
+                       hipStream_t stream);
+hipError_t launch_unpack(const uint8_t *packed, int64_t nbytes, int8_t *q, hipStream_t stream);
+
+// All linear launchers: x/y are 2-byte elements (bf16 or fp16 by `fp16`),
+// group_size is -1 or 128, shapes already validated by the caller.
+hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
+                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
+                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
+                         const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+
+// Shape requirements of the fast kernels.
+inline bool gemv_takes(int64_t M, int64_t K) { return M >= 1 && M <= kGemvMaxM && K % 128 == 0; }
+inline bool gemm_takes(int64_t M, int64_t K) { return M >= 1 && K % 128 == 0; }
+
+}  // namespace ternary

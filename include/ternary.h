@@ -1,0 +1,145 @@
+/*
+ * ternary.h - C ABI of the MI355X (gfx950) ternary-weight linear layer.
+ *
+ *     y[m,n] = sum_k x[m,k] * q[n,k] * s(n,k)          (y = x * (q (.) s)^T)
+ *
+ * Sources (page titles and sections):
+ *   [trdm] trdm.cn, "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战":
+ *          §3.1 packing rule; §4.2 operand shapes; §4.4 2-D contiguous input.
+ *   [nxbn] m.nxbn.cn/news/169761 (a 7B ternary checkpoint into vLLM):
+ *          §2.2 code table and bit order; §3.2 per-channel scale broadcast
+ *          over rows; §5.2 the layer's forward takes (x, weight, scale).
+ *   [xxqk] m.xxqk.cn/news/593501 (Bonsai 2 27B into vLLM): §4.3 the layer is
+ *          dequantise-then-matmul.
+ *   [ch13] yangyitao.com vLLM book, "第13章 量化：精度与速度的工程平衡":
+ *          §13.3 scale granularity (per channel, per group); §13.8.2
+ *          group_size = -1 means one group per row.
+ *
+ * Format (fixed by [trdm §3.1] and [nxbn §2.2]):
+ *   - each weight is a 2-bit code: 00 -> 0, 01 -> +1, 10 -> -1, 11 -> reserved,
+ *     read as 0 by every function here and never written by ternary_pack;
+ *   - four codes per byte, little-endian: weight 4j+i of a row lives in bits
+ *     [2i+1:2i] of byte j of that row;
+ *   - packed weights are [N, K/4] bytes, row-major (one row per output channel,
+ *     K contiguous);
+ *   - scales are IEEE binary16 bit patterns: [N] when group_size == -1 (one per
+ *     output channel, [nxbn §3.2]) or [N, K/128] row-major when group_size ==
+ *     128 (128 consecutive K weights of a row share one, [trdm §3.1]).
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers, owned by the caller.  The library
+ *     keeps no reference after a call returns and never allocates or frees
+ *     caller memory.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
+ *     Arguments are validated on the host before anything is launched; on any
+ *     error a negative ternary_status is returned and nothing is enqueued.
+ *     Faults during execution surface at the next synchronisation of the
+ *     stream, as for any HIP kernel.
+ *   - Every call is deterministic: the same inputs give the same bits.
+ *   - No function throws; C++ exceptions never cross this boundary.
+ */
+#ifndef TERNARY_LINEAR_H
+#define TERNARY_LINEAR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TERNARY_OK = 0,
+    TERNARY_ERR_NULL = -1,   /* a required pointer is NULL                       */
+    TERNARY_ERR_SHAPE = -2,  /* negative size, K % 4 != 0, K % group != 0, ...   */
+    TERNARY_ERR_GROUP = -3,  /* group_size is neither -1 nor 128                 */
+    TERNARY_ERR_DTYPE = -4,  /* activation dtype is not TERNARY_BF16/TERNARY_FP16*/
+    TERNARY_ERR_ALIGN = -5,  /* a pointer is not aligned as documented           */
+    TERNARY_ERR_ALIAS = -6,  /* the output overlaps an input                     */
+    TERNARY_ERR_HIP = -7,    /* a HIP runtime call or kernel launch failed       */
+    TERNARY_ERR_PATH = -8    /* a forced kernel path cannot take this shape      */
+} ternary_status;
+
+/* Activation / output element type (2 bytes per element). */
+typedef enum { TERNARY_BF16 = 0, TERNARY_FP16 = 1 } ternary_dtype;
+
+/* Kernel path for ternary_linear_ex.  AUTO picks by M (see ternary_linear). */
+typedef enum {
+    TERNARY_PATH_AUTO = 0,
+    TERNARY_PATH_GEMV = 1,   /* decode kernel, requires 1 <= M <= ternary_gemv_max_m() */
+    TERNARY_PATH_GEMM = 2,   /* prefill kernel (LDS expansion + bf16/fp16 MFMA)        */
+    TERNARY_PATH_SIMPLE = 3  /* plain one-output-per-thread kernel, any valid shape    */
+} ternary_path;
+
+/*
+ * ternary_pack - encode ternary values as 2-bit codes ([trdm §3.1]).
+ *   q             int8 [N, K], row-major, values in {-1, 0, +1}; 16-byte aligned.
+ *   N, K          N >= 0, K >= 0, K % 4 == 0.
+ *   packed        uint8 [N, K/4] output, 16-byte aligned, must not overlap q.
+ *   invalid_count optional int32 (device).  Each value outside {-1, 0, +1} is
+ *                 written as code 00 and counted; the count is ADDED to
+ *                 *invalid_count (the caller zeroes it).  NULL skips counting.
+ * N == 0 or K == 0 is a successful no-op.
+ */
+int ternary_pack(const int8_t *q, int64_t N, int64_t K, uint8_t *packed,
+                 int32_t *invalid_count, hipStream_t stream);
+
+/*
+ * ternary_unpack - decode 2-bit codes to int8 {-1, 0, +1} ([trdm §3.1],
+ * [nxbn §2.2]); code 11 decodes to 0.  Bit-exact inverse of ternary_pack for
+ * bytes that hold no code 11.
+ *   packed  uint8 [N, K/4], 16-byte aligned.
+ *   q       int8 [N, K] output, 16-byte aligned, must not overlap packed.
+ */
+int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipStream_t stream);
+
+/*
+ * ternary_linear - y = x * (q (.) s)^T ([xxqk §4.3]; operand shapes [trdm §4.2]).
+ *   x           [M, K] activations, dtype `dtype`, row-major contiguous
+ *               ([trdm §4.4]: callers flatten leading dims to M), 16-byte aligned.
+ *   dtype       TERNARY_BF16 or TERNARY_FP16; y has the same dtype.
+ *   M, N, K     M >= 0, N >= 0, K > 0, K % 4 == 0; K % 128 == 0 when grouped.
+ *               M == 0 or N == 0 is a successful no-op.
+ *   packed      uint8 [N, K/4] codes as above, 16-byte aligned.
+ *   scale       fp16 bit patterns, [N] (group_size == -1) or [N, K/128]
+ *               (group_size == 128), 2-byte aligned.
+ *   group_size  -1 (per output channel) or 128 ([ch13 §13.8.2] convention).
+ *   y           [M, N] output, 16-byte aligned, must not overlap any input.
+ * Products are formed exactly and accumulated in fp32; the scale multiplies
+ * each group's (or the row's) fp32 partial sum; y is rounded from fp32 to the
+ * output dtype, round-to-nearest-even.  x and s must be finite (results for
+ * non-finite inputs are unspecified) and |x| < 2^126.
+ * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV, larger M the
+ * MFMA GEMM; shapes neither fast kernel takes (K % 128 != 0) run the plain
+ * kernel.  Results of different paths agree within the bound
+ * |y - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6, not bitwise.
+ */
+int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                   const uint8_t *packed, const uint16_t *scale, int64_t group_size,
+                   void *y, hipStream_t stream);
+
+/* ternary_linear with an explicit kernel path (ternary_path); AUTO is the
+ * default choice above.  A forced path that cannot take the shape returns
+ * TERNARY_ERR_PATH without launching. */
+int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                      const uint8_t *packed, const uint16_t *scale, int64_t group_size,
+                      void *y, int path, hipStream_t stream);
+
+/* The path ternary_linear_ex(..., TERNARY_PATH_AUTO, ...) takes for a shape
+ * (a ternary_path value), or a negative status for invalid shapes. */
+int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size);
+
+/* Largest M the decode GEMV accepts. */
+int ternary_gemv_max_m(void);
+
+/* Human-readable name of a ternary_status value (static storage). */
+const char *ternary_status_string(int status);
+
+/* Library ABI version (increments when a signature or a convention changes). */
+int ternary_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_LINEAR_H */

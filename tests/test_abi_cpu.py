@@ -1,0 +1,141 @@
+"""The C-ABI library without a GPU: it loads, exports what include/ternary.h
+declares, and rejects invalid arguments on the host before any launch.
+
+None of these calls reach the device: every case fails host-side validation
+(or is an M == 0 / N == 0 no-op), so the pointers passed are never used.
+"""
+
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "ternary.h"
+
+
+@pytest.fixture(scope="module")
+def tl():
+    import gemm_ternary_linear_amd as tl
+    if not tl.LIB_PATH.exists():
+        from gemm_ternary_linear_amd import build
+        build.build()
+    return tl
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ternary_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected(tl):
+    assert declared_functions() == sorted(tl.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(tl):
+    L = tl.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_exported_symbols_in_dynamic_table(tl):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", str(tl.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared_functions():
+        assert name in names, name
+
+
+def test_no_oracle_linkage(tl):
+    import subprocess
+    out = subprocess.run(["nm", "-D", str(tl.LIB_PATH)], capture_output=True, text=True,
+                         check=True).stdout
+    assert "oracle" not in out
+    ldd = subprocess.run(["ldd", str(tl.LIB_PATH)], capture_output=True, text=True).stdout
+    assert "oracle" not in ldd
+
+
+def test_versions_and_strings(tl):
+    assert tl.abi_version() == 1
+    assert tl.gemv_max_m() == 8
+    for st in range(0, -9, -1):
+        s = tl.status_string(st)
+        assert s and s != "unknown status"
+    assert tl.status_string(-99) == "unknown status"
+
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
+
+
+def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y=FAKE * 4, path=0):
+    return tl.lib().ternary_linear_ex(x, dtype, M, N, K, p, s, g, y, path, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), -4),
+    (dict(g=64), -3),
+    (dict(g=0), -3),
+    (dict(K=0), -2),
+    (dict(K=130, g=-1), -2),
+    (dict(K=132), -2),           # grouped needs K % 128 == 0
+    (dict(M=-1), -2),
+    (dict(N=-5), -2),
+    (dict(M=1 << 25), -2),
+    (dict(x=0), -1),
+    (dict(p=0), -1),
+    (dict(s=0), -1),
+    (dict(y=0), -1),
+    (dict(x=FAKE + 8), -5),
+    (dict(y=FAKE * 4 + 2), -5),
+    (dict(p=FAKE * 2 + 1), -5),
+    (dict(s=FAKE * 3 + 1), -5),
+    (dict(y=FAKE), -6),                       # y == x
+    (dict(y=FAKE * 2 + 16), -6),              # y inside packed
+    (dict(path=9), -8),
+    (dict(M=9, path=1), -8),                  # GEMV takes M <= 8 only
+    (dict(K=132, g=-1, path=1), -8),          # fast kernels need K % 128 == 0
+    (dict(K=132, g=-1, path=2), -8),
+])
+def test_linear_rejects(tl, kw, status):
+    assert _lin(tl, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(M=0, x=0, y=0), dict(N=0, p=0, s=0)])
+def test_linear_empty_is_noop(tl, kw):
+    assert _lin(tl, **kw) == 0
+
+
+def test_pack_unpack_reject(tl):
+    L = tl.lib()
+    assert L.ternary_pack(FAKE, 4, 6, FAKE * 2, None, None) == -2
+    assert L.ternary_pack(FAKE, -1, 8, FAKE * 2, None, None) == -2
+    assert L.ternary_pack(0, 4, 8, FAKE * 2, None, None) == -1
+    assert L.ternary_pack(FAKE + 1, 4, 8, FAKE * 2, None, None) == -5
+    assert L.ternary_pack(FAKE, 4, 8, FAKE * 2, FAKE * 3 + 2, None) == -5
+    assert L.ternary_pack(FAKE, 4, 64, FAKE + 16, None, None) == -6
+    assert L.ternary_pack(FAKE, 0, 64, 0, None, None) == 0
+    assert L.ternary_unpack(FAKE, 4, 6, FAKE * 2, None) == -2
+    assert L.ternary_unpack(0, 4, 8, FAKE * 2, None) == -1
+    assert L.ternary_unpack(FAKE, 4, 8, FAKE * 2 + 4, None) == -5
+    assert L.ternary_unpack(FAKE, 4, 64, FAKE - 16, None) == -6
+    assert L.ternary_unpack(FAKE, 4, 0, 0, None) == 0
+
+
+@pytest.mark.parametrize("M,K,g,path", [
+    (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "gemm"),
+    (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
+    (0, 128, 128, "gemv"),
+])
+def test_select_path(tl, M, K, g, path):
+    if M == 0:
+        assert tl.select_path(M, 16, K, g) in ("gemv", "gemm", "simple")
+    else:
+        assert tl.select_path(M, 16, K, g) == path
+
+
+def test_select_path_rejects(tl):
+    L = tl.lib()
+    assert L.ternary_select_path(1, 16, 130, -1) == -2
+    assert L.ternary_select_path(1, 16, 256, 64) == -3

@@ -1,0 +1,228 @@
+"""GPU ternary_linear against the CPU oracle.
+
+Bar: |y_gpu - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6 for every output
+(the stated tolerance; y_ref and the bound are fp64 from the oracle).  The
+oracle packs the codes itself; the GPU side packs the same codes with its own
+kernel, and the bytes are compared bit-exactly first.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bits_of, check_within, say, to_dev, widen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tl():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_ternary_linear_amd as tl
+    tl.lib()
+    return tl
+
+
+def _tdt(dtype):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float16
+
+
+def _case(rng, M, N, K, g, dtype, raw=False, p0=0.4):
+    pm = (1.0 - p0) / 2
+    if raw:
+        packed = synth.draw_bytes(rng, N, K)
+        codes = None
+    else:
+        codes = synth.draw_codes(rng, N, K, pm, pm)
+        packed, _ = oracle.pack(codes)
+    scale = synth.draw_scales(rng, N, K, g)
+    x = synth.draw_x(rng, M, K, dtype)
+    return codes, packed, scale, x
+
+
+def _run(tl, x, packed, scale, g, dtype, path="auto", codes=None):
+    import torch
+    if codes is not None:
+        p_dev = tl.pack(to_dev(codes, None))
+        torch.cuda.synchronize()
+        assert np.array_equal(p_dev.cpu().numpy(), packed), "GPU pack differs from the oracle"
+    else:
+        p_dev = to_dev(packed, None)
+    y = tl.linear(to_dev(x, _tdt(dtype)), p_dev, to_dev(scale, torch.float16), g, path=path)
+    torch.cuda.synchronize()
+    return widen(bits_of(y), dtype)
+
+
+SMALL = [
+    # (M, N, K, group) -- several tiles and a ragged tail in N (and M for GEMM)
+    (1, 16, 128, 128), (1, 100, 384, 128), (1, 300, 1024, -1), (2, 33, 256, -1),
+    (3, 257, 4096, 128), (5, 64, 2048, -1), (8, 100, 18944, -1), (8, 48, 5120, 128),
+    (1, 1, 128, 128), (7, 1030, 640, 128),
+    (9, 100, 256, 128), (16, 130, 1024, -1), (64, 257, 384, 128), (130, 129, 1024, -1),
+    (256, 64, 512, 128), (200, 300, 2048, -1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K,g", SMALL)
+def test_linear_auto_small(tl, M, N, K, g, dtype):
+    say(f"linear auto M={M} N={N} K={K} g={g} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr((M, N, K, g, dtype)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, g, dtype)
+    y_ref, bound = oracle.linear(x, packed, scale, g, dtype=dtype)
+    y = _run(tl, x, packed, scale, g, dtype, codes=codes)
+    check_within(y, y_ref, bound, f"auto M={M} N={N} K={K} g={g} {dtype}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm", "simple"])
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("g", [128, -1])
+def test_forced_paths_agree_with_oracle(tl, path, M, g):
+    say(f"linear forced {path} M={M} g={g}")
+    rng = np.random.default_rng(1000 + M * 10 + (g > 0))
+    N, K = 200, 1536
+    codes, packed, scale, x = _case(rng, M, N, K, g, "bf16")
+    y_ref, bound = oracle.linear(x, packed, scale, g)
+    y = _run(tl, x, packed, scale, g, "bf16", path=path, codes=codes)
+    check_within(y, y_ref, bound, f"{path} M={M} g={g}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5, 132), (3, 300, 4), (2, 70, 1000), (40, 33, 36)])
+def test_simple_path_odd_K(tl, M, N, K):
+    say(f"linear odd K M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    codes, packed, scale, x = _case(rng, M, N, K, -1, "bf16")
+    assert tl.select_path(M, N, K, -1) == "simple"
+    y_ref, bound = oracle.linear(x, packed, scale, -1)
+    y = _run(tl, x, packed, scale, -1, "bf16", codes=codes)
+    # K as small as 4: |y| may reach B, so the bf16 rounding of y is allowed for
+    check_within(y, y_ref, bound, f"odd K M={M} N={N} K={K}", out_rounding="bf16")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm", "simple"])
+@pytest.mark.parametrize("g", [128, -1])
+def test_reserved_codes_read_as_zero(tl, path, g):
+    say(f"linear random bytes (with 11 codes) {path} g={g}")
+    rng = np.random.default_rng(77 + (g > 0))
+    M = 3 if path != "gemm" else 40
+    _, packed, scale, x = _case(rng, M, 150, 1024, g, "bf16", raw=True)
+    assert oracle.count_reserved(packed) > 0
+    y_ref, bound = oracle.linear(x, packed, scale, g)
+    y = _run(tl, x, packed, scale, g, "bf16", path=path)
+    check_within(y, y_ref, bound, f"raw bytes {path} g={g}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm", "simple"])
+def test_closed_form_exact(tl, path):
+    # All +1 codes, integer activations and power-of-two scales: every partial
+    # sum is exact in fp32, so y is exact and must match bit for bit.
+    say(f"linear closed form all +1 {path}")
+    rng = np.random.default_rng(4)
+    M, N, K, g = (4 if path != "gemm" else 20), 48, 512, 128
+    xi = rng.integers(-4, 5, size=(M, K)).astype(np.float64)
+    x = synth.f64_to_bf16_bits(xi)
+    sv = np.ldexp(1.0, rng.integers(-8, -3, size=(N, K // g)))
+    s = synth.f64_to_f16_bits(sv)
+    packed, _ = oracle.pack(np.ones((N, K), np.int8))
+    expect = xi.reshape(M, K // g, g).sum(axis=2) @ sv.T
+    y = _run(tl, x, packed, s, g, "bf16", path=path)
+    # the exact result is a short dyadic number; bf16 rounding of it is exact
+    # only if it fits 8 significant bits, so compare against its bf16 rounding
+    assert np.array_equal(y, widen(synth.f64_to_bf16_bits(expect), "bf16"))
+    neg, _ = oracle.pack(-np.ones((N, K), np.int8))
+    y2 = _run(tl, x, neg, s, g, "bf16", path=path)
+    assert np.array_equal(y2, -widen(synth.f64_to_bf16_bits(expect), "bf16"))
+    zero = np.zeros((N, K // 4), np.uint8)
+    y3 = _run(tl, x, zero, s, g, "bf16", path=path)
+    assert np.all(y3 == 0.0)
+
+
+def test_deterministic(tl):
+    say("linear determinism")
+    import torch
+    rng = np.random.default_rng(8)
+    for M in (1, 8, 300):
+        codes, packed, scale, x = _case(rng, M, 513, 2048, 128, "bf16")
+        xd, pd, sd = to_dev(x, torch.bfloat16), to_dev(packed, None), to_dev(scale, torch.float16)
+        a = tl.linear(xd, pd, sd, 128)
+        b = tl.linear(xd, pd, sd, 128)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_and_out_argument(tl):
+    say("linear M=0 and out=")
+    import torch
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda:0")
+    p = torch.zeros((10, 64), dtype=torch.uint8, device="cuda:0")
+    s = torch.ones((10, 2), dtype=torch.float16, device="cuda:0")
+    y = tl.linear(x, p, s)
+    assert tuple(y.shape) == (0, 10)
+    rng = np.random.default_rng(9)
+    codes, packed, scale, xb = _case(rng, 2, 10, 256, 128, "bf16")
+    out = torch.full((2, 10), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    r = tl.linear(to_dev(xb, torch.bfloat16), to_dev(packed, None), to_dev(scale, torch.float16),
+                  out=out)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == out.data_ptr()
+    y_ref, bound = oracle.linear(xb, packed, scale, 128)
+    check_within(widen(bits_of(out), "bf16"), y_ref, bound, "out=")
+
+
+def test_rejects_through_binding(tl):
+    say("binding error paths")
+    import torch
+    p = torch.zeros((10, 64), dtype=torch.uint8, device="cuda:0")
+    s = torch.ones((10, 2), dtype=torch.float16, device="cuda:0")
+    x9 = torch.zeros((9, 256), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(tl.TernaryError) as e:
+        tl.linear(x9, p, s, path="gemv")
+    assert e.value.status == -8
+    buf = torch.zeros(4096, dtype=torch.bfloat16, device="cuda:0")
+    x = buf[:512].view(2, 256)
+    out = buf[:20].view(2, 10)  # output overlapping the activations
+    with pytest.raises(tl.TernaryError) as e:
+        tl.linear(x, p, s, out=out)
+    assert e.value.status == -6
+
+
+# ---------------------------------------------------------------- full-size configs
+
+FULL = [(c, si, M) for c, cfg in sorted(synth.CONFIGS.items())
+        for si in range(len(cfg.shapes)) for M in cfg.Ms]
+
+
+def _sample_indices(rng, M, N, count=1536):
+    ms = rng.integers(0, M, size=count)
+    ns = rng.integers(0, N, size=count)
+    edge_m = np.array([0, M - 1, 0, M - 1, M // 2])
+    edge_n = np.array([0, 0, N - 1, N - 1, N // 2])
+    return np.concatenate([ms, edge_m]), np.concatenate([ns, edge_n])
+
+
+@pytest.mark.parametrize("cfg,si,M", FULL, ids=[f"c{c}-{synth.CONFIGS[c].shapes[s].name}-M{m}"
+                                                for c, s, m in FULL])
+def test_full_size_sampled(tl, cfg, si, M):
+    import torch
+    case = synth.make_case(cfg, si, M)
+    shp = case.shape
+    g = case.group_size
+    say(f"full config {cfg} {shp.name} N={shp.N} K={shp.K} M={M} g={g} "
+        f"path={tl.select_path(M, shp.N, shp.K, g)}")
+    packed, _ = oracle.pack(case.codes)
+    p_dev = tl.pack(to_dev(case.codes, None))
+    y = tl.linear(to_dev(case.x, torch.bfloat16), p_dev, to_dev(case.scale, torch.float16), g)
+    torch.cuda.synchronize()
+    assert np.array_equal(p_dev.cpu().numpy(), packed)
+    yv = widen(bits_of(y), "bf16")
+    rng = np.random.default_rng(cfg * 100 + si * 10 + M)
+    ms, ns = _sample_indices(rng, M, shp.N)
+    y_ref, bound = oracle.linear_at(case.x, packed, case.scale, g, ms, ns)
+    check_within(yv[ms, ns], y_ref, bound, f"config {cfg} {shp.name} M={M}")
+    assert np.all(np.isfinite(yv))
