@@ -23,7 +23,7 @@ from pathlib import Path
 import torch
 
 __all__ = [
-    "TernaryError", "lib", "pack", "unpack", "linear", "select_path", "gemv_max_m",
+    "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
     "PATHS", "BF16", "FP16", "abi_version", "LIB_PATH",
 ]
 
@@ -35,8 +35,17 @@ PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3}
 # Every symbol include/ternary.h declares.
 EXPORTS = (
     "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
-    "ternary_select_path", "ternary_gemv_max_m", "ternary_status_string", "ternary_abi_version",
+    "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
+    "ternary_status_string", "ternary_abi_version",
 )
+MAX_BATCH = 8
+
+
+class Problem(ctypes.Structure):
+    """ternary_problem of include/ternary.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("group_size", ctypes.c_int64)]
 
 _lib = None
 
@@ -62,11 +71,13 @@ def lib() -> ctypes.CDLL:
     L.ternary_unpack.argtypes = [p, i64, i64, p, p]
     L.ternary_linear.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, p]
     L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
+    L.ternary_linear_batch.argtypes = [p, i32, i32, p]
     L.ternary_select_path.argtypes = [i64, i64, i64, i64]
     L.ternary_status_string.argtypes = [i32]
     L.ternary_status_string.restype = ctypes.c_char_p
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
-               "ternary_select_path", "ternary_gemv_max_m", "ternary_abi_version"):
+               "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
+               "ternary_abi_version"):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -91,8 +102,14 @@ def select_path(M: int, N: int, K: int, group_size: int) -> str:
     return {v: k for k, v in PATHS.items()}[r]
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """The current HIP stream of t's device (what torch would launch on)."""
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _check(status: int, where: str):
@@ -141,6 +158,46 @@ def unpack(packed: torch.Tensor, K: int | None = None) -> torch.Tensor:
     return out
 
 
+_ACT = {torch.bfloat16: BF16, torch.float16: FP16}
+
+
+def _check_problem(x, packed, scale, group_size, out):
+    """Shapes/dtypes of one problem checked against each other -> (dt, M, N, K, g, packed, out)."""
+    dt = _ACT.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bfloat16 or float16")
+    if packed.dtype == torch.int8:
+        packed = packed.view(torch.uint8)
+    xs, ps, ss = x.shape, packed.shape, scale.shape
+    if len(xs) != 2:
+        raise ValueError("x must be 2-D [M, K] (flatten leading dimensions first)")
+    if packed.dtype != torch.uint8 or len(ps) != 2:
+        raise ValueError("packed must be a 2-D uint8/int8 tensor")
+    if scale.dtype != torch.float16:
+        raise ValueError("scale must be float16")
+    M, K = xs
+    N = ps[0]
+    if ps[1] * 4 != K:
+        raise ValueError(f"packed has {ps[1]} bytes per row, K={K} needs {K // 4}")
+    if group_size is None:
+        group_size = -1 if len(ss) == 1 else (K // ss[1] if ss[1] else 0)
+    if group_size == -1:
+        ok = tuple(ss) == (N,)
+    else:
+        ok = len(ss) == 2 and group_size > 0 and ss[0] == N and ss[1] * group_size == K
+    if not ok:
+        raise ValueError(f"scale shape {tuple(ss)} does not match N={N}, K={K}, "
+                         f"group_size={group_size}")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be contiguous, match x's dtype and have shape [M, N]")
+    for t in (x, packed, scale, out):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    return dt, M, N, K, group_size, packed, out
+
+
 def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
            group_size: int | None = None, path: str = "auto",
            out: torch.Tensor | None = None) -> torch.Tensor:
@@ -148,40 +205,36 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
 
     ``scale`` is fp16 [N] (per channel) or [N, K/128]; ``group_size`` is
     inferred from its shape when not given.  ``path`` forces a kernel
-    ("gemv", "gemm", "simple"); "auto" picks by M.
+    ("gemv", "gemm", "simple"); "auto" picks by M.  Shapes are checked here
+    against each other, so the sizes passed to the C ABI match the tensors.
     """
-    for t, nm in ((x, "x"), (packed, "packed"), (scale, "scale")):
-        _dev(t, nm)
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [M, K] (flatten leading dimensions first)")
-    if x.dtype == torch.bfloat16:
-        dt = BF16
-    elif x.dtype == torch.float16:
-        dt = FP16
-    else:
-        raise ValueError("x must be bfloat16 or float16")
-    if packed.dtype == torch.int8:
-        packed = packed.view(torch.uint8)
-    if packed.dtype != torch.uint8 or packed.dim() != 2:
-        raise ValueError("packed must be a 2-D uint8/int8 tensor")
-    if scale.dtype != torch.float16:
-        raise ValueError("scale must be float16")
-    M, K = x.shape
-    N = packed.shape[0]
-    if packed.shape[1] * 4 != K:
-        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {K // 4}")
-    if group_size is None:
-        group_size = -1 if scale.dim() == 1 else K // scale.shape[1]
-    expect = (N,) if group_size == -1 else (N, K // group_size if group_size > 0 else 0)
-    if tuple(scale.shape) != expect:
-        raise ValueError(f"scale shape {tuple(scale.shape)} does not match {expect}")
-    if out is None:
-        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    else:
-        _dev(out, "out")
-        if out.dtype != x.dtype or tuple(out.shape) != (M, N):
-            raise ValueError("out must match x's dtype and have shape [M, N]")
+    dt, M, N, K, group_size, packed, out = _check_problem(x, packed, scale, group_size, out)
     st = lib().ternary_linear_ex(x.data_ptr(), dt, M, N, K, packed.data_ptr(), scale.data_ptr(),
                                  group_size, out.data_ptr(), PATHS[path], _stream(x))
-    _check(st, "ternary_linear")
+    if st:
+        raise TernaryError(st, "ternary_linear")
     return out
+
+
+def linear_batch(problems) -> list:
+    """Several projections in as few launches as possible (one for all decode
+    shapes).  ``problems`` is a sequence of (x, packed, scale, group_size, out)
+    tuples (group_size and out may be None); returns the outputs."""
+    n = len(problems)
+    if not 1 <= n <= MAX_BATCH:
+        raise ValueError(f"1..{MAX_BATCH} problems per batch")
+    arr = (Problem * n)()
+    outs = []
+    dts = set()
+    for i, (x, packed, scale, g, out) in enumerate(problems):
+        dt, M, N, K, g, packed, out = _check_problem(x, packed, scale, g, out)
+        dts.add(dt)
+        arr[i] = Problem(x.data_ptr(), packed.data_ptr(), scale.data_ptr(), out.data_ptr(),
+                         M, N, K, g)
+        outs.append(out)
+    if len(dts) != 1:
+        raise ValueError("all problems of a batch share one activation dtype")
+    st = lib().ternary_linear_batch(arr, n, dts.pop(), _stream(problems[0][0]))
+    if st:
+        raise TernaryError(st, "ternary_linear_batch")
+    return outs

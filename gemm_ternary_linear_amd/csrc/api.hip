@@ -179,6 +179,57 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     return hip_status(e);
 }
 
+int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
+                         hipStream_t stream)
+{
+    if (count < 1 || count > TERNARY_MAX_BATCH)
+        return TERNARY_ERR_SHAPE;
+    if (!problems)
+        return TERNARY_ERR_NULL;
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &p = problems[i];
+        const int st = check_linear(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y);
+        if (st != TERNARY_OK)
+            return st;
+    }
+    // No output may overlap another problem's inputs or output.
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &a = problems[i];
+        const int64_t ya = 2 * a.M * a.N;
+        for (int j = 0; j < count; ++j) {
+            if (i == j)
+                continue;
+            const ternary_problem &b = problems[j];
+            const int64_t sb = 2 * (b.group_size == -1 ? b.N : b.N * (b.K / 128));
+            if (overlap(a.y, ya, b.x, 2 * b.M * b.K) ||
+                overlap(a.y, ya, b.packed, b.N * (b.K / 4)) || overlap(a.y, ya, b.scale, sb) ||
+                overlap(a.y, ya, b.y, 2 * b.M * b.N))
+                return TERNARY_ERR_ALIAS;
+        }
+    }
+    const bool fp16 = dtype == TERNARY_FP16;
+    ternary::GemvArgs fused[TERNARY_MAX_BATCH];
+    int nf = 0;
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &p = problems[i];
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (ternary::gemv_takes(p.M, p.K)) {
+            fused[nf++] = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
+                           static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
+                           p.group_size == 128};
+        } else {
+            const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,
+                                             p.group_size, p.y, TERNARY_PATH_AUTO, stream);
+            if (st != TERNARY_OK)
+                return st;
+        }
+    }
+    if (nf)
+        return hip_status(ternary::launch_gemv_batch(fused, nf, fp16, stream));
+    return TERNARY_OK;
+}
+
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
                    const uint8_t *packed, const uint16_t *scale, int64_t group_size, void *y,
                    hipStream_t stream)

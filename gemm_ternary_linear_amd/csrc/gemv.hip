@@ -1,4 +1,5 @@
-// Decode GEMV (1 <= M <= 8) for the ternary linear layer on gfx950.
+// Decode GEMV (1 <= M <= 8) for the ternary linear layer on gfx950, for one
+// projection or a batch of projections fused into one launch.
 //
 // The layer ([xxqk] m.xxqk.cn/news/593501 §4.3: y = x @ (unpack(q) * s)^T) at
 // small M is bound by the HBM stream of packed weights ([nxbn]
@@ -6,32 +7,65 @@
 // is what cuts the bytes).  Scale granularity: one fp16 per output channel
 // ([nxbn] §3.2) or per 128 consecutive K weights ([trdm] trdm.cn
 // "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1), applied to the
-// finished partial sum of its block ([trdm] §4.2).
+// finished partial sum of its block ([trdm] §4.2).  Several projections (for
+// instance the segments of a fused QKV weight, [trdm] §2.2) can share one
+// launch, which pays the fixed launch and first-byte latency once.
 //
 // Mapping onto CDNA4:
-//  * One workgroup owns a block of 16 output channels and the whole K range;
-//    its W waves take 256-wide K slabs round-robin.
+//  * A workgroup is 4 waves and owns RB blocks of 16 output channels (RB =
+//    1, 2 or 4 by M): each wave takes one block and 1/KP of its K slabs
+//    (KP = 4/RB), a slab being 256 codes (64 bytes) of every channel.
 //  * Per slab a lane issues ONE 16-byte load of packed codes: lane l reads
-//    channel (l & 15), bytes [16*(l>>4), +16) of the slab's 64 bytes, so a
-//    wave reads 16 channels x 64 contiguous bytes per instruction.
+//    channel (l & 15), bytes [16*(l>>4), +16) of the slab, so a wave reads
+//    16 channels x 64 contiguous bytes per instruction.  Slabs stream in
+//    groups of four, the next group's loads in flight while the current one
+//    is decoded.
 //  * The codes are decoded in registers (decode16, branch-free byte permutes)
 //    into the A operand of v_mfma_f32_16x16x32_{bf16,f16}: rows = channels,
 //    k in natural order.  The B operand is the activation: column 2t+p holds
 //    token t restricted to 128-group p of the slab (lanes of the other group
 //    keep zeros), so one MFMA chain yields both groups' partial sums
 //    separately and each is scaled by its own fp16 scale before it joins the
-//    fp32 accumulator.  Only the lanes that own real B entries load x.
+//    fp32 accumulator.  Only the lanes that own real B entries read x.
+//  * Per-channel and group-scaled problems are separate kernel instances, so
+//    a batch that holds both takes two launches.
+//  * x (all M tokens) is copied into LDS with direct global->LDS loads, whole
+//    K when it fits 64 KB, otherwise in K chunks (then KP = 1 and the waves
+//    walk the chunks together).  Group scales of the workgroup's channels are
+//    staged in LDS too.
 //  * The MFMA does the add/sub accumulate (weights are exactly +-2 or 0, the
-//    products exact, the sums fp32); zero codes cost no extra work.
-//  * The W waves' 16x16 fp32 tiles are reduced through LDS in a fixed order,
-//    the two group columns of a token are combined with a lane shuffle, and
-//    the result is rounded to the output dtype (round to nearest even).
+//    products exact, the sums fp32).
+//  * The KP partial tiles of a channel block are reduced through LDS in a
+//    fixed order, the two group columns of a token are combined with a lane
+//    shuffle, and the result is rounded to the output dtype (nearest even).
 #include "common.h"
 #include "internal.h"
 
 namespace ternary {
 
 namespace {
+
+constexpr int kThreads = 256;         // 4 waves
+constexpr int kGroup = 4;             // slabs per load group
+constexpr int kXLdsBytes = 64 << 10;  // activation chunk staged in LDS per workgroup
+
+struct GemvProblem {
+    const uint16_t *x;
+    const uint8_t *packed;
+    const uint16_t *scale;
+    uint16_t *y;
+    int M, N, K;
+    int grouped;  // group-128 scales
+    int rb;       // 16-channel blocks per workgroup: 1, 2 or 4
+    int spart;    // slabs per wave (one K part)
+    int kc;       // K elements staged in LDS at once (multiple of 1024)
+    int unit0;    // first workgroup of this problem
+};
+
+struct GemvBatch {
+    int count;
+    GemvProblem p[kGemvMaxBatch];
+};
 
 template <bool FP16>
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f32x4_t c)
@@ -46,101 +80,195 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f3
                                                        0);
 }
 
-struct SlabRegs {
-    uint4 w;      // 64 codes of this lane's channel
-    uint4 xb[8];  // B operand pieces (8 activations each), zero on idle lanes
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void load_slab(SlabRegs &r, const uint8_t *prow, const uint16_t *xrow,
-                                          int s, int k_lane, int K, bool row_ok, bool b_on)
+// Copy x[:, k0 : k0 + kc] into xs[t][kk] (t < M) with direct global->LDS
+// loads, one 16-byte piece per lane; pieces past K are written as zeros, so
+// codes read past the end of a row (clamped loads below) meet zero activations.
+__device__ __forceinline__ void stage_x(const uint16_t *x, uint16_t *xs, int M, int K, int k0,
+                                        int kc, int wave, int lane)
 {
-    const bool in_k = k_lane < K;
-    r.w = make_uint4(0, 0, 0, 0);
-    if (row_ok && in_k)
-        r.w = *reinterpret_cast<const uint4 *>(prow + (int64_t)s * 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        r.xb[i] = make_uint4(0, 0, 0, 0);
-    if (b_on && in_k) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(xrow + (int64_t)s * 256);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            r.xb[i] = src[i];
+    const int per_tok = kc >> 3;
+    const int pieces = M * per_tok;
+    for (int v = wave * 64; v < pieces; v += kThreads) {
+        const int idx = v + lane;
+        if (idx < pieces) {
+            const int t = idx / per_tok;
+            const int k = k0 + ((idx - t * per_tok) << 3);
+            if (k < K)
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void *>(x + (int64_t)t * K + k),
+                    (lds_void *)(xs + v * 8), 16, 0, 0);
+            else
+                *reinterpret_cast<uint4 *>(xs + idx * 8) = make_uint4(0, 0, 0, 0);
+        }
     }
 }
 
 template <bool FP16, bool GROUPED>
-__global__ void __launch_bounds__(1024)
-    gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N, int K)
+__global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
 {
-    extern __shared__ f32x4_t red[];  // [waves][64]
+    // LDS: [4][64] fp32x4 reduction tiles | scales [RB][K/128][16] | x [M][kc]
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int rb = blockIdx.x;
-    const int g = lane >> 4;          // lane group: which 64-code quarter of the slab
-    const int col = lane & 15;        // MFMA column
-    const int tok = col >> 1;         // token of this column
+    int pi = 0;
+    for (int i = 1; i < batch.count; ++i)
+        if ((int)blockIdx.x >= batch.p[i].unit0)
+            pi = i;
+    const GemvProblem &P = batch.p[pi];
+    const uint16_t *__restrict__ x = P.x;
+    const uint8_t *__restrict__ packed = P.packed;
+    const uint16_t *__restrict__ scale = P.scale;
+    const int M = P.M, N = P.N, K = P.K, RB = P.rb, kc = P.kc;
+    constexpr bool grouped = GROUPED;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int KP = 4 / RB;
+    const int rbi = wave % RB;        // which of the workgroup's channel blocks
+    const int kp = wave / RB;         // which K part of that block
+    const int blk0 = ((int)blockIdx.x - P.unit0) * RB;
+    const int rb = blk0 + rbi;
+    const int g = lane >> 4;          // lane group: which 64-code quarter of a slab
+    const int col = lane & 15;        // MFMA column (B) and row (A) index of this lane
+    const int tok = col >> 1;         // token of this B column
     const int par = col & 1;          // 128-group of the slab this column collects
     const int row = rb * 16 + col;    // channel whose codes this lane loads (A row)
     const bool row_ok = row < N;
-    const bool b_on = tok < M && (g >> 1) == par;
+    const bool b_lane = tok < M && (g >> 1) == par;
     const int nslabs = (K + 255) >> 8;
     const int ngroups = K >> 7;
+    const int s_begin = kp * P.spart;
+    const int s_end = s_begin + P.spart < nslabs ? s_begin + P.spart : nslabs;
+    const int chunk_slabs = kc >> 8;
 
-    const uint8_t *prow = packed + (int64_t)row * (K >> 2) + g * 16;
-    const uint16_t *xrow = x + (int64_t)(tok < M ? tok : 0) * K + g * 64;
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+    uint16_t *sc = reinterpret_cast<uint16_t *>(smem + 4 * 1024);
+    uint16_t *xs = sc + (grouped ? ((RB * ngroups * 16 + 7) & ~7) : 0);
+
+    // Packed codes: every load is in bounds.  Rows past N read row N-1 (their
+    // C rows are never stored); slabs past this wave's range repeat its last
+    // slab (never decoded); a slab quarter past K reads the row's last 16
+    // bytes (its activations are zero in LDS).
+    const int rowbytes = K >> 2;
+    const uint8_t *prow = packed + (int64_t)(row_ok ? row : N - 1) * rowbytes;
+    const int s_last = s_end > s_begin ? s_end - 1 : s_begin;
+    auto load_group = [&](uint4 (&buf)[kGroup], int s0) {
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            const int s = s0 + i < s_last ? s0 + i : s_last;
+            int off = s * 64 + g * 16;
+            off = off + 16 <= rowbytes ? off : rowbytes - 16;
+            buf[i] = *reinterpret_cast<const uint4 *>(prow + off);
+        }
+    };
+    uint4 wa[kGroup], wb[kGroup];
+    if (s_begin < s_end)
+        load_group(wa, s_begin);
+
+    // Per-channel scales of this lane's four C rows (epilogue lanes only).
+    float sc_pc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!GROUPED && kp == 0 && par == 0 && tok < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ch = rb * 16 + 4 * g + r;
+            if (ch < N)
+                sc_pc[r] = f16_bits_to_f32(scale[ch]);
+        }
+    }
+    if constexpr (GROUPED) {
+        // sc[(bi*ngroups + gr)*16 + r] = scale of channel (blk0 + bi)*16 + r, group gr
+        for (int e = tid; e < RB * 16 * ngroups; e += kThreads) {
+            const int rr = e / ngroups, gr = e - rr * ngroups;
+            const int ch = blk0 * 16 + rr;
+            sc[((rr >> 4) * ngroups + gr) * 16 + (rr & 15)] =
+                ch < N ? scale[(int64_t)ch * ngroups + gr] : (uint16_t)0;
+        }
+    }
+    stage_x(x, xs, M, K, 0, kc, wave, lane);
+    __syncthreads();
+    int chunk = 0;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    SlabRegs cur, nxt;
-    int s = wave;
-    if (s < nslabs)
-        load_slab(nxt, prow, xrow, s, s * 256 + g * 64, K, row_ok, b_on);
-    for (; s < nslabs; s += nwaves) {
-        cur = nxt;
-        const int sn = s + nwaves;
-        if (sn < nslabs)
-            load_slab(nxt, prow, xrow, sn, sn * 256 + g * 64, K, row_ok, b_on);
+    // B operand pieces (two per decoded word).  Lanes without real B entries
+    // keep zeros for the whole kernel; lanes with them overwrite both each time.
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
 
-        const uint32_t wv[4] = {cur.w.x, cur.w.y, cur.w.z, cur.w.w};
-        f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t a[8];
-            decode16(wv[d], a);
-            part = mfma16x16x32<FP16>(a, cur.xb[2 * d], part);
-            part = mfma16x16x32<FP16>(a + 4, cur.xb[2 * d + 1], part);
+    // Decode + MFMA one held group of slabs starting at s0.
+    auto compute_group = [&](const uint4 (&buf)[kGroup], int s0) {
+        const int c = s0 / chunk_slabs;
+        if (c != chunk) {
+            // Only when x is chunked: then KP == 1 and every wave of the
+            // workgroup reaches this point at the same iteration.
+            __syncthreads();
+            stage_x(x, xs, M, K, c * kc, kc, wave, lane);
+            __syncthreads();
+            chunk = c;
         }
-        if constexpr (GROUPED) {
-            // C rows of this lane: channels rb*16 + 4g + r; column group par.
-            const int grp = 2 * s + par;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ch = rb * 16 + 4 * g + r;
-                float sc = 0.f;
-                if (ch < N && grp < ngroups)
-                    sc = f16_bits_to_f32(scale[(int64_t)ch * ngroups + grp]);
-                acc[r] += sc * part[r];
+        for (int i = 0; i < kGroup; ++i) {
+            const int s = s0 + i;
+            if (s >= s_end)
+                break;
+            const uint4 *xb = reinterpret_cast<const uint4 *>(
+                xs + tok * kc + (s - chunk * chunk_slabs) * 256 + g * 64);
+            const uint32_t wv[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+            f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                if (b_lane) {
+                    b0 = xb[2 * d];
+                    b1 = xb[2 * d + 1];
+                }
+                uint32_t a[8];
+                decode16(wv[d], a);
+                part = mfma16x16x32<FP16>(a, b0, part);
+                part = mfma16x16x32<FP16>(a + 4, b1, part);
             }
-        } else {
-            acc = part;
+            if constexpr (GROUPED) {
+                // C rows of this lane: channels rb*16 + 4g + r; column group `par`.
+                const int grp = 2 * s + par;
+                if (grp < ngroups) {
+                    const uint2 s4 = *reinterpret_cast<const uint2 *>(
+                        sc + (rbi * ngroups + grp) * 16 + 4 * g);
+                    acc[0] += f16_bits_to_f32((uint16_t)s4.x) * part[0];
+                    acc[1] += f16_bits_to_f32((uint16_t)(s4.x >> 16)) * part[1];
+                    acc[2] += f16_bits_to_f32((uint16_t)s4.y) * part[2];
+                    acc[3] += f16_bits_to_f32((uint16_t)(s4.y >> 16)) * part[3];
+                }
+            } else {
+                acc = part;
+            }
         }
+    };
+
+    // Two register buffers in turn: the next group's loads are in flight
+    // while the current group is decoded.
+    for (int s0 = s_begin; s0 < s_end; s0 += 2 * kGroup) {
+        if (s0 + kGroup < s_end)
+            load_group(wb, s0 + kGroup);
+        compute_group(wa, s0);
+        if (s0 + kGroup >= s_end)
+            break;
+        if (s0 + 2 * kGroup < s_end)
+            load_group(wa, s0 + 2 * kGroup);
+        compute_group(wb, s0 + kGroup);
     }
 
     red[wave * 64 + lane] = acc;
     __syncthreads();
-    if (wave != 0)
+    if (kp != 0)
         return;
-    f32x4_t sum = red[lane];
-    for (int w = 1; w < nwaves; ++w) {
-        const f32x4_t v = red[w * 64 + lane];
+    f32x4_t sum = acc;
+    for (int j = 1; j < KP; ++j) {
+        const f32x4_t v = red[(rbi + j * RB) * 64 + lane];
         sum[0] += v[0];
         sum[1] += v[1];
         sum[2] += v[2];
         sum[3] += v[3];
     }
+    uint16_t *__restrict__ y = P.y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float tot = sum[r] + __shfl_xor(sum[r], 1);
@@ -148,36 +276,109 @@ __global__ void __launch_bounds__(1024)
         if (par == 0 && tok < M && ch < N) {
             float o = 0.5f * tot;  // decoded weights are +-2
             if constexpr (!GROUPED)
-                o *= f16_bits_to_f32(scale[ch]);
+                o *= sc_pc[r];
             y[(int64_t)tok * N + ch] = round_out<FP16>(o);
         }
     }
 }
 
-template <bool FP16, bool GROUPED>
-hipError_t launch_gemv_t(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
-                         const uint16_t *scale, uint16_t *y, hipStream_t stream)
+// Launch shape of one problem; returns its LDS bytes.
+size_t plan(GemvProblem &p)
 {
-    const int nslabs = (K + 255) / 256;
-    int waves = nslabs / 4;
-    waves = waves < 1 ? 1 : (waves > 16 ? 16 : waves);
-    const int blocks = (N + 15) / 16;
-    const size_t lds = (size_t)waves * 64 * sizeof(f32x4_t);
-    hipLaunchKernelGGL((gemv_kernel<FP16, GROUPED>), dim3(blocks), dim3(64 * waves), lds, stream,
-                       x, packed, scale, y, M, N, K);
+    const int nslabs = (p.K + 255) / 256;
+    p.rb = p.M <= 2 ? 1 : (p.M <= 4 ? 2 : 4);
+    int kc = ((nslabs + 3) / 4) * 1024;  // whole K, padded to a multiple of 1024
+    if ((size_t)p.M * kc * 2 > (size_t)kXLdsBytes) {
+        // x does not fit: walk K in chunks, each wave on a whole channel block
+        p.rb = 4;
+        kc = (kXLdsBytes / (2 * p.M)) / 1024 * 1024;
+    }
+    p.kc = kc;
+    const int KP = 4 / p.rb;
+    p.spart = (nslabs + KP - 1) / KP;
+    return 4 * 1024 + (p.grouped ? (size_t)((p.rb * (p.K / 128) * 16 + 7) & ~7) * 2 : 0) +
+           (size_t)p.M * kc * 2;
+}
+
+int units_of(const GemvProblem &p) { return ((p.N + 15) / 16 + p.rb - 1) / p.rb; }
+
+}  // namespace
+
+namespace {
+
+// One launch for the problems of one scale mode.
+hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool fp16, bool grouped,
+                       hipStream_t stream)
+{
+    GemvBatch b;
+    b.count = 0;
+    size_t lds = 0;
+    int units = 0;
+    for (int oi = 0; oi < count; ++oi) {
+        const GemvArgs &a = args[order[oi]];
+        if (a.M == 0 || a.N == 0 || a.grouped != grouped)
+            continue;
+        GemvProblem &p = b.p[b.count++];
+        p.x = a.x;
+        p.packed = a.packed;
+        p.scale = a.scale;
+        p.y = a.y;
+        p.M = a.M;
+        p.N = a.N;
+        p.K = a.K;
+        p.grouped = grouped ? 1 : 0;
+        const size_t l = plan(p);
+        lds = l > lds ? l : lds;
+        p.unit0 = units;
+        units += units_of(p);
+    }
+    if (b.count == 0)
+        return hipSuccess;
+    if (fp16) {
+        if (grouped)
+            hipLaunchKernelGGL((gemv_kernel<true, true>), dim3(units), dim3(kThreads), lds, stream, b);
+        else
+            hipLaunchKernelGGL((gemv_kernel<true, false>), dim3(units), dim3(kThreads), lds, stream, b);
+    } else {
+        if (grouped)
+            hipLaunchKernelGGL((gemv_kernel<false, true>), dim3(units), dim3(kThreads), lds, stream, b);
+        else
+            hipLaunchKernelGGL((gemv_kernel<false, false>), dim3(units), dim3(kThreads), lds, stream,
+                               b);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
+{
+    if (count < 1 || count > kGemvMaxBatch)
+        return hipErrorInvalidValue;
+    // Longest workgroups first (most K each), so they start early and the
+    // short ones fill in behind them.
+    int order[kGemvMaxBatch];
+    for (int i = 0; i < count; ++i)
+        order[i] = i;
+    for (int i = 1; i < count; ++i)
+        for (int j = i; j > 0 && args[order[j]].K > args[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    // Per-channel and group-scaled problems are separate kernels (one launch
+    // each, only when the batch holds both).
+    hipError_t e = launch_mode(args, order, count, fp16, false, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_mode(args, order, count, fp16, true, stream);
+}
+
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
 {
-    if (fp16)
-        return grouped ? launch_gemv_t<true, true>(x, M, N, K, packed, scale, y, stream)
-                       : launch_gemv_t<true, false>(x, M, N, K, packed, scale, y, stream);
-    return grouped ? launch_gemv_t<false, true>(x, M, N, K, packed, scale, y, stream)
-                   : launch_gemv_t<false, false>(x, M, N, K, packed, scale, y, stream);
+    const GemvArgs a = {x, packed, scale, y, M, N, K, grouped};
+    return launch_gemv_batch(&a, 1, fp16, stream);
 }
 
 }  // namespace ternary

@@ -8,6 +8,18 @@ namespace ternary {
 
 // Largest M the decode GEMV takes (two MFMA B columns per token, 16 columns).
 constexpr int kGemvMaxM = 8;
+// Most projections one fused decode launch takes.
+constexpr int kGemvMaxBatch = 8;
+
+// One decode GEMV problem (shapes already validated).
+struct GemvArgs {
+    const uint16_t *x;
+    const uint8_t *packed;
+    const uint16_t *scale;
+    uint16_t *y;
+    int M, N, K;
+    bool grouped;
+};
 
 hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,
                        hipStream_t stream);
@@ -17,13 +29,20 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t nbytes, int8_t *q, hipSt
 // group_size is -1 or 128, shapes already validated by the caller.
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+// Up to kGemvMaxBatch decode problems in one launch (all gemv_takes()).
+hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                          const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
 
 // Shape requirements of the fast kernels.
-inline bool gemv_takes(int64_t M, int64_t K) { return M >= 1 && M <= kGemvMaxM && K % 128 == 0; }
+// The GEMV stages a workgroup's group scales (K/4 bytes) in LDS, so K is capped.
+constexpr int64_t kGemvMaxK = 65536;
+inline bool gemv_takes(int64_t M, int64_t K)
+{
+    return M >= 1 && M <= kGemvMaxM && K % 128 == 0 && K <= kGemvMaxK;
+}
 inline bool gemm_takes(int64_t M, int64_t K) { return M >= 1 && K % 128 == 0; }
 
 }  // namespace ternary

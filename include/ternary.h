@@ -125,6 +125,37 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
                       const uint8_t *packed, const uint16_t *scale, int64_t group_size,
                       void *y, int path, hipStream_t stream);
 
+/* Most problems one ternary_linear_batch call takes. */
+#define TERNARY_MAX_BATCH 8
+
+/* One projection of a batched call: the arguments of ternary_linear. */
+typedef struct {
+    const void *x;          /* [M, K] activations, 16-byte aligned                  */
+    const uint8_t *packed;  /* [N, K/4] codes, 16-byte aligned                      */
+    const uint16_t *scale;  /* fp16 [N] or [N, K/128], 2-byte aligned               */
+    void *y;                /* [M, N] output, 16-byte aligned                       */
+    int64_t M, N, K;        /* as for ternary_linear                                */
+    int64_t group_size;     /* -1 or 128                                            */
+} ternary_problem;
+
+/*
+ * ternary_linear_batch - several independent ternary_linear problems in as
+ * few launches as possible, for the projections of one layer: the segments of
+ * a fused QKV (or gate+up) weight, each with its own packed rows and scales
+ * ([trdm §2.2]), or any set of projections that are ready together.
+ *   problems  host array of `count` problems (1 <= count <= TERNARY_MAX_BATCH),
+ *             read during the call only.
+ *   dtype     activation/output dtype shared by all problems.
+ * Every problem is validated as by ternary_linear; in addition no output may
+ * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
+ * any error nothing is launched.  Problems the decode GEMV takes (1 <= M <=
+ * ternary_gemv_max_m(), K % 128 == 0) run together in one launch per scale
+ * mode (per-channel, group-128); the others run as separate launches on the
+ * same stream.  Results are bitwise equal to ternary_linear on each problem.
+ */
+int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
+                         hipStream_t stream);
+
 /* The path ternary_linear_ex(..., TERNARY_PATH_AUTO, ...) takes for a shape
  * (a ternary_path value), or a negative status for invalid shapes. */
 int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size);

@@ -139,3 +139,33 @@ def test_select_path_rejects(tl):
     L = tl.lib()
     assert L.ternary_select_path(1, 16, 130, -1) == -2
     assert L.ternary_select_path(1, 16, 256, 64) == -3
+
+
+def _prob(tl, x, p, s, y, M=1, N=16, K=128, g=128):
+    return tl.Problem(x, p, s, y, M, N, K, g)
+
+
+def test_batch_rejects(tl):
+    L = tl.lib()
+    P = tl.Problem
+    ok1 = _prob(tl, FAKE, FAKE * 2, FAKE * 3, FAKE * 4)
+    ok2 = _prob(tl, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8)
+    arr = (P * 2)(ok1, ok2)
+    assert L.ternary_linear_batch(None, 1, 0, None) == -1
+    assert L.ternary_linear_batch(arr, 0, 0, None) == -2
+    assert L.ternary_linear_batch(arr, 9, 0, None) == -2
+    assert L.ternary_linear_batch(arr, 2, 5, None) == -4
+    # second output overlaps the first problem's activations
+    bad = (P * 2)(ok1, _prob(tl, FAKE * 5, FAKE * 6, FAKE * 7, FAKE + 64))
+    assert L.ternary_linear_batch(bad, 2, 0, None) == -6
+    # two outputs overlap each other
+    bad2 = (P * 2)(ok1, _prob(tl, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 4 + 16))
+    assert L.ternary_linear_batch(bad2, 2, 0, None) == -6
+    # an invalid member fails the whole batch with its own status
+    bad3 = (P * 2)(ok1, _prob(tl, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, K=130, g=-1))
+    assert L.ternary_linear_batch(bad3, 2, 0, None) == -2
+    bad4 = (P * 2)(ok1, _prob(tl, FAKE * 5, 0, FAKE * 7, FAKE * 8))
+    assert L.ternary_linear_batch(bad4, 2, 0, None) == -1
+    # all members empty: success without any launch
+    empty = (P * 2)(_prob(tl, 0, 0, 0, 0, M=0), _prob(tl, 0, 0, 0, 0, N=0))
+    assert L.ternary_linear_batch(empty, 2, 0, None) == 0

@@ -1,0 +1,91 @@
+"""ternary_linear_batch: one fused decode launch for several projections.
+
+Each output must equal the single-problem ternary_linear result bit for bit
+(the fused launch runs the same per-problem kernel code) and lie within the
+bound of the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bits_of, check_within, say, to_dev, widen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tl():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_ternary_linear_amd as tl
+    tl.lib()
+    return tl
+
+
+def _problems(rng, specs, dtype="bf16"):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    out = []
+    for M, N, K, g in specs:
+        codes = synth.draw_codes(rng, N, K, 0.3, 0.3)
+        packed, _ = oracle.pack(codes)
+        scale = synth.draw_scales(rng, N, K, g)
+        x = synth.draw_x(rng, M, K, dtype)
+        out.append((x, packed, scale, g,
+                    (to_dev(x, tdt), to_dev(packed, None), to_dev(scale, torch.float16), g)))
+    return out
+
+
+def _run_and_check(tl, probs, dtype="bf16", samples=None):
+    import torch
+    singles = [tl.linear(*d) for *_, d in probs]
+    outs = tl.linear_batch([(d[0], d[1], d[2], d[3], None) for *_, d in probs])
+    torch.cuda.synchronize()
+    for i, ((x, packed, scale, g, _), a, b) in enumerate(zip(probs, singles, outs)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"problem {i} differs"
+        yv = widen(bits_of(b), dtype)
+        if samples is None:
+            y_ref, bound = oracle.linear(x, packed, scale, g, dtype=dtype)
+            check_within(yv, y_ref, bound, f"batch problem {i}",
+                         out_rounding=dtype if x.shape[1] < 256 else None)
+        else:
+            rng = np.random.default_rng(i)
+            M, N = yv.shape
+            ms, ns = rng.integers(0, M, samples), rng.integers(0, N, samples)
+            y_ref, bound = oracle.linear_at(x, packed, scale, g, ms, ns, dtype=dtype)
+            check_within(yv[ms, ns], y_ref, bound, f"batch problem {i}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_batch_7b_decode_layer(tl, M):
+    say(f"batch of the 7 decode projections, M={M}")
+    specs = [(M, s.N, s.K, -1) for s in synth.CONFIGS[2].shapes]
+    _run_and_check(tl, _problems(np.random.default_rng(40 + M), specs), samples=800)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_batch_mixed(tl, dtype):
+    say(f"mixed batch (GEMV + GEMM + plain kernel) {dtype}")
+    specs = [(1, 300, 1024, 128), (3, 65, 2304, -1), (8, 129, 9216, 128), (64, 100, 512, 128),
+             (2, 40, 132, -1), (5, 1, 128, 128), (1, 2000, 640, -1)]
+    _run_and_check(tl, _problems(np.random.default_rng(41), specs, dtype), dtype=dtype)
+
+
+def test_batch_big_k_chunked(tl):
+    say("batch with chunked activations (M=8, K=18944; M=4, K=25600)")
+    specs = [(8, 200, 18944, -1), (4, 100, 25600, 128), (8, 64, 5120, 128)]
+    _run_and_check(tl, _problems(np.random.default_rng(42), specs), samples=600)
+
+
+def test_batch_rejects_alias_on_device(tl):
+    import torch
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda:0")
+    p = torch.zeros((16, 64), dtype=torch.uint8, device="cuda:0")
+    s = torch.ones((16, 2), dtype=torch.float16, device="cuda:0")
+    y = torch.empty((1, 16), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(tl.TernaryError) as e:
+        tl.linear_batch([(x, p, s, 128, y), (x, p, s, 128, y)])
+    assert e.value.status == -6
