@@ -12,9 +12,9 @@
 // launch, which pays the fixed launch and first-byte latency once.
 //
 // Mapping onto CDNA4:
-//  * A workgroup is 4 waves and owns RB blocks of 16 output channels (RB =
-//    1, 2 or 4 by M): each wave takes one block and 1/KP of its K slabs
-//    (KP = 4/RB), a slab being 256 codes (64 bytes) of every channel.
+//  * A workgroup is 4 waves and owns RB blocks of 16 output channels: each
+//    wave takes one block and 1/KP of its K slabs (KP = 4/RB, chosen by K and
+//    M), a slab being 256 codes (64 bytes) of every channel.
 //  * Per slab a lane issues ONE 16-byte load of packed codes: lane l reads
 //    channel (l & 15), bytes [16*(l>>4), +16) of the slab, so a wave reads
 //    16 channels x 64 contiguous bytes per instruction.  Slabs stream in
@@ -88,27 +88,29 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void stage_x(const uint16_t *x, uint16_t *xs, int M, int K, int k0,
                                         int kc, int wave, int lane)
 {
-    const int per_tok = kc >> 3;
-    const int pieces = M * per_tok;
-    for (int v = wave * 64; v < pieces; v += kThreads) {
-        const int idx = v + lane;
-        if (idx < pieces) {
-            const int t = idx / per_tok;
-            const int k = k0 + ((idx - t * per_tok) << 3);
-            if (k < K)
-                __builtin_amdgcn_global_load_lds(
-                    reinterpret_cast<const void *>(x + (int64_t)t * K + k),
-                    (lds_void *)(xs + v * 8), 16, 0, 0);
-            else
-                *reinterpret_cast<uint4 *>(xs + idx * 8) = make_uint4(0, 0, 0, 0);
+    const int per_tok = kc >> 3;  // 16-byte pieces per token
+    for (int t = 0; t < M; ++t) {
+        const uint16_t *src = x + (int64_t)t * K + k0;
+        uint16_t *dst = xs + t * kc;
+        for (int v = wave * 64; v < per_tok; v += kThreads) {
+            const int p = v + lane;
+            if (p < per_tok) {
+                if (k0 + p * 8 < K)
+                    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + p * 8),
+                                                     (lds_void *)(dst + v * 8), 16, 0, 0);
+                else
+                    *reinterpret_cast<uint4 *>(dst + p * 8) = make_uint4(0, 0, 0, 0);
+            }
         }
     }
 }
 
 template <bool FP16, bool GROUPED>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8)))
+gemv_kernel(const GemvBatch batch)
 {
-    // LDS: [4][64] fp32x4 reduction tiles | scales [RB][K/128][16] | x [M][kc]
+    // LDS: [4][64] fp32x4 reduction tiles | scales ([RB][K/128][16] grouped,
+    // [RB*16] per channel, 128 bytes) | x [M][kc]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     int pi = 0;
@@ -145,7 +147,7 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
 
     f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
     uint16_t *sc = reinterpret_cast<uint16_t *>(smem + 4 * 1024);
-    uint16_t *xs = sc + (grouped ? ((RB * ngroups * 16 + 7) & ~7) : 0);
+    uint16_t *xs = sc + (GROUPED ? ((RB * ngroups * 16 + 7) & ~7) : 64);
 
     // Packed codes: every load is in bounds.  Rows past N read row N-1 (their
     // C rows are never stored); slabs past this wave's range repeat its last
@@ -167,16 +169,6 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
     if (s_begin < s_end)
         load_group(wa, s_begin);
 
-    // Per-channel scales of this lane's four C rows (epilogue lanes only).
-    float sc_pc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (!GROUPED && kp == 0 && par == 0 && tok < M) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ch = rb * 16 + 4 * g + r;
-            if (ch < N)
-                sc_pc[r] = f16_bits_to_f32(scale[ch]);
-        }
-    }
     if constexpr (GROUPED) {
         // sc[(bi*ngroups + gr)*16 + r] = scale of channel (blk0 + bi)*16 + r, group gr
         for (int e = tid; e < RB * 16 * ngroups; e += kThreads) {
@@ -184,6 +176,12 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
             const int ch = blk0 * 16 + rr;
             sc[((rr >> 4) * ngroups + gr) * 16 + (rr & 15)] =
                 ch < N ? scale[(int64_t)ch * ngroups + gr] : (uint16_t)0;
+        }
+    } else {
+        // sc[r] = scale of channel blk0*16 + r (read by the epilogue)
+        if (tid < RB * 16) {
+            const int ch = blk0 * 16 + tid;
+            sc[tid] = ch < N ? scale[ch] : (uint16_t)0;
         }
     }
     stage_x(x, xs, M, K, 0, kc, wave, lane);
@@ -276,17 +274,23 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(const GemvBatch batch)
         if (par == 0 && tok < M && ch < N) {
             float o = 0.5f * tot;  // decoded weights are +-2
             if constexpr (!GROUPED)
-                o *= sc_pc[r];
+                o *= f16_bits_to_f32(sc[rbi * 16 + 4 * g + r]);
             y[(int64_t)tok * N + ch] = round_out<FP16>(o);
         }
     }
 }
 
-// Launch shape of one problem; returns its LDS bytes.
+// Launch shape of one problem; returns its LDS bytes.  The K split KP (waves
+// per channel block) keeps a wave's slab run long enough to amortise its
+// fixed costs but bounded for long K; larger M puts more channel blocks in a
+// workgroup so the x it stages serves more rows.
 size_t plan(GemvProblem &p)
 {
     const int nslabs = (p.K + 255) / 256;
-    p.rb = p.M <= 2 ? 1 : (p.M <= 4 ? 2 : 4);
+    int kp = nslabs >= 32 ? 4 : (nslabs >= 8 ? 2 : 1);
+    if (p.M >= 3 && kp > 1)
+        kp = p.M >= 5 ? 1 : 2;
+    p.rb = 4 / kp;
     int kc = ((nslabs + 3) / 4) * 1024;  // whole K, padded to a multiple of 1024
     if ((size_t)p.M * kc * 2 > (size_t)kXLdsBytes) {
         // x does not fit: walk K in chunks, each wave on a whole channel block
@@ -296,7 +300,7 @@ size_t plan(GemvProblem &p)
     p.kc = kc;
     const int KP = 4 / p.rb;
     p.spart = (nslabs + KP - 1) / KP;
-    return 4 * 1024 + (p.grouped ? (size_t)((p.rb * (p.K / 128) * 16 + 7) & ~7) * 2 : 0) +
+    return 4 * 1024 + (p.grouped ? (size_t)((p.rb * (p.K / 128) * 16 + 7) & ~7) * 2 : 128) +
            (size_t)p.M * kc * 2;
 }
 
@@ -366,12 +370,34 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             order[j] = order[j - 1];
             order[j - 1] = t;
         }
-    // Per-channel and group-scaled problems are separate kernels (one launch
-    // each, only when the batch holds both).
-    hipError_t e = launch_mode(args, order, count, fp16, false, stream);
-    if (e != hipSuccess)
-        return e;
-    return launch_mode(args, order, count, fp16, true, stream);
+    // Per-channel and group-scaled problems are separate kernels, and so are
+    // the problems the streaming kernel takes (M <= 2) and the others: one
+    // launch per non-empty class.
+    for (int mode = 0; mode < 2; ++mode) {
+        const bool grouped = mode == 1;
+        int stream_idx[kGemvMaxBatch], other_idx[kGemvMaxBatch];
+        int ns = 0, no = 0;
+        for (int oi = 0; oi < count; ++oi) {
+            const GemvArgs &a = args[order[oi]];
+            if (a.grouped != grouped || a.M == 0 || a.N == 0)
+                continue;
+            if (gemv_stream_takes(a.M, a.K, grouped))
+                stream_idx[ns++] = order[oi];
+            else
+                other_idx[no++] = order[oi];
+        }
+        if (ns > 0) {
+            const hipError_t e = launch_gemv_stream(args, stream_idx, ns, fp16, grouped, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+        if (no > 0) {
+            const hipError_t e = launch_mode(args, other_idx, no, fp16, grouped, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,

@@ -1,8 +1,9 @@
 """ternary_linear_batch: one fused decode launch for several projections.
 
-Each output must equal the single-problem ternary_linear result bit for bit
-(the fused launch runs the same per-problem kernel code) and lie within the
-bound of the oracle.
+Each output must lie within the bound of the oracle, and a batch must give
+the same bits every time it runs.  Batched and single calls may differ in the
+last bits (the batch plans its K split over all of its problems), so each is
+checked against the oracle on its own.
 """
 
 import numpy as np
@@ -43,20 +44,24 @@ def _run_and_check(tl, probs, dtype="bf16", samples=None):
     import torch
     singles = [tl.linear(*d) for *_, d in probs]
     outs = tl.linear_batch([(d[0], d[1], d[2], d[3], None) for *_, d in probs])
+    again = tl.linear_batch([(d[0], d[1], d[2], d[3], None) for *_, d in probs])
     torch.cuda.synchronize()
-    for i, ((x, packed, scale, g, _), a, b) in enumerate(zip(probs, singles, outs)):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"problem {i} differs"
+    for i, ((x, packed, scale, g, _), a, b, c) in enumerate(zip(probs, singles, outs, again)):
+        assert torch.equal(b.view(torch.int16), c.view(torch.int16)), f"problem {i} not repeatable"
         yv = widen(bits_of(b), dtype)
+        ya = widen(bits_of(a), dtype)
         if samples is None:
             y_ref, bound = oracle.linear(x, packed, scale, g, dtype=dtype)
-            check_within(yv, y_ref, bound, f"batch problem {i}",
-                         out_rounding=dtype if x.shape[1] < 256 else None)
+            rounding = dtype if x.shape[1] < 256 else None
+            check_within(yv, y_ref, bound, f"batch problem {i}", out_rounding=rounding)
+            check_within(ya, y_ref, bound, f"single problem {i}", out_rounding=rounding)
         else:
             rng = np.random.default_rng(i)
             M, N = yv.shape
             ms, ns = rng.integers(0, M, samples), rng.integers(0, N, samples)
             y_ref, bound = oracle.linear_at(x, packed, scale, g, ms, ns, dtype=dtype)
             check_within(yv[ms, ns], y_ref, bound, f"batch problem {i}")
+            check_within(ya[ms, ns], y_ref, bound, f"single problem {i}")
 
 
 @pytest.mark.parametrize("M", [1, 8])

@@ -80,6 +80,29 @@ def test_linear_auto_small(tl, M, N, K, g, dtype):
     check_within(y, y_ref, bound, f"auto M={M} N={N} K={K} g={g} {dtype}")
 
 
+# Decode shapes at M <= 2 aimed at the streaming kernel's limits: K split in
+# 1, 2 or 4 parts, a part of exactly 20 slabs (the whole ring), x staging of
+# exactly 40 KB, a workgroup scale slice of exactly 2560 entries, a half slab
+# at the end of K, ragged N, and small launches whose K split is raised to
+# fill the chip.
+STREAM = [
+    (1, 40, 20480, 128), (1, 50, 18944, -1), (2, 45, 10240, -1), (2, 77, 6272, 128),
+    (1, 4100, 4096, -1), (2, 19, 5248, 128), (1, 600, 3200, 128), (2, 1, 8192, -1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K,g", STREAM)
+def test_linear_stream_decode(tl, M, N, K, g, dtype):
+    say(f"linear stream decode M={M} N={N} K={K} g={g} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr(("stream", M, N, K, g, dtype)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, g, dtype)
+    assert tl.select_path(M, N, K, g) == "gemv"
+    y_ref, bound = oracle.linear(x, packed, scale, g, dtype=dtype)
+    y = _run(tl, x, packed, scale, g, dtype, codes=codes)
+    check_within(y, y_ref, bound, f"stream M={M} N={N} K={K} g={g} {dtype}")
+
+
 @pytest.mark.parametrize("path", ["gemv", "gemm", "simple"])
 @pytest.mark.parametrize("M", [1, 4, 8])
 @pytest.mark.parametrize("g", [128, -1])
