@@ -371,23 +371,25 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             order[j - 1] = t;
         }
     // Per-channel and group-scaled problems are separate kernels, and so are
-    // the problems the streaming kernel takes (M <= 2) and the others: one
-    // launch per non-empty class.
+    // the problems the streaming kernel takes (M = 1, M = 2) and the others:
+    // one launch per non-empty class.
     for (int mode = 0; mode < 2; ++mode) {
         const bool grouped = mode == 1;
-        int stream_idx[kGemvMaxBatch], other_idx[kGemvMaxBatch];
-        int ns = 0, no = 0;
+        int stream_idx[kGemvStreamMaxM][kGemvMaxBatch], other_idx[kGemvMaxBatch];
+        int ns[kGemvStreamMaxM] = {}, no = 0;
         for (int oi = 0; oi < count; ++oi) {
             const GemvArgs &a = args[order[oi]];
             if (a.grouped != grouped || a.M == 0 || a.N == 0)
                 continue;
             if (gemv_stream_takes(a.M, a.K, grouped))
-                stream_idx[ns++] = order[oi];
+                stream_idx[a.M - 1][ns[a.M - 1]++] = order[oi];
             else
                 other_idx[no++] = order[oi];
         }
-        if (ns > 0) {
-            const hipError_t e = launch_gemv_stream(args, stream_idx, ns, fp16, grouped, stream);
+        for (int m = 0; m < kGemvStreamMaxM; ++m) {
+            if (ns[m] == 0)
+                continue;
+            const hipError_t e = launch_gemv_stream(args, stream_idx[m], ns[m], fp16, grouped, stream);
             if (e != hipSuccess)
                 return e;
         }

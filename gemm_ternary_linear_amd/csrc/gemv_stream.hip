@@ -3,72 +3,90 @@
 // The layer ([xxqk] m.xxqk.cn/news/593501 §4.3: y = x @ (unpack(q) * s)^T)
 // at one or two tokens reads every packed weight byte once and does little
 // arithmetic per byte, so its speed is the HBM stream ([nxbn]
-// m.nxbn.cn/news/169761 §4.1/§4.4).  This kernel is built so that the stream
-// starts at the first instruction and never waits on anything else:
+// m.nxbn.cn/news/169761 §4.1/§4.4).  The kernel is shaped by how gfx950
+// serves such a stream (measured on MI355X):
 //
-//  * Every wave owns one block of 16 output channels and one K part of at
-//    most kRing slabs (a slab = 256 codes = 64 bytes of each of the 16 rows),
-//    and issues ALL of its slab loads before it does anything else.  The
-//    number of loads is fixed per kernel instance: slots past the wave's K
-//    part use a buffer offset outside the resource, which returns zeros and
-//    touches no memory.  With a fixed count the compiler's vmcnt waits are
-//    exact, so slab i is consumed as soon as it has landed while later slabs
-//    are still in flight.
-//  * Rows past N and codes past the end of the weight matrix are outside
-//    the buffer resource of their block as well (zeros), so no load is
-//    clamped or branched around.
-//  * The activation x of the workgroup (all M tokens, whole K, slab-major in
-//    LDS) is fetched through registers with buffer loads issued before the
-//    slab loads; pieces past K read as zeros.  Only these x loads gate the
-//    LDS writes and the one workgroup barrier; the slab loads issued before
-//    that point stay in flight across it.  (Direct global->LDS copies would
-//    make the compiler wait for every outstanding load before the first LDS
-//    read.)
-//  * Decoding and MFMA are the same as in the general decode kernel: each
-//    32-bit word of codes becomes 16 bf16/fp16 weights of +-2 or 0 in
-//    registers (decode16), the A operand of v_mfma_f32_16x16x32_{bf16,f16}
-//    (rows = channels); B column 2t+p holds token t restricted to 128-group
-//    p of the slab, so group-128 scales ([trdm] trdm.cn
-//    "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1/§4.2) apply
-//    to each group's fp32 partial, and per-channel scales ([nxbn] §3.2) to
-//    the final sum.
-//  * K parts of a channel block (KP = 1, 2 or 4 waves) are reduced through
-//    LDS in a fixed order, reusing the x region after a barrier, so the LDS
-//    of a workgroup is x plus its scales: the K = 18944 projection at M = 1
-//    needs 38 KB and four workgroups still fit a CU.
+//  * HBM is fastest when the 16 rows x 1 KB of a block of output channels
+//    are requested together by several waves with a few loads each; one wave
+//    streaming a whole block alone, or a wave with many loads in flight, is
+//    markedly slower.  So a channel block's K range is split over KP waves
+//    (KP up to 16) and every wave issues all loads of its short K part
+//    (S <= kMaxS slabs; a slab = 256 codes = 64 bytes of each of the 16 rows)
+//    at once, as its first instructions.  Workgroups are short-lived; the
+//    dispatcher keeps the CUs supplied.
+//  * A wave's loads return in issue order, so each slab's activations (512
+//    bytes per token) are loaded right before that slab's codes: x arrives
+//    with the codes that need it.  (x fetched once per workgroup up front
+//    would queue behind the flood of code requests at the L2 and DRAM and
+//    hold every wave back.)  All 64 lanes load x; the wave moves it into the
+//    lanes that feed the MFMA B operand through two small LDS buffers of its
+//    own (no workgroup barrier).
+//  * The number of loads of a wave is exactly what its part needs: the wave
+//    body is instantiated per part length S (a switch on S), so the compiler's
+//    vmcnt waits are exact and no placeholder load takes a slot in the memory
+//    pipeline.  Buffer loads bound every access: rows past N, codes past the
+//    matrix and x past K read as zeros.
+//  * Decoding and MFMA: each 32-bit word of codes becomes 16 bf16/fp16
+//    weights of +-2 or 0 in registers (decode16), the A operand of
+//    v_mfma_f32_16x16x32_{bf16,f16} (rows = channels); B column 2t+p holds
+//    token t restricted to 128-group p of the slab, so group-128 scales
+//    ([trdm] trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战"
+//    §3.1/§4.2) apply to each group's fp32 partial, and per-channel scales
+//    ([nxbn] §3.2) to the final sum.
+//  * A workgroup holds RB channel blocks x KP K parts (RB * KP <= 16 waves);
+//    the K parts of a block are reduced through LDS in a fixed order.
 #include "common.h"
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace ternary {
 
 namespace {
 
-constexpr int kThreads = 256;          // 4 waves
-constexpr int kRing = 20;              // slab loads per wave, all in flight together
-constexpr int kXPieces = 10;           // 16-byte x pieces staged per thread (x <= 40 KB)
-constexpr int kSPieces = 10;           // group scales staged per thread
-constexpr int kOOB = 0x40000000;       // buffer offset past every resource: reads zero
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxS = 6;             // slabs per wave (all its loads in flight at once)
+// Preferred slabs per wave: 4 (measured best for launches that fill the chip
+// several times over), 2 when that leaves fewer than kFewUnits workgroups.
+constexpr int kTargetS = 4;
+constexpr int kTargetSmall = 2;
+constexpr int kFewUnits = 512;
+constexpr int kOOB = 0x40000000;     // buffer offset past every resource: reads zero
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 struct StreamProblem {
     const uint16_t *x;
     const uint8_t *packed;
     const uint16_t *scale;
     uint16_t *y;
-    int M, N, K;
-    int kp;     // waves (K parts) per 16-channel block: 1, 2 or 4
-    int spart;  // slabs per K part (<= kRing)
+    int N, K;
+    int rb;     // 16-channel blocks per workgroup
+    int kp;     // K parts (waves) per block, rb * kp <= kWaves
+    int spart;  // slabs per K part (<= kMaxS)
     int unit0;  // first workgroup of this problem
+    // wave w -> (block rbi, part kpi) = 4-bit fields w of these maps (15 in
+    // both: the wave holds no part); precomputed so that the kernel's start
+    // needs no division
+    uint64_t rbi_map, kpi_map;
 };
 
+// Kernel argument.  The first workgroup of every problem comes first, in one
+// array, so that a workgroup finds its problem with one round of scalar loads.
 struct StreamBatch {
     int count;
+    int unit0[kGemvMaxBatch];
     StreamProblem p[kGemvMaxBatch];
 };
+
+// LDS per wave: two x buffers of M*256 elements, then (group-scaled) the
+// scales of the wave's 2*kMaxS groups x 16 channels.
+constexpr int kXBufElems = kGemvStreamMaxM * 256;
+constexpr int kWaveLdsElems = 2 * kXBufElems + 2 * kMaxS * 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -89,211 +107,224 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f3
                                                        0);
 }
 
-template <bool FP16, bool GROUPED>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-gemv_stream_kernel(const StreamBatch batch)
+// What one wave needs to run its K part.
+struct WaveCtx {
+    __amdgpu_buffer_rsrc_t xr, wr, sr;
+    int K, ngroups;
+    int s_begin;   // first slab of the part
+    int woff;      // this lane's byte offset of slab 0 in the block resource
+    int lane, g, tok, par;
+    bool b_lane;
+    uint16_t *xbuf;  // this wave's two x buffers
+    uint16_t *sbuf;  // this wave's group scales [2*kMaxS][16]
+    int srow_off;    // grouped: scale offset (bytes) of this lane's row, group 0; < 0: none
+};
+
+// Byte offset of this lane's piece of slab s of x (M = 1: 8 bytes, M = 2:
+// 16 bytes), or kOOB past K.
+template <int MT>
+__device__ __forceinline__ int x_piece_off(const WaveCtx &c, int s)
 {
-    // LDS: x [nslabs][M][256] (reused for the K-part reduction, >= 4 KB when
-    // KP > 1) | scales: grouped [RB][ngroups][16], per channel [RB*16].
+    if constexpr (MT == 1) {
+        const int e = s * 256 + 4 * c.lane;
+        return e < c.K ? e * 2 : kOOB;
+    }
+    const int e = s * 256 + 8 * (c.lane & 31);
+    return e < c.K ? ((c.lane >> 5) * c.K + e) * 2 : kOOB;
+}
+
+// This lane's x piece of one slab: 4 elements (M = 1) or 8 (M = 2).
+template <int MT>
+using XPiece = typename std::conditional<MT == 1, u32x2_t, u32x4_t>::type;
+
+// Store this lane's x piece of a slab into buffer `buf`, laid out [M][256].
+template <int MT>
+__device__ __forceinline__ void x_piece_store(const WaveCtx &c, int buf, XPiece<MT> v)
+{
+    uint16_t *b = c.xbuf + buf * kXBufElems;
+    if constexpr (MT == 1)
+        *reinterpret_cast<u32x2_t *>(b + 4 * c.lane) = v;
+    else
+        *reinterpret_cast<u32x4_t *>(b + (c.lane >> 5) * 256 + 8 * (c.lane & 31)) = v;
+}
+
+template <int MT>
+__device__ __forceinline__ XPiece<MT> x_piece_load(const WaveCtx &c, int s)
+{
+    const int off = x_piece_off<MT>(c, s);
+    if constexpr (MT == 1)
+        return __builtin_amdgcn_raw_buffer_load_b64(c.xr, off, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b128(c.xr, off, 0, 0);
+}
+
+// Run a K part of exactly S slabs; returns this lane's fp32 accumulator
+// (C rows 4g..4g+3 of the block, column 2*tok + par).
+template <bool FP16, bool GROUPED, int MT, int S>
+__device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
+{
+    // ---- issue every load of the part: scales, then (x, codes) per slab ----
+    constexpr int kSL = GROUPED ? (2 * S + 3) / 4 : 0;  // scale loads per lane
+    uint32_t sv[kSL > 0 ? kSL : 1];
+#pragma unroll
+    for (int j = 0; j < kSL; ++j) {
+        // lane l: row l & 15, local group (l >> 4) + 4j of the part's 2S groups
+        const int lg = (c.lane >> 4) + 4 * j;
+        const int gr = 2 * c.s_begin + lg;
+        const int off = (c.srow_off >= 0 && lg < 2 * S && gr < c.ngroups) ? c.srow_off + gr * 2
+                                                                          : kOOB;
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b16(c.sr, off, 0, 0);
+    }
+    XPiece<MT> xv[S];
+    u32x4_t w[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        xv[i] = x_piece_load<MT>(c, c.s_begin + i);
+        w[i] = __builtin_amdgcn_raw_buffer_load_b128(c.wr, c.woff + (c.s_begin + i) * 64, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
+    }
+
+    // ---- scales and the first x piece into this wave's LDS -----------------
+#pragma unroll
+    for (int j = 0; j < kSL; ++j) {
+        const int lg = (c.lane >> 4) + 4 * j;
+        if (lg < 2 * S)
+            c.sbuf[lg * 16 + (c.lane & 15)] = (uint16_t)sv[j];
+    }
+    x_piece_store<MT>(c, 0, xv[0]);
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // B operand pieces: lanes without real B entries keep zeros throughout.
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        // the next slab's x goes into the other buffer while this slab runs
+        if (i + 1 < S)
+            x_piece_store<MT>(c, (i + 1) & 1, xv[i + 1]);
+        __builtin_amdgcn_wave_barrier();
+        const uint4 *xb =
+            reinterpret_cast<const uint4 *>(c.xbuf + (i & 1) * kXBufElems + c.tok * 256 + c.g * 64);
+        const uint32_t wv[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if (c.b_lane) {
+                b0 = xb[2 * d];
+                b1 = xb[2 * d + 1];
+            }
+            uint32_t a[8];
+            decode16(wv[d], a);
+            part = mfma16x16x32<FP16>(a, b0, part);
+            part = mfma16x16x32<FP16>(a + 4, b1, part);
+        }
+        if constexpr (GROUPED) {
+            // C rows of this lane: channels 4g + r of the block; group 2i + par
+            // of the part (scales past K or N were loaded as zeros).
+            const uint2 s4 =
+                *reinterpret_cast<const uint2 *>(c.sbuf + (2 * i + c.par) * 16 + 4 * c.g);
+            acc[0] += f16_bits_to_f32((uint16_t)s4.x) * part[0];
+            acc[1] += f16_bits_to_f32((uint16_t)(s4.x >> 16)) * part[1];
+            acc[2] += f16_bits_to_f32((uint16_t)s4.y) * part[2];
+            acc[3] += f16_bits_to_f32((uint16_t)(s4.y >> 16)) * part[3];
+        } else {
+            acc = part;
+        }
+        // this buffer is rewritten two slabs on; LDS ops of a wave run in order
+        __builtin_amdgcn_wave_barrier();
+    }
+    return acc;
+}
+
+template <bool FP16, bool GROUPED, int MT>
+__device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int S)
+{
+    switch (S) {
+    case 1: return run_part<FP16, GROUPED, MT, 1>(c);
+    case 2: return run_part<FP16, GROUPED, MT, 2>(c);
+    case 3: return run_part<FP16, GROUPED, MT, 3>(c);
+    case 4: return run_part<FP16, GROUPED, MT, 4>(c);
+    case 5: return run_part<FP16, GROUPED, MT, 5>(c);
+    case 6: return run_part<FP16, GROUPED, MT, 6>(c);
+    default: return f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+}
+static_assert(kMaxS == 6, "run_part_n covers S = 1..kMaxS");
+
+template <bool FP16, bool GROUPED, int MT>
+__global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch batch)
+{
+    // LDS: per wave [2][M*256] x buffers + [2*kMaxS][16] group scales; the
+    // K-part reduction reuses it after a barrier.
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     int pi = 0;
-    for (int i = 1; i < batch.count; ++i)
-        if ((int)blockIdx.x >= batch.p[i].unit0)
+#pragma unroll
+    for (int i = 1; i < kGemvMaxBatch; ++i)
+        if (i < batch.count && (int)blockIdx.x >= batch.unit0[i])
             pi = i;
     const StreamProblem &P = batch.p[pi];
-    const int M = P.M, N = P.N, K = P.K, KP = P.kp;
-    const int RB = 4 / KP;
+    constexpr int M = MT;
+    const int N = P.N, K = P.K, RB = P.rb, KP = P.kp;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rbi = wave % RB;   // which of the workgroup's channel blocks
-    const int kp = wave / RB;    // which K part of that block
-    const int blk0 = ((int)blockIdx.x - P.unit0) * RB;
-    const int rb = blk0 + rbi;
-    const int g = lane >> 4;     // lane group: which 64-code quarter of a slab
-    const int col = lane & 15;   // A row / B column / C column of this lane
-    const int tok = col >> 1;    // token of this B column
-    const int par = col & 1;     // 128-group of the slab this column collects
-    const bool b_lane = tok < M && (g >> 1) == par;
+    const int rbi = (int)((P.rbi_map >> (4 * wave)) & 15);  // the workgroup's channel block
+    const int kpi = (int)((P.kpi_map >> (4 * wave)) & 15);  // K part of that block
+    const bool active = kpi < KP;        // waves past RB*KP hold no part
+    const int rb = ((int)blockIdx.x - P.unit0) * RB + rbi;
     const int nslabs = (K + 255) >> 8;
     const int ngroups = K >> 7;
     const int rowbytes = K >> 2;
-    const int s_begin = kp * P.spart;
-    const int S = min(P.spart, nslabs - s_begin);  // slabs of this wave (>= 1)
-    const int xbytes = M * nslabs * 512;
-    const int xregion = KP > 1 ? max(xbytes, 4096) : xbytes;
 
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    uint16_t *sc = reinterpret_cast<uint16_t *>(smem + ((xregion + 15) & ~15));
-
-    // ---- activation pieces (issued first, so they land first) -------------
-    // Piece p of the LDS image: slab s = (p/32) >> log2(M), token (p/32) & (M-1),
-    // elements 8*(p%32) .. +7 of that slab.
-    const int npieces = M * nslabs * 32;
-    const int nxp = (npieces + kThreads - 1) / kThreads;  // pieces per thread (uniform)
-    const int mshift = M == 2 ? 1 : 0;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x, (uint32_t)M * (uint32_t)K * 2u);
-    u32x4_t xv[kXPieces];
-#pragma unroll
-    for (int i = 0; i < kXPieces; ++i) {
-        if (i < nxp) {
-            const int p = tid + i * kThreads;
-            const int q = p >> 5;
-            const int e = ((q >> mshift) << 8) + ((p & 31) << 3);
-            const int t = q & (M - 1);
-            const int off = (p < npieces && e < K) ? (t * K + e) * 2 : kOOB;
-            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-        }
-    }
-    // ---- scales --------------------------------------------------------
-    const __amdgpu_buffer_rsrc_t sr =
-        make_rsrc(P.scale, (uint32_t)N * (uint32_t)(GROUPED ? ngroups : 1) * 2u);
-    constexpr int kSc = GROUPED ? kSPieces : 1;
-    // grouped: entries per thread of the workgroup's scale slice (uniform)
-    const int nsp = GROUPED ? (RB * 16 * ngroups + kThreads - 1) / kThreads : 1;
-    uint32_t sv[kSc];
-    // grouped: entry j of the workgroup's [RB*16][ngroups] slice of the scale
-    // matrix, j = tid + i*256 -> channel c, group gr (stepped without division)
-    int sc_c = 0, sc_g = 0, sc_dq = 0, sc_dr = 0;
-    if constexpr (GROUPED) {
-        sc_c = tid / ngroups;
-        sc_g = tid - sc_c * ngroups;
-        sc_dq = kThreads / ngroups;
-        sc_dr = kThreads - sc_dq * ngroups;
-    }
-    {
-        int c = sc_c, gr = sc_g;
-#pragma unroll
-        for (int i = 0; i < kSc; ++i) {
-            if (i >= nsp)
-                break;
-            int off = kOOB;
-            if constexpr (GROUPED) {
-                const int ch = blk0 * 16 + c;
-                if (c < RB * 16 && ch < N)
-                    off = (ch * ngroups + gr) * 2;
-                gr += sc_dr;
-                c += sc_dq;
-                if (gr >= ngroups) {
-                    gr -= ngroups;
-                    ++c;
-                }
-            } else {
-                const int ch = blk0 * 16 + tid;
-                if (tid < RB * 16 && ch < N)
-                    off = ch * 2;
-            }
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-        }
-    }
-
-    // ---- packed slabs ----------------------------------------------------
-    // Lane l reads row (l & 15) of the block, bytes [16*(l>>4), +16) of each
-    // slab; the resource covers exactly the block's valid rows.
-    // (readfirstlane: the clamp lowers to a vector op, and a descriptor held in
+    WaveCtx c;
+    c.K = K;
+    c.ngroups = ngroups;
+    c.lane = lane;
+    c.g = lane >> 4;                // lane group: which 64-code quarter of a slab
+    const int col = lane & 15;      // A row / B column / C column of this lane
+    c.tok = col >> 1;               // token of this B column
+    c.par = col & 1;                // 128-group of the slab this column collects
+    c.b_lane = c.tok < M && (c.g >> 1) == c.par;
+    c.s_begin = kpi * P.spart;
+    const int S = active ? min(P.spart, nslabs - c.s_begin) : 0;
+    // (readfirstlane: the clamp lowers to a vector op, and a descriptor in
     // vector registers would put every load in a waterfall loop)
-    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - rb * 16)));
+    const int nrows = __builtin_amdgcn_readfirstlane(active ? max(0, min(16, N - rb * 16)) : 0);
     const uint8_t *wbase = nrows > 0 ? P.packed + (int64_t)rb * 16 * rowbytes : P.packed;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)(nrows * rowbytes));
-    const int woff = col * rowbytes + g * 16 + s_begin * 64;
-    constexpr int kEarly = kRing - (4 * kXPieces + kSc + 3) / 4;
-    u32x4_t w[kRing];
-    // Every wave of the workgroup has issued its x and scale loads before any
-    // slab load is issued: a CU returns vector loads in issue order, so x that
-    // queued behind slab loads would wait for their HBM misses.  (Issue order
-    // only: s_barrier waits for no memory operation.)
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < kEarly; ++i)
-        w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, i < S ? woff + i * 64 : kOOB, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    c.wr = make_rsrc(wbase, (uint32_t)(nrows * rowbytes));
+    c.woff = col * rowbytes + c.g * 16;
+    c.xr = make_rsrc(P.x, (uint32_t)M * (uint32_t)K * 2u);
+    c.sr = make_rsrc(P.scale, (uint32_t)N * (uint32_t)(GROUPED ? ngroups : 1) * 2u);
+    c.srow_off = (lane & 15) < nrows ? (rb * 16 + (lane & 15)) * ngroups * 2 : -1;
+    uint16_t *wlds = reinterpret_cast<uint16_t *>(smem) + wave * kWaveLdsElems;
+    c.xbuf = wlds;
+    c.sbuf = wlds + 2 * kXBufElems;
 
-    // ---- stage x and scales in LDS (waits for the x and scale loads only)
-#pragma unroll
-    for (int i = 0; i < kXPieces; ++i) {
-        const int p = tid + i * kThreads;
-        if (i < nxp && p < npieces)
-            *reinterpret_cast<u32x4_t *>(xs + p * 8) = xv[i];
-    }
-    if constexpr (GROUPED) {
-        int c = sc_c, gr = sc_g;
-#pragma unroll
-        for (int i = 0; i < kSc; ++i) {
-            if (i >= nsp)
-                break;
-            if (c < RB * 16)
-                sc[((c >> 4) * ngroups + gr) * 16 + (c & 15)] = (uint16_t)sv[i];
-            gr += sc_dr;
-            c += sc_dq;
-            if (gr >= ngroups) {
-                gr -= ngroups;
-                ++c;
-            }
+    // per-channel scales: lane l < 16 of the wave that finishes the block
+    // loads channel l (issued before the part's loads, used at the end)
+    uint32_t chs = 0u;
+    if constexpr (!GROUPED) {
+        if (active && kpi == 0) {
+            const int ch = rb * 16 + lane;
+            chs = __builtin_amdgcn_raw_buffer_load_b16(c.sr, lane < 16 && ch < N ? ch * 2 : kOOB,
+                                                       0, 0);
         }
-    } else {
-        if (tid < RB * 16)
-            sc[tid] = (uint16_t)sv[0];
     }
-    __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-    for (int i = kEarly; i < kRing; ++i)
-        w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, i < S ? woff + i * 64 : kOOB, 0, 0);
-    __syncthreads();
-
-    // ---- consume the slabs in issue order ---------------------------------
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // B operand pieces: lanes without real B entries keep zeros throughout.
-    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-    const uint16_t *xw = xs + tok * 256 + g * 64;
-    const int xslab = M * 256;  // LDS elements per slab
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-        if (i < S) {
-            const int s = s_begin + i;
-            const uint4 *xb = reinterpret_cast<const uint4 *>(xw + s * xslab);
-            const uint32_t wv[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-            f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                if (b_lane) {
-                    b0 = xb[2 * d];
-                    b1 = xb[2 * d + 1];
-                }
-                uint32_t a[8];
-                decode16(wv[d], a);
-                part = mfma16x16x32<FP16>(a, b0, part);
-                part = mfma16x16x32<FP16>(a + 4, b1, part);
-            }
-            if constexpr (GROUPED) {
-                // C rows of this lane: channels rb*16 + 4g + r; column group `par`.
-                const int grp = 2 * s + par;
-                if (grp < ngroups) {
-                    const uint2 s4 = *reinterpret_cast<const uint2 *>(
-                        sc + (rbi * ngroups + grp) * 16 + 4 * g);
-                    acc[0] += f16_bits_to_f32((uint16_t)s4.x) * part[0];
-                    acc[1] += f16_bits_to_f32((uint16_t)(s4.x >> 16)) * part[1];
-                    acc[2] += f16_bits_to_f32((uint16_t)s4.y) * part[2];
-                    acc[3] += f16_bits_to_f32((uint16_t)(s4.y >> 16)) * part[3];
-                }
-            } else {
-                acc = part;
-            }
-        }
-    }
+    if (S > 0)
+        acc = run_part_n<FP16, GROUPED, MT>(c, S);
 
-    // ---- K-part reduction (fixed order) and epilogue ----------------------
+    // ---- K-part reduction (fixed order) and epilogue ------------------------
     f32x4_t sum = acc;
     if (KP > 1) {
         f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
-        __syncthreads();  // every wave is done with x
-        red[wave * 64 + lane] = acc;
+        __syncthreads();  // every wave is done with its LDS buffers
+        if (active)
+            red[wave * 64 + lane] = acc;
         __syncthreads();
-        if (kp != 0)
+        if (!active || kpi != 0)
             return;
         for (int j = 1; j < KP; ++j) {
             const f32x4_t v = red[(rbi + j * RB) * 64 + lane];
@@ -302,126 +333,119 @@ gemv_stream_kernel(const StreamBatch batch)
             sum[2] += v[2];
             sum[3] += v[3];
         }
+    } else if (!active) {
+        return;
     }
     uint16_t *__restrict__ y = P.y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float tot = sum[r] + __shfl_xor(sum[r], 1);
-        const int ch = rb * 16 + 4 * g + r;
-        if (par == 0 && tok < M && ch < N) {
-            float o = 0.5f * tot;  // decoded weights are +-2
-            if constexpr (!GROUPED)
-                o *= f16_bits_to_f32(sc[rbi * 16 + 4 * g + r]);
-            y[(int64_t)tok * N + ch] = round_out<FP16>(o);
-        }
+        const int ch = rb * 16 + 4 * c.g + r;
+        float o = 0.5f * tot;  // decoded weights are +-2
+        if constexpr (!GROUPED)
+            o *= f16_bits_to_f32((uint16_t)__shfl((int)chs, 4 * c.g + r));
+        if (c.par == 0 && c.tok < M && ch < N)
+            y[(int64_t)c.tok * N + ch] = round_out<FP16>(o);
     }
 }
 
+// LDS bytes of a workgroup: the per-wave buffers, or the K-part reduction
+// area if larger.
+constexpr size_t kLdsBytes = std::max<size_t>((size_t)kWaves * kWaveLdsElems * 2,
+                                              (size_t)kWaves * 64 * 16);
 
-// K parts per channel block for one problem: the fewest whose parts fit the
-// ring and whose workgroup scale slice fits the staging registers; 0 when this
-// kernel cannot take the problem.
-int min_parts(int M, int K, bool grouped)
+// K split of one problem: parts of about `target` slabs, at most kMaxS, on at
+// most kWaves waves per block.  Returns false when this kernel cannot take it.
+bool split_k(int M, int K, int target, int &kp, int &spart)
 {
+    if (M < 1 || M > kGemvStreamMaxM)
+        return false;
     const int nslabs = (K + 255) / 256;
-    if (M < 1 || M > kGemvStreamMaxM || M * nslabs * 32 > kXPieces * kThreads)
-        return 0;
-    int kp = 1;
-    while (kp <= 4 && ((nslabs + kp - 1) / kp > kRing ||
-                       (grouped && (4 / kp) * 16 * (K / 128) > kSPieces * kThreads)))
-        kp *= 2;
-    return kp <= 4 ? kp : 0;
+    if (nslabs > kWaves * kMaxS)
+        return false;
+    kp = std::min(kWaves, (nslabs + target - 1) / target);
+    spart = (nslabs + kp - 1) / kp;
+    kp = (nslabs + spart - 1) / spart;  // no empty parts
+    return spart <= kMaxS;
 }
-
-size_t lds_bytes(const StreamProblem &p, bool grouped)
-{
-    const int nslabs = (p.K + 255) / 256;
-    const int xbytes = p.M * nslabs * 512;
-    const int xregion = p.kp > 1 ? std::max(xbytes, 4096) : xbytes;
-    const int scb = grouped ? (4 / p.kp) * (p.K / 128) * 16 * 2 : 64 * 2;
-    return (size_t)((xregion + 15) & ~15) + (size_t)scb;
-}
-
-// A launch with fewer waves than this leaves SIMDs idle; its longest K parts
-// are split further while a part keeps at least kMinPart slabs.
-constexpr int kMinWaves = 2048;
-constexpr int kMinPart = 4;
 
 }  // namespace
 
 bool gemv_stream_takes(int64_t M, int64_t K, bool grouped)
 {
-    return K % 128 == 0 && K <= kGemvMaxK && min_parts((int)M, (int)K, grouped) > 0;
+    (void)grouped;
+    int kp = 0, spart = 0;
+    return K % 128 == 0 && K <= kGemvMaxK && split_k((int)M, (int)K, kTargetSmall, kp, spart);
 }
+
+namespace {
+template <bool FP16, bool GROUPED>
+void launch_m(int mt, dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
+{
+    if (mt == 1)
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1>), grid, block, kLdsBytes, stream, b);
+    else
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2>), grid, block, kLdsBytes, stream, b);
+}
+}  // namespace
 
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
                               bool grouped, hipStream_t stream)
 {
+    // The plan with parts of kTargetS slabs, or of kTargetSmall when that
+    // yields few workgroups (a function of the whole batch, so deterministic).
     StreamBatch b;
-    b.count = 0;
-    int nblocks[kGemvMaxBatch], nslabs[kGemvMaxBatch];
-    int waves = 0;
-    for (int oi = 0; oi < count; ++oi) {
-        const GemvArgs &a = args[order[oi]];
-        if (a.M == 0 || a.N == 0)
-            continue;
-        const int kp = min_parts(a.M, a.K, grouped);
-        if (kp == 0 || a.grouped != grouped)
-            return hipErrorInvalidValue;
-        StreamProblem &p = b.p[b.count];
-        p.x = a.x;
-        p.packed = a.packed;
-        p.scale = a.scale;
-        p.y = a.y;
-        p.M = a.M;
-        p.N = a.N;
-        p.K = a.K;
-        p.kp = kp;
-        nblocks[b.count] = (a.N + 15) / 16;
-        nslabs[b.count] = (a.K + 255) / 256;
-        waves += nblocks[b.count] * kp;
-        ++b.count;
+    int units = 0, mt = 0;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        const int target = attempt == 0 ? kTargetS : kTargetSmall;
+        b.count = 0;
+        units = 0;
+        mt = 0;
+        for (int oi = 0; oi < count; ++oi) {
+            const GemvArgs &a = args[order[oi]];
+            if (a.M == 0 || a.N == 0)
+                continue;
+            StreamProblem &p = b.p[b.count];
+            if (a.grouped != grouped || (mt != 0 && a.M != mt) ||
+                !split_k(a.M, a.K, target, p.kp, p.spart))
+                return hipErrorInvalidValue;
+            mt = a.M;
+            p.x = a.x;
+            p.packed = a.packed;
+            p.scale = a.scale;
+            p.y = a.y;
+            p.N = a.N;
+            p.K = a.K;
+            const int nblocks = (a.N + 15) / 16;
+            p.rb = std::min(kWaves / p.kp, nblocks);
+            p.rbi_map = 0;
+            p.kpi_map = 0;
+            for (int w = 0; w < kWaves; ++w) {
+                const bool act = w < p.rb * p.kp;
+                p.rbi_map |= (uint64_t)(act ? w % p.rb : 15) << (4 * w);
+                p.kpi_map |= (uint64_t)(act ? w / p.rb : 15) << (4 * w);
+            }
+            p.unit0 = units;
+            b.unit0[b.count] = units;
+            units += (nblocks + p.rb - 1) / p.rb;
+            ++b.count;
+        }
+        if (units >= kFewUnits)
+            break;
     }
     if (b.count == 0)
         return hipSuccess;
-    while (waves < kMinWaves) {
-        int best = -1, best_part = 0;
-        for (int i = 0; i < b.count; ++i) {
-            const int part = (nslabs[i] + b.p[i].kp - 1) / b.p[i].kp;
-            const int half = (nslabs[i] + 2 * b.p[i].kp - 1) / (2 * b.p[i].kp);
-            if (b.p[i].kp < 4 && half >= kMinPart && part > best_part) {
-                best = i;
-                best_part = part;
-            }
-        }
-        if (best < 0)
-            break;
-        waves += nblocks[best] * b.p[best].kp;
-        b.p[best].kp *= 2;
-    }
-    size_t lds = 0;
-    int units = 0;
-    for (int i = 0; i < b.count; ++i) {
-        StreamProblem &p = b.p[i];
-        p.spart = (nslabs[i] + p.kp - 1) / p.kp;
-        p.unit0 = units;
-        units += (nblocks[i] + 4 / p.kp - 1) / (4 / p.kp);
-        lds = std::max(lds, lds_bytes(p, grouped));
-    }
+    const dim3 grid(units), block(kThreads);
     if (fp16) {
         if (grouped)
-            hipLaunchKernelGGL((gemv_stream_kernel<true, true>), dim3(units), dim3(kThreads), lds,
-                               stream, b);
+            launch_m<true, true>(mt, grid, block, stream, b);
         else
-            hipLaunchKernelGGL((gemv_stream_kernel<true, false>), dim3(units), dim3(kThreads), lds,
-                               stream, b);
+            launch_m<true, false>(mt, grid, block, stream, b);
     } else {
         if (grouped)
-            hipLaunchKernelGGL((gemv_stream_kernel<false, true>), dim3(units), dim3(kThreads), lds,
-                               stream, b);
+            launch_m<false, true>(mt, grid, block, stream, b);
         else
-            hipLaunchKernelGGL((gemv_stream_kernel<false, false>), dim3(units), dim3(kThreads), lds,
-                               stream, b);
+            launch_m<false, false>(mt, grid, block, stream, b);
     }
     return hipGetLastError();
 }

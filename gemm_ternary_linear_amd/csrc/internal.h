@@ -35,8 +35,8 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
 constexpr int kGemvStreamMaxM = 2;
 // Whether the streaming decode kernel takes a gemv_takes() shape.
 bool gemv_stream_takes(int64_t M, int64_t K, bool grouped);
-// The problems args[order[0..count)] (all gemv_stream_takes(), one scale mode)
-// in one launch of the streaming decode kernel.
+// The problems args[order[0..count)] (all gemv_stream_takes(), one scale mode,
+// one M) in one launch of the streaming decode kernel.
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
                               bool grouped, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,

@@ -80,14 +80,15 @@ def test_linear_auto_small(tl, M, N, K, g, dtype):
     check_within(y, y_ref, bound, f"auto M={M} N={N} K={K} g={g} {dtype}")
 
 
-# Decode shapes at M <= 2 aimed at the streaming kernel's limits: K split in
-# 1, 2 or 4 parts, a part of exactly 20 slabs (the whole ring), x staging of
-# exactly 40 KB, a workgroup scale slice of exactly 2560 entries, a half slab
-# at the end of K, ragged N, and small launches whose K split is raised to
-# fill the chip.
+# Decode shapes at M <= 2 for the streaming kernel: K split over up to 16
+# waves, K parts longer than the load window (several window steps, the last
+# one partial), x staging of exactly 64 KB, a half slab at the end of K,
+# ragged N (a last block of 4 rows), tiny N, and workgroups whose last waves
+# hold no K part.
 STREAM = [
     (1, 40, 20480, 128), (1, 50, 18944, -1), (2, 45, 10240, -1), (2, 77, 6272, 128),
     (1, 4100, 4096, -1), (2, 19, 5248, 128), (1, 600, 3200, 128), (2, 1, 8192, -1),
+    (1, 48, 30720, 128), (1, 33, 32768, -1), (2, 20, 16384, 128), (1, 7, 31872, 128),
 ]
 
 
@@ -249,3 +250,26 @@ def test_full_size_sampled(tl, cfg, si, M):
     y_ref, bound = oracle.linear_at(case.x, packed, case.scale, g, ms, ns)
     check_within(yv[ms, ns], y_ref, bound, f"config {cfg} {shp.name} M={M}")
     assert np.all(np.isfinite(yv))
+
+
+# Shapes large enough that the streaming kernel keeps several channel blocks
+# per workgroup: the per-channel cases run the full ring of 20 slabs in every
+# wave, the group-scaled one needs more workgroups than CUs.  Raw random bytes
+# (reserved code 11 included) stand in for packed codes.
+RING = [(1, 16384, 20480, 128), (1, 16384, 20480, -1), (2, 32768, 10240, -1)]
+
+
+@pytest.mark.parametrize("M,N,K,g", RING)
+def test_stream_full_ring_sampled(tl, M, N, K, g):
+    import torch
+    say(f"stream full ring M={M} N={N} K={K} g={g}")
+    rng = np.random.default_rng(zlib.crc32(repr(("ring", M, N, K, g)).encode()))
+    packed = synth.draw_bytes(rng, N, K)
+    scale = synth.draw_scales(rng, N, K, g)
+    x = synth.draw_x(rng, M, K, "bf16")
+    y = tl.linear(to_dev(x, torch.bfloat16), to_dev(packed, None), to_dev(scale, torch.float16), g)
+    torch.cuda.synchronize()
+    yv = widen(bits_of(y), "bf16")
+    ms, ns = _sample_indices(rng, M, N, count=1500)
+    y_ref, bound = oracle.linear_at(x, packed, scale, g, ms, ns)
+    check_within(yv[ms, ns], y_ref, bound, f"ring M={M} N={N} K={K} g={g}")
