@@ -15,6 +15,8 @@
 // global loads of step k+1 are in flight while step k runs on the matrix cores.
 // Rows are padded to 72 elements (144 bytes) so the 16 rows a fragment read
 // touches fall on distinct LDS banks.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -186,6 +188,274 @@ __global__ void __launch_bounds__(THREADS)
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for per-channel scales.  x and the packed weights reach LDS
+// by buffer-to-LDS DMA (no register staging), NS stages deep, so the loads of
+// K step kt+NS-1 are in flight while step kt runs on the matrix cores.  Each
+// wave reads its packed codes (one dword = 16 codes per lane and fragment)
+// from LDS and expands them in registers straight into MFMA A operands: the
+// decoded weights never pass through LDS.
+//
+// K order inside one 64-wide step: lane group g (lanes 16g..16g+15) of an
+// MFMA operand holds k = 16g + 8*kk + (0..7) for the two 32-deep MFMAs kk of
+// the step, which is exactly what the packed dword g of a row decodes to;
+// the x fragment reads use the same order, so the contraction is unchanged.
+//
+// x stage layout: token row r of the stage is 128 bytes = 8 chunks of 8
+// elements; logical chunk c sits in physical chunk c ^ f(r) with
+// f(r) = (r & 7) ^ ((r >> 3) & 1), which spreads the 16 rows a fragment read
+// touches over all LDS banks.  The DMA gathers each chunk from the global
+// address that belongs to its physical slot.
+namespace dma {
+
+constexpr int TK = 64;
+constexpr int kOOB = 0x40000000;  // buffer offset past every record: reads as 0
+
+template <int TN_, int TM_, int WGN_, int WGM_, int NS_, int OCC_>
+struct Cfg {
+    static constexpr int TN = TN_, TM = TM_, WGN = WGN_, WGM = WGM_, NS = NS_, OCC = OCC_;
+    static constexpr int THREADS = WGN * WGM * 64;
+    static constexpr int FN = TN / WGN / 16;  // 16-channel fragments per wave
+    static constexpr int FM = TM / WGM / 16;  // 16-token fragments per wave
+    static constexpr int XI = TM * 8 / THREADS;  // 16-byte x DMAs per thread and stage
+    static constexpr int WI = TN * 4 / THREADS;  // 4-byte packed DMAs per thread and stage
+    static constexpr int VPS = XI + WI;          // vector memory ops per thread and stage
+    static constexpr int XSTAGE = TM * 8;        // 16-byte chunks per x stage
+    static constexpr int WSTAGE = TN * 4;        // dwords per packed stage
+    static_assert(TM * 8 % THREADS == 0 && TN * 4 % THREADS == 0, "stage split");
+    static_assert(FN >= 1 && FM >= 1 && NS >= 2 && NS <= 4, "tile");
+    static_assert((NS - 2) * VPS <= 63, "vmcnt range");
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// One buffer-to-LDS DMA: every lane reads BYTES from rsrc at voff + soff and
+// the wave writes them to LDS at lds + lane * BYTES.  The builtin exists for
+// the device target only; the host pass (which emits just the launch stub)
+// sees an empty body.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voff, int soff)
+{
+    static_assert(BYTES == 4 || BYTES == 16, "DMA size");
+#if defined(__HIP_DEVICE_COMPILE__)
+    auto *l = (__attribute__((address_space(3))) void *)lds;
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, l, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, l, 4, voff, soff, 0, 0);
+#endif
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their
+// maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most N of this wave's DMAs are outstanding, then meet the
+// other waves at a barrier; afterwards every wave's older DMAs have landed.
+// The scheduling fences keep the wait from being hoisted into the compute
+// before it, and the memory clobber keeps LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<N>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool FP16, class C>
+__global__ void __launch_bounds__(C::THREADS, C::OCC)
+    gemm_dma_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
+                    const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N,
+                    int K)
+{
+    constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
+    // One LDS object per stage: the compiler then knows that a DMA into one
+    // stage does not write the stage being read and waits for nothing there.
+    __shared__ __attribute__((aligned(16))) uint4 sx0[C::XSTAGE], sx1[C::XSTAGE],
+        sx2[NS > 2 ? C::XSTAGE : 1], sx3[NS > 3 ? C::XSTAGE : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sw0[C::WSTAGE], sw1[C::WSTAGE],
+        sw2[NS > 2 ? C::WSTAGE : 1], sw3[NS > 3 ? C::WSTAGE : 1];
+    lds_u4 *const lx[4] = {(lds_u4 *)sx0, (lds_u4 *)sx1, (lds_u4 *)sx2, (lds_u4 *)sx3};
+    lds_u32 *const lw[4] = {(lds_u32 *)sw0, (lds_u32 *)sw1, (lds_u32 *)sw2, (lds_u32 *)sw3};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave % C::WGN;
+    const int wm = wave / C::WGN;
+
+    // Tile order: workgroup b runs on XCD b % 8.  When the token tiles split
+    // evenly over the 8 XCDs, XCD k takes token tiles k, k+8, ... and walks
+    // every channel tile of each, so its L2 keeps that token tile's x.
+    const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
+    int tn, tm;
+    const int bid = blockIdx.x;
+    if (ntm % 8 == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        tm = xcd + 8 * (slot / ntn);
+        tn = slot % ntn;
+    } else {
+        tm = bid / ntn;
+        tn = bid % ntn;
+    }
+    const int n0 = tn * C::TN;
+    const int m0 = tm * C::TM;
+    const int nk = K / TK;
+
+    // DMA sources.  x DMA i of this thread fills physical chunk p = i*THREADS
+    // + tid of the stage (lanes of a wave write consecutive chunks).
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(packed), (short)0, (int)((uint32_t)N * (uint32_t)(K >> 2)),
+        0x00020000);
+    int xoff[C::XI], woff[C::WI];
+#pragma unroll
+    for (int i = 0; i < C::XI; ++i) {
+        const int p = i * THREADS + tid;
+        const int r = p >> 3, c = (p & 7) ^ xswz(p >> 3);
+        xoff[i] = m0 + r < M ? ((m0 + r) * K + 8 * c) * 2 : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < C::WI; ++i) {
+        const int d = i * THREADS + tid;
+        const int row = d >> 2;
+        woff[i] = n0 + row < N ? (n0 + row) * (K >> 2) + 4 * (d & 3) : kOOB;
+    }
+    // Wave-uniform LDS destinations of this wave's DMAs (kept in SGPRs).
+    const int wave_chunk = __builtin_amdgcn_readfirstlane(wave) * 64;
+
+    // Every step issues the same number of DMAs, so that one vmcnt value
+    // is right everywhere: steps past the end reload the last K step into a
+    // stage that is never read again.
+    auto issue = [&](auto S, int kt) {
+        constexpr int s = decltype(S)::value;
+        const int kc = kt < nk ? kt : nk - 1;
+#pragma unroll
+        for (int i = 0; i < C::XI; ++i)
+            dma_to_lds<16>(xr, (void *)(lx[s] + i * THREADS + wave_chunk), xoff[i], kc * (TK * 2));
+#pragma unroll
+        for (int i = 0; i < C::WI; ++i)
+            dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * (TK / 4));
+    };
+
+    f32x4_t acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Per-lane LDS read offsets.  x: token row (lane & 15) of each fragment,
+    // logical chunk 2g + kk; packed: dword g of channel row (lane & 15).
+    const int g = lane >> 4;
+    const int fr = lane & 15;
+    const int xrow0 = wm * FM * 16 + fr;
+    const int xa0 = xrow0 * 8 + ((2 * g) ^ xswz(fr));  // kk = 0; kk = 1 flips bit 0
+    const int xa1 = xa0 ^ 1;
+    const int wa = (wn * FN * 16 + fr) * 4 + g;
+
+    auto compute = [&](auto S) {
+        constexpr int s = decltype(S)::value;
+        uint32_t wv[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            wv[f] = lw[s][wa + f * 64];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 xf[FM];
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                xf[j] = __builtin_bit_cast(uint4, lx[s][(kk ? xa1 : xa0) + j * 128]);
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                uint32_t d[8];
+                decode16(wv[f], d);
+                const uint4 a = kk ? make_uint4(d[4], d[5], d[6], d[7])
+                                   : make_uint4(d[0], d[1], d[2], d[3]);
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[f][j] = mfma<FP16>(a, xf[j], acc[f][j]);
+            }
+        }
+    };
+
+    // One K step: wait for this wave's DMA of stage kt, barrier (all waves'
+    // DMA of stage kt landed, all waves done with stage kt-1), start the DMA
+    // of step kt+NS-1 into the stage kt-1 used, then compute stage kt.
+    auto step = [&](auto S, int kt) {
+        constexpr int s = decltype(S)::value;
+        wait_and_barrier<(NS - 2) * C::VPS>();
+        issue(std::integral_constant<int, (s + NS - 1) % NS>{}, kt + NS - 1);
+        compute(S);
+    };
+
+    // Prologue: stages 0 .. NS-2.
+    issue(std::integral_constant<int, 0>{}, 0);
+    if constexpr (NS > 2)
+        issue(std::integral_constant<int, 1>{}, 1);
+    if constexpr (NS > 3)
+        issue(std::integral_constant<int, 2>{}, 2);
+
+    // K is a whole number of NS-step rounds (the host checks), so every
+    // stage index below is a constant.
+    for (int kt = 0; kt < nk; kt += NS) {
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
+        if constexpr (NS > 2)
+            step(std::integral_constant<int, 2>{}, kt + 2);
+        if constexpr (NS > 3)
+            step(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    // No DMA may still be writing LDS when the workgroup ends.
+    wait_vm<0>();
+
+    // Epilogue: C tile (f, j) element r of this lane is channel
+    // n0 + (wn*FN + f)*16 + 4*g + r of token m0 + (wm*FM + j)*16 + fr.
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+        const int n = n0 + (wn * FN + f) * 16 + 4 * g;
+        float post[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            post[r] = n + r < N ? 0.5f * f16_bits_to_f32(scale[n + r]) : 0.f;  // weights are +-2
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + (wm * FM + j) * 16 + fr;
+            if (m >= M)
+                continue;
+            uint16_t *yr = y + (int64_t)m * N;
+            if (vec && n + 3 < N) {
+                const uint32_t lo = (uint32_t)round_out<FP16>(acc[f][j][0] * post[0]) |
+                                    (uint32_t)round_out<FP16>(acc[f][j][1] * post[1]) << 16;
+                const uint32_t hi = (uint32_t)round_out<FP16>(acc[f][j][2] * post[2]) |
+                                    (uint32_t)round_out<FP16>(acc[f][j][3] * post[3]) << 16;
+                *reinterpret_cast<uint2 *>(yr + n) = make_uint2(lo, hi);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        yr[n + r] = round_out<FP16>(acc[f][j][r] * post[r]);
+            }
+        }
+    }
+}
+
+}  // namespace dma
+
 template <bool FP16, bool GROUPED>
 hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
                          const uint16_t *scale, uint16_t *y, hipStream_t stream)
@@ -198,9 +468,34 @@ hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *
 
 }  // namespace
 
+// Tile shape, wave grid, stage count and waves per SIMD of the pipelined kernel.
+typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;
+
+// The pipelined kernel takes per-channel problems whose K is a whole number
+// of 64-wide steps and that fill its tiles.
+bool gemm_big_takes(int M, int N, int K, bool grouped)
+{
+    // buffer offsets are 32-bit and must stay below the out-of-range marker
+    return !grouped && M >= 256 && N >= 1024 && K % (dma::TK * BigCfg::NS) == 0 &&
+           (int64_t)M * K * 2 < dma::kOOB && (int64_t)N * (K / 4) < dma::kOOB;
+}
+
+template <bool FP16>
+hipError_t launch_gemm_big(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
+                           const uint16_t *scale, uint16_t *y, hipStream_t stream)
+{
+    const dim3 grid(((N + BigCfg::TN - 1) / BigCfg::TN) * ((M + BigCfg::TM - 1) / BigCfg::TM));
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), grid, dim3(BigCfg::THREADS), 0,
+                       stream, x, packed, scale, y, M, N, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
 {
+    if (gemm_big_takes(M, N, K, grouped))
+        return fp16 ? launch_gemm_big<true>(x, M, N, K, packed, scale, y, stream)
+                    : launch_gemm_big<false>(x, M, N, K, packed, scale, y, stream);
     if (fp16)
         return grouped ? launch_gemm_t<true, true>(x, M, N, K, packed, scale, y, stream)
                        : launch_gemm_t<true, false>(x, M, N, K, packed, scale, y, stream);

@@ -252,6 +252,28 @@ def test_full_size_sampled(tl, cfg, si, M):
     assert np.all(np.isfinite(yv))
 
 
+# Prefill shapes, per-channel, M >= 256, N >= 1024.  K % 256 == 0 runs the
+# DMA-pipelined kernel: ragged token and channel tiles, N % 4 != 0 (element
+# stores instead of 8-byte stores), exact tile multiples, and M = 2048 (eight
+# token tiles: the XCD-ordered tile walk).  K = 640 and K = 128 run the
+# 128 x 128 kernel.
+BIG = [(300, 1100, 768), (260, 1030, 256), (512, 1024, 1280), (257, 1027, 512),
+       (2048, 1040, 256), (300, 1100, 640), (257, 1027, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K", BIG)
+def test_linear_gemm_large_tiles(tl, M, N, K, dtype):
+    say(f"linear large-tile gemm M={M} N={N} K={K} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr(("big", M, N, K, dtype)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, -1, dtype)
+    assert tl.select_path(M, N, K, -1) == "gemm"
+    y_ref, bound = oracle.linear(x, packed, scale, -1, dtype=dtype)
+    y = _run(tl, x, packed, scale, -1, dtype, codes=codes)
+    check_within(y, y_ref, bound, f"big M={M} N={N} K={K} {dtype}",
+                 out_rounding=dtype if K < 256 else None)
+
+
 # Shapes large enough that the streaming kernel keeps several channel blocks
 # per workgroup: the per-channel cases run the full ring of 20 slabs in every
 # wave, the group-scaled one needs more workgroups than CUs.  Raw random bytes
