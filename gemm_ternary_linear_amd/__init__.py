@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
-    "PATHS", "BF16", "FP16", "abi_version", "LIB_PATH",
+    "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
@@ -36,7 +36,7 @@ PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3}
 EXPORTS = (
     "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
     "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
-    "ternary_status_string", "ternary_abi_version",
+    "ternary_status_string", "ternary_abi_version", "ternary_shutdown",
 )
 MAX_BATCH = 8
 
@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.ternary_status_string.restype = ctypes.c_char_p
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
-               "ternary_abi_version"):
+               "ternary_abi_version", "ternary_shutdown"):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -89,6 +89,11 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return int(lib().ternary_abi_version())
+
+
+def shutdown() -> None:
+    """Free the library's per-stream workspaces (ternary_shutdown)."""
+    _check(int(lib().ternary_shutdown()), "ternary_shutdown")
 
 
 def gemv_max_m() -> int:

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -69,6 +69,11 @@ int select_path(int64_t M, int64_t K)
 extern "C" {
 
 int ternary_abi_version(void) { return kAbiVersion; }
+
+int ternary_shutdown(void)
+{
+    return ternary::release_workspaces() == hipSuccess ? TERNARY_OK : TERNARY_ERR_HIP;
+}
 
 int ternary_gemv_max_m(void) { return ternary::kGemvMaxM; }
 

@@ -278,7 +278,7 @@ template <bool FP16, class C>
 __global__ void __launch_bounds__(C::THREADS, C::OCC)
     gemm_dma_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                     const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N,
-                    int K)
+                    int K, int ksplit, float4 *__restrict__ partial)
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
     // One LDS object per stage: the compiler then knows that a DMA into one
@@ -296,23 +296,39 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     const int wn = wave % C::WGN;
     const int wm = wave / C::WGN;
 
-    // Tile order: workgroup b runs on XCD b % 8.  When the token tiles split
-    // evenly over the 8 XCDs, XCD k takes token tiles k, k+8, ... and walks
-    // every channel tile of each, so its L2 keeps that token tile's x.
+    // Tile order: workgroup b runs on XCD b % 8.  Without a K split, when the
+    // token tiles split evenly over the 8 XCDs, XCD k takes token tiles k,
+    // k+8, ... and walks every channel tile of each, so its L2 keeps that
+    // token tile's x.  With a K split of `ksplit` slices, the slices of one
+    // tile go to one XCD when the tiles split evenly over the XCDs.
     const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
-    int tn, tm;
+    int tn, tm, tile = 0, slice = 0;
     const int bid = blockIdx.x;
-    if (ntm % 8 == 0) {
-        const int xcd = bid & 7, slot = bid >> 3;
-        tm = xcd + 8 * (slot / ntn);
-        tn = slot % ntn;
+    if (ksplit == 1) {
+        if (ntm % 8 == 0) {
+            const int xcd = bid & 7, slot = bid >> 3;
+            tm = xcd + 8 * (slot / ntn);
+            tn = slot % ntn;
+        } else {
+            tm = bid / ntn;
+            tn = bid % ntn;
+        }
     } else {
-        tm = bid / ntn;
-        tn = bid % ntn;
+        if ((ntn * ntm) % 8 == 0) {
+            const int xcd = bid & 7, slot = bid >> 3;
+            tile = xcd + 8 * (slot / ksplit);
+            slice = slot % ksplit;
+        } else {
+            tile = bid / ksplit;
+            slice = bid % ksplit;
+        }
+        tm = tile / ntn;
+        tn = tile % ntn;
     }
     const int n0 = tn * C::TN;
     const int m0 = tm * C::TM;
-    const int nk = K / TK;
+    const int nk = K / TK / ksplit;  // K steps of this workgroup's slice
+    const int kbase = slice * nk;
 
     // DMA sources.  x DMA i of this thread fills physical chunk p = i*THREADS
     // + tid of the stage (lanes of a wave write consecutive chunks).
@@ -342,7 +358,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     // stage that is never read again.
     auto issue = [&](auto S, int kt) {
         constexpr int s = decltype(S)::value;
-        const int kc = kt < nk ? kt : nk - 1;
+        const int kc = kbase + (kt < nk ? kt : nk - 1);
 #pragma unroll
         for (int i = 0; i < C::XI; ++i)
             dma_to_lds<16>(xr, (void *)(lx[s] + i * THREADS + wave_chunk), xoff[i], kc * (TK * 2));
@@ -422,6 +438,19 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     // No DMA may still be writing LDS when the workgroup ends.
     wait_vm<0>();
 
+    if (ksplit > 1) {
+        // Split K: store this slice's fp32 partial tile, fragment by fragment
+        // (lane-contiguous float4s); gemm_split_reduce adds the slices.
+        float4 *mine = partial + ((int64_t)tile * ksplit + slice) * (C::TN * C::TM / 4);
+        const int lo = wave * FN * FM * 64 + lane;
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                mine[lo + (f * FM + j) * 64] = __builtin_bit_cast(float4, acc[f][j]);
+        return;
+    }
+
     // Epilogue: C tile (f, j) element r of this lane is channel
     // n0 + (wn*FN + f)*16 + 4*g + r of token m0 + (wm*FM + j)*16 + fr.
     const bool vec = (N & 3) == 0;
@@ -454,6 +483,52 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     }
 }
 
+// Second half of a split-K product: thread t of the grid takes float4 t of
+// the partial tiles (the layout gemm_dma_kernel stores), adds the `ksplit`
+// slices in slice order, applies the per-channel scale and writes four
+// outputs of one token.
+template <bool FP16, class C>
+__global__ void __launch_bounds__(256)
+    gemm_split_reduce(const float4 *__restrict__ partial, const uint16_t *__restrict__ scale,
+                      uint16_t *__restrict__ y, int M, int N, int ksplit)
+{
+    constexpr int FN = C::FN, FM = C::FM, TILE4 = C::TN * C::TM / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
+    if (idx >= (int64_t)ntn * ntm * TILE4)
+        return;
+    const int tile = (int)(idx / TILE4), e = (int)(idx % TILE4);
+    const int lane = e & 63, t = e >> 6;
+    const int j = t % FM, f = (t / FM) % FN, wave = t / (FM * FN);
+    const int n = (tile % ntn) * C::TN + ((wave % C::WGN) * FN + f) * 16 + 4 * (lane >> 4);
+    const int m = (tile / ntn) * C::TM + ((wave / C::WGN) * FM + j) * 16 + (lane & 15);
+    if (m >= M || n >= N)
+        return;
+    const float4 *src = partial + (int64_t)tile * ksplit * TILE4 + e;
+    float4 v = src[0];
+    for (int q = 1; q < ksplit; ++q) {
+        const float4 w = src[(int64_t)q * TILE4];
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+    uint16_t *yr = y + (int64_t)m * N;
+    if ((N & 3) == 0 && n + 3 < N) {
+        uint32_t o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            o[r] = round_out<FP16>(a[r] * (0.5f * f16_bits_to_f32(scale[n + r])));
+        *reinterpret_cast<uint2 *>(yr + n) = make_uint2(o[0] | o[1] << 16, o[2] | o[3] << 16);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (n + r < N)
+                yr[n + r] = round_out<FP16>(a[r] * (0.5f * f16_bits_to_f32(scale[n + r])));
+    }
+}
+
 }  // namespace dma
 
 template <bool FP16, bool GROUPED>
@@ -476,17 +551,68 @@ typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;
 bool gemm_big_takes(int M, int N, int K, bool grouped)
 {
     // buffer offsets are 32-bit and must stay below the out-of-range marker
-    return !grouped && M >= 256 && N >= 1024 && K % (dma::TK * BigCfg::NS) == 0 &&
+    return !grouped && M >= 256 && N >= 256 && K % (dma::TK * BigCfg::NS) == 0 &&
            (int64_t)M * K * 2 < dma::kOOB && (int64_t)N * (K / 4) < dma::kOOB;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// K slices of the pipelined kernel: doubled while the tiles do not cover the
+// compute units and each slice keeps at least two rounds of NS steps.
+int big_ksplit(int tiles, int K)
+{
+    const int nk = K / dma::TK, ns = BigCfg::NS, cus = device_cus();
+    int ks = 1;
+    while ((int64_t)tiles * ks < cus && nk % (2 * ks * ns) == 0 && nk / (2 * ks) >= 2 * ns &&
+           (int64_t)tiles * ks * 2 * BigCfg::TN * BigCfg::TM * 4 <= (int64_t(1) << 31))
+        ks *= 2;
+    return ks;
 }
 
 template <bool FP16>
 hipError_t launch_gemm_big(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
                            const uint16_t *scale, uint16_t *y, hipStream_t stream)
 {
-    const dim3 grid(((N + BigCfg::TN - 1) / BigCfg::TN) * ((M + BigCfg::TM - 1) / BigCfg::TM));
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), grid, dim3(BigCfg::THREADS), 0,
-                       stream, x, packed, scale, y, M, N, K);
+    const int tiles = ((N + BigCfg::TN - 1) / BigCfg::TN) * ((M + BigCfg::TM - 1) / BigCfg::TM);
+    int ks = big_ksplit(tiles, K);
+    float4 *partial = nullptr;
+    if (ks > 1) {
+        void *ws = nullptr;
+        const size_t bytes = (size_t)tiles * ks * BigCfg::TN * BigCfg::TM * 4;
+        const hipError_t e = stream_workspace(stream, bytes, &ws);
+        if (e != hipSuccess)
+            return e;
+        if (ws)
+            partial = static_cast<float4 *>(ws);
+        else
+            ks = 1;  // under capture without a workspace: the unsplit kernel
+    }
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), dim3(tiles * ks),
+                       dim3(BigCfg::THREADS), 0, stream, x, packed, scale, y, M, N, K, ks,
+                       partial);
+    if (ks > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const int64_t n4 = (int64_t)tiles * (BigCfg::TN * BigCfg::TM / 4);
+        hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, BigCfg>), dim3((unsigned)((n4 + 255) / 256)),
+                           dim3(256), 0, stream, partial, scale, y, M, N, ks);
+    }
     return hipGetLastError();
 }
 

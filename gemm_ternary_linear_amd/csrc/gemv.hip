@@ -122,7 +122,6 @@ gemv_kernel(const GemvBatch batch)
     const uint8_t *__restrict__ packed = P.packed;
     const uint16_t *__restrict__ scale = P.scale;
     const int M = P.M, N = P.N, K = P.K, RB = P.rb, kc = P.kc;
-    constexpr bool grouped = GROUPED;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

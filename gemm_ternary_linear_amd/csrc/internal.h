@@ -41,6 +41,15 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
                               bool grouped, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+
+// Library-owned scratch of at least `bytes` for work on `stream` of the
+// current device.  While `stream` is being captured nothing is allocated:
+// *out is set to nullptr (with hipSuccess) when the stream has no workspace
+// that large yet.
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void **out);
+// Frees every workspace (after the work queued on its stream has finished).
+hipError_t release_workspaces();
+
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                          const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
 

@@ -30,6 +30,14 @@
  *   - All data pointers are DEVICE pointers, owned by the caller.  The library
  *     keeps no reference after a call returns and never allocates or frees
  *     caller memory.
+ *   - The library owns one device workspace per (device, stream) for GEMM
+ *     shapes whose K range it splits over several workgroups (fp32 partial
+ *     tiles, added in a fixed order by a second kernel).  The first call on a stream that needs
+ *     a larger one allocates it (hipMalloc).  Under stream capture nothing is
+ *     allocated: a stream without a large enough workspace then runs the
+ *     unsplit kernel, so warm a stream up (one call per shape) before
+ *     capturing on it to capture the split kernel.  ternary_shutdown() frees
+ *     them all.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
  *     Arguments are validated on the host before anything is launched; on any
  *     error a negative ternary_status is returned and nothing is enqueued.
@@ -172,6 +180,14 @@ const char *ternary_status_string(int status);
 
 /* Library ABI version (increments when a signature or a convention changes). */
 int ternary_abi_version(void);
+
+/*
+ * ternary_shutdown - free the library's workspaces.  Waits for the work queued
+ * on each workspace's stream, then frees it; later calls allocate again as
+ * needed.  Returns TERNARY_ERR_HIP if a synchronisation or free failed (the
+ * remaining workspaces are still released).
+ */
+int ternary_shutdown(void);
 
 #ifdef __cplusplus
 }

@@ -58,7 +58,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 1
+    assert tl.abi_version() == 2
     assert tl.gemv_max_m() == 8
     for st in range(0, -9, -1):
         s = tl.status_string(st)

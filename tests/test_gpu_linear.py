@@ -274,6 +274,36 @@ def test_linear_gemm_large_tiles(tl, M, N, K, dtype):
                  out_rounding=dtype if K < 256 else None)
 
 
+# Prefill shapes with too few 256x128 tiles for the CUs: the K range is split
+# over several workgroups (8, 2 and 16 slices here) that store fp32 partial
+# tiles, and a second kernel adds them in slice order.  Ragged tiles, tile
+# counts that do and do not split over the 8 XCDs, both dtypes; every call is
+# repeated (once on another stream, with its own workspace) to check that the
+# result is bit-identical.
+SPLIT = [(256, 256, 4096), (300, 520, 2048), (512, 1024, 8192)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K", SPLIT)
+def test_linear_gemm_split_k(tl, M, N, K, dtype):
+    import torch
+    say(f"linear split-K gemm M={M} N={N} K={K} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr(("splitk", M, N, K, dtype)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, -1, dtype)
+    y_ref, bound = oracle.linear(x, packed, scale, -1, dtype=dtype)
+    xd, pd, sd = to_dev(x, _tdt(dtype)), to_dev(packed, None), to_dev(scale, torch.float16)
+    y1 = tl.linear(xd, pd, sd, -1)
+    y2 = tl.linear(xd, pd, sd, -1)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y3 = tl.linear(xd, pd, sd, -1)
+    side.synchronize()
+    torch.cuda.synchronize()
+    b1, b2, b3 = (bits_of(t) for t in (y1, y2, y3))
+    assert np.array_equal(b1, b2) and np.array_equal(b1, b3), "split-K result not repeatable"
+    check_within(widen(b1, dtype), y_ref, bound, f"split-K M={M} N={N} K={K} {dtype}")
+
+
 # Shapes large enough that the streaming kernel keeps several channel blocks
 # per workgroup: the per-channel cases run the full ring of 20 slabs in every
 # wave, the group-scaled one needs more workgroups than CUs.  Raw random bytes
