@@ -213,22 +213,31 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
         }
     }
     const bool fp16 = dtype == TERNARY_FP16;
-    ternary::GemvArgs fused[TERNARY_MAX_BATCH];
-    int nf = 0;
+    ternary::GemvArgs fused[TERNARY_MAX_BATCH], grouped_gemm[TERNARY_MAX_BATCH];
+    int nf = 0, ng = 0;
     for (int i = 0; i < count; ++i) {
         const ternary_problem &p = problems[i];
         if (p.M == 0 || p.N == 0)
             continue;
+        const ternary::GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
+                                     static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
+                                     p.group_size == 128};
         if (ternary::gemv_takes(p.M, p.K)) {
-            fused[nf++] = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
-                           static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
-                           p.group_size == 128};
+            fused[nf++] = a;
+        } else if (ternary::gemm_takes(p.M, p.K) &&
+                   ternary::gemm_big_takes(a.M, a.N, a.K, a.grouped)) {
+            grouped_gemm[ng++] = a;
         } else {
             const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,
                                              p.group_size, p.y, TERNARY_PATH_AUTO, stream);
             if (st != TERNARY_OK)
                 return st;
         }
+    }
+    if (ng) {
+        const int st = hip_status(ternary::launch_gemm_batch(grouped_gemm, ng, fp16, stream));
+        if (st != TERNARY_OK)
+            return st;
     }
     if (nf)
         return hip_status(ternary::launch_gemv_batch(fused, nf, fp16, stream));

@@ -274,11 +274,27 @@ __device__ __forceinline__ void wait_and_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One problem of a launch: y = x * (q (.) s)^T, K range split into ksplit
+// slices whose fp32 partial tiles go to `partial` when ksplit > 1.
+struct BigProblem {
+    const uint16_t *x;
+    const uint8_t *packed;
+    const uint16_t *scale;
+    uint16_t *y;
+    float4 *partial;
+    int M, N, K, ksplit;
+};
+
+// The problems of one launch; workgroups wg0[i] .. wg0[i+1]-1 belong to
+// problem i (wg0 ascending, wg0[0] == 0).
+struct BigBatch {
+    int count;
+    int wg0[kGemvMaxBatch];
+    BigProblem p[kGemvMaxBatch];
+};
+
 template <bool FP16, class C>
-__global__ void __launch_bounds__(C::THREADS, C::OCC)
-    gemm_dma_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                    const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N,
-                    int K, int ksplit, float4 *__restrict__ partial)
+__global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigBatch batch)
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
     // One LDS object per stage: the compiler then knows that a DMA into one
@@ -301,9 +317,22 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     // k+8, ... and walks every channel tile of each, so its L2 keeps that
     // token tile's x.  With a K split of `ksplit` slices, the slices of one
     // tile go to one XCD when the tiles split evenly over the XCDs.
+    // This workgroup's problem: one round of scalar loads and compares.
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxBatch; ++i)
+        pi += (i < batch.count && (int)blockIdx.x >= batch.wg0[i]) ? 1 : 0;
+    const BigProblem &P = batch.p[pi];
+    const uint16_t *__restrict__ x = P.x;
+    const uint8_t *__restrict__ packed = P.packed;
+    const uint16_t *__restrict__ scale = P.scale;
+    uint16_t *__restrict__ y = P.y;
+    float4 *__restrict__ partial = P.partial;
+    const int M = P.M, N = P.N, K = P.K, ksplit = P.ksplit;
+
     const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
     int tn, tm, tile = 0, slice = 0;
-    const int bid = blockIdx.x;
+    const int bid = (int)blockIdx.x - batch.wg0[pi];
     if (ksplit == 1) {
         if (ntm % 8 == 0) {
             const int xcd = bid & 7, slot = bid >> 3;
@@ -584,44 +613,99 @@ int big_ksplit(int tiles, int K)
     return ks;
 }
 
+// Launches the problems args[0..count) (all gemm_big_takes()) as one
+// grouped launch of the pipelined kernel, problems with the longest K first
+// so that the longest tiles start first.  When all their tiles together do not
+// cover the compute units, each problem's K range is split as big_ksplit()
+// says and per-problem reduce kernels follow.
 template <bool FP16>
-hipError_t launch_gemm_big(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
-                           const uint16_t *scale, uint16_t *y, hipStream_t stream)
+hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
 {
-    const int tiles = ((N + BigCfg::TN - 1) / BigCfg::TN) * ((M + BigCfg::TM - 1) / BigCfg::TM);
-    int ks = big_ksplit(tiles, K);
-    float4 *partial = nullptr;
-    if (ks > 1) {
-        void *ws = nullptr;
-        const size_t bytes = (size_t)tiles * ks * BigCfg::TN * BigCfg::TM * 4;
-        const hipError_t e = stream_workspace(stream, bytes, &ws);
-        if (e != hipSuccess)
-            return e;
-        if (ws)
-            partial = static_cast<float4 *>(ws);
-        else
-            ks = 1;  // under capture without a workspace: the unsplit kernel
+    int order[kGemvMaxBatch];
+    int tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        order[i] = i;
+        const GemvArgs &a = args[i];
+        tiles[i] = ((a.N + BigCfg::TN - 1) / BigCfg::TN) * ((a.M + BigCfg::TM - 1) / BigCfg::TM);
+        total += tiles[i];
     }
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), dim3(tiles * ks),
-                       dim3(BigCfg::THREADS), 0, stream, x, packed, scale, y, M, N, K, ks,
-                       partial);
-    if (ks > 1) {
-        const hipError_t e = hipGetLastError();
+    for (int i = 1; i < count; ++i)  // stable insertion sort, K descending
+        for (int j = i; j > 0 && args[order[j]].K > args[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    size_t ws_bytes = 0;
+    for (int i = 0; i < count; ++i) {
+        ks[i] = total < device_cus() ? big_ksplit(tiles[i], args[i].K) : 1;
+        if (ks[i] > 1)
+            ws_bytes += (size_t)tiles[i] * ks[i] * BigCfg::TN * BigCfg::TM * 4;
+    }
+    char *ws = nullptr;
+    if (ws_bytes) {
+        void *w = nullptr;
+        const hipError_t e = stream_workspace(stream, ws_bytes, &w);
         if (e != hipSuccess)
             return e;
-        const int64_t n4 = (int64_t)tiles * (BigCfg::TN * BigCfg::TM / 4);
+        ws = static_cast<char *>(w);
+        if (!ws)  // under capture without a workspace: the unsplit kernel
+            for (int i = 0; i < count; ++i)
+                ks[i] = 1;
+    }
+    dma::BigBatch b = {};
+    b.count = count;
+    int wg = 0;
+    size_t off = 0;
+    for (int r = 0; r < count; ++r) {
+        const int i = order[r];
+        const GemvArgs &a = args[i];
+        dma::BigProblem &p = b.p[r];
+        p.x = a.x;
+        p.packed = a.packed;
+        p.scale = a.scale;
+        p.y = a.y;
+        p.partial = nullptr;
+        if (ks[i] > 1) {
+            p.partial = reinterpret_cast<float4 *>(ws + off);
+            off += (size_t)tiles[i] * ks[i] * BigCfg::TN * BigCfg::TM * 4;
+        }
+        p.M = a.M;
+        p.N = a.N;
+        p.K = a.K;
+        p.ksplit = ks[i];
+        b.wg0[r] = wg;
+        wg += tiles[i] * ks[i];
+    }
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), dim3(wg), dim3(BigCfg::THREADS), 0,
+                       stream, b);
+    hipError_t e = hipGetLastError();
+    for (int r = 0; r < count && e == hipSuccess; ++r) {
+        const dma::BigProblem &p = b.p[r];
+        if (p.ksplit == 1)
+            continue;
+        const int i = order[r];
+        const int64_t n4 = (int64_t)tiles[i] * (BigCfg::TN * BigCfg::TM / 4);
         hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, BigCfg>), dim3((unsigned)((n4 + 255) / 256)),
-                           dim3(256), 0, stream, partial, scale, y, M, N, ks);
+                           dim3(256), 0, stream, p.partial, p.scale, p.y, p.M, p.N, p.ksplit);
+        e = hipGetLastError();
     }
-    return hipGetLastError();
+    return e;
+}
+
+hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
+{
+    return fp16 ? launch_gemm_big_batch<true>(args, count, stream)
+                : launch_gemm_big_batch<false>(args, count, stream);
 }
 
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
 {
-    if (gemm_big_takes(M, N, K, grouped))
-        return fp16 ? launch_gemm_big<true>(x, M, N, K, packed, scale, y, stream)
-                    : launch_gemm_big<false>(x, M, N, K, packed, scale, y, stream);
+    if (gemm_big_takes(M, N, K, grouped)) {
+        const GemvArgs a = {x, packed, scale, y, M, N, K, false};
+        return launch_gemm_batch(&a, 1, fp16, stream);
+    }
     if (fp16)
         return grouped ? launch_gemm_t<true, true>(x, M, N, K, packed, scale, y, stream)
                        : launch_gemm_t<true, false>(x, M, N, K, packed, scale, y, stream);

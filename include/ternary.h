@@ -158,8 +158,10 @@ typedef struct {
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
  * any error nothing is launched.  Problems the decode GEMV takes (1 <= M <=
  * ternary_gemv_max_m(), K % 128 == 0) run together in one launch per scale
- * mode (per-channel, group-128) and kernel class (M <= 2, larger M); the
- * others run as separate launches on the same stream.  Results are
+ * mode (per-channel, group-128) and kernel class (M <= 2, larger M);
+ * per-channel prefill problems with M >= 256, N >= 256 and K % 256 == 0 run
+ * together in one grouped GEMM launch (longest K first); the others run as
+ * separate launches on the same stream.  Results are
  * deterministic (the same batch gives the same bits) and each satisfies the
  * bound of ternary_linear; they may differ from a single ternary_linear call on
  * the same problem in the last bits, because a batch may split a problem's K

@@ -1,4 +1,5 @@
-"""ternary_linear_batch: one fused decode launch for several projections.
+"""ternary_linear_batch: one fused decode launch, or one grouped prefill
+GEMM launch, for several projections.
 
 Each output must lie within the bound of the oracle, and a batch must give
 the same bits every time it runs.  Batched and single calls may differ in the
@@ -83,6 +84,37 @@ def test_batch_big_k_chunked(tl):
     say("batch with chunked activations (M=8, K=18944; M=4, K=25600)")
     specs = [(8, 200, 18944, -1), (4, 100, 25600, 128), (8, 64, 5120, 128)]
     _run_and_check(tl, _problems(np.random.default_rng(42), specs), samples=600)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_batch_grouped_prefill(tl, dtype):
+    # Per-channel prefill problems of one grouped GEMM launch: 256 + 6 + 16 +
+    # 15 + 9 tiles of 256 x 128, so no K range is split; different K, ragged M
+    # and N, a problem that shares another's activations (as q/k/v do), plus a
+    # group-scaled problem that runs on its own.
+    import torch
+    say(f"grouped prefill batch {dtype}")
+    specs = [(2048, 4096, 512, -1), (300, 520, 1024, -1), (2048, 256, 256, -1),
+             (300, 1100, 2048, -1), (256, 300, 512, 128)]
+    rng = np.random.default_rng(43)
+    probs = _problems(rng, specs, dtype)
+    x1, d1 = probs[1][0], probs[1][4]
+    codes = synth.draw_codes(rng, 700, 1024, 0.3, 0.3)
+    packed, _ = oracle.pack(codes)
+    scale = synth.draw_scales(rng, 700, 1024, -1)
+    probs.append((x1, packed, scale, -1,
+                  (d1[0], to_dev(packed, None), to_dev(scale, torch.float16), -1)))
+    _run_and_check(tl, probs, dtype=dtype)
+
+
+def test_batch_grouped_prefill_split(tl):
+    # Small per-channel prefill problems (32 + 9 + 15 tiles): each problem
+    # whose K allows it is split (its own partial tiles and reduce launch),
+    # the K = 256 one is not.
+    say("grouped prefill batch with split K")
+    specs = [(512, 2048, 1024, -1), (300, 520, 4096, -1), (300, 1100, 2048, -1),
+             (256, 300, 256, -1)]
+    _run_and_check(tl, _problems(np.random.default_rng(44), specs))
 
 
 def test_batch_rejects_alias_on_device(tl):
