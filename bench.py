@@ -18,8 +18,10 @@ Printed (one JSON line on stdout):
                stream around the timed replay), against 8 TB/s; `traffic` = HBM bytes per launch from rocprofv3
                FETCH_SIZE/WRITE_SIZE counters (profiles/), or null when the
                kernels changed since those were taken;
-  prefill      the same seven projections at M = 2048 tokens (GEMM path):
-               TFLOP/s and its own roofline against 2.5 PFLOP/s bf16 MFMA;
+  prefill      the same seven projections at M = 2048 tokens (GEMM path), one
+               ternary_linear_batch call per step (one grouped GEMM launch):
+               TFLOP/s and its own roofline against 2.5 PFLOP/s bf16 MFMA, with
+               seven separate calls per step and per-projection launches beside;
   pack         ternary_pack / ternary_unpack throughput on the 18944 x 4096 weight;
   cpu_baseline the CPU oracle (fp64, OpenMP) on the full decode layer at
                M = 1 on this host's cores, same algorithmic bytes.
@@ -28,7 +30,9 @@ Algorithmic bytes per launch: N*K/4 (codes) + scales (2N, or N*K/64 grouped)
 
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
 digests two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE)
-into profiles/gemv_decode_7b_counters.txt.
+into profiles/gemv_stream_7b_decode_m1_counters.txt (the fused decode launch)
+and profiles/gemm_dma_7b_prefill_m2048_counters.txt (the grouped prefill
+launch).
 """
 
 from __future__ import annotations
@@ -50,7 +54,14 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 ROTATE_BYTES = 1 << 30          # weight bytes cycled per rotation (> 256 MB MALL)
 COPY_PROBE_BYTES = 512 << 20    # known-size copy kernel used to calibrate counters
-COUNTERS_FILE = ROOT / "profiles" / "gemv_decode_7b_counters.txt"
+COUNTERS = {
+    # kernel family -> (file, kernel-name substring, what the launch is)
+    "decode": (ROOT / "profiles" / "gemv_stream_7b_decode_m1_counters.txt", "gemv",
+               "the fused decode GEMV launch (all 7 projections of the 7B layer at M=1)"),
+    "prefill": (ROOT / "profiles" / "gemm_dma_7b_prefill_m2048_counters.txt", "gemm_dma_kernel",
+                "the grouped prefill GEMM launch (all 7 projections of the 7B layer at "
+                "M=2048)"),
+}
 DECODE_CFG, PREFILL_CFG = 2, 3
 
 
@@ -232,55 +243,66 @@ def read_counter_csv(d: Path):
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
-    """Digest two counter runs into profiles/gemv_decode_7b_counters.txt."""
-    res = {}
+    """Digest two counter runs into one counters file per kernel family: the
+    largest-grid dispatch of the family is the fused (decode) or grouped
+    (prefill) launch of the layer's seven projections."""
+    per = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read_counter_csv(Path(d))
         if not rows:
             raise SystemExit(f"no counter_collection.csv under {d}")
-        per_dispatch = {}
+        disp = {}
         for r in rows:
             if r.get("Counter_Name") != name:
                 continue
             key = r["Dispatch_Id"]
-            per_dispatch.setdefault(key, [r["Kernel_Name"], int(r.get("Grid_Size", 0)), 0.0])
-            per_dispatch[key][2] += float(r["Counter_Value"])
-        # the fused decode launch is the gemv dispatch with the largest grid
-        grids = [gs for k, gs, _ in per_dispatch.values() if "gemv_kernel" in k]
-        top = max(grids) if grids else -1
-        gemv = [v for k, gs, v in per_dispatch.values() if "gemv_kernel" in k and gs == top]
-        probe = [v for k, _, v in per_dispatch.values() if "neg_kernel" in k]
-        if not gemv or not probe:
-            raise SystemExit(f"{name}: missing gemv ({len(gemv)}) or copy-probe ({len(probe)}) dispatches")
-        res[name] = (sum(gemv) / len(gemv), len(gemv), sum(probe) / len(probe), len(probe))
-    f_g, nf, f_p, _ = res["FETCH_SIZE"]
-    w_g, nw, w_p, _ = res["WRITE_SIZE"]
-    k_fetch = COPY_PROBE_BYTES / (f_p * 1024.0)
-    k_write = COPY_PROBE_BYTES / (w_p * 1024.0)
-    traffic = f_g * 1024.0 * k_fetch + w_g * 1024.0 * k_write
-    lines = [
-        "# HBM traffic of the fused decode GEMV launch (gemv_kernel, all 7 projections of",
-        "# the 7B decode layer at M=1) from two rocprofv3 --pmc runs of bench.py:",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- \\",
-        "#       python3 bench.py --no-cpu --steps 10 --warmup 2 --prefill-steps 1",
-        "#   (the same with --pmc WRITE_SIZE into <W>), then",
-        "#   python3 bench.py --summarize-pmc <F> <W>",
-        "# Counters read KiB per dispatch; each is scaled by a copy kernel of known size",
-        f"# (torch.neg over {COPY_PROBE_BYTES >> 20} MiB fp32: reads and writes that many bytes).",
-        f"source_hash {kernel_source_hash()}",
-        f"gemv_dispatches_fetch {nf}",
-        f"gemv_dispatches_write {nw}",
-        f"gemv_fetch_kib_mean {f_g:.3f}",
-        f"gemv_write_kib_mean {w_g:.3f}",
-        f"probe_fetch_kib {f_p:.3f}",
-        f"probe_write_kib {w_p:.3f}",
-        f"fetch_scale {k_fetch:.5f}",
-        f"write_scale {k_write:.5f}",
-        f"gemv_traffic_bytes_per_launch {traffic:.1f}",
-    ]
-    COUNTERS_FILE.parent.mkdir(exist_ok=True)
-    COUNTERS_FILE.write_text("\n".join(lines) + "\n")
-    print("\n".join(lines))
+            disp.setdefault(key, [r["Kernel_Name"], int(r.get("Grid_Size", 0)), 0.0])
+            disp[key][2] += float(r["Counter_Value"])
+        per[name] = disp
+    probe = {}
+    for name, disp in per.items():
+        v = [c for k, _, c in disp.values() if "neg_kernel" in k]
+        if not v:
+            raise SystemExit(f"{name}: no copy-probe dispatch")
+        probe[name] = sum(v) / len(v)
+    k_fetch = COPY_PROBE_BYTES / (probe["FETCH_SIZE"] * 1024.0)
+    k_write = COPY_PROBE_BYTES / (probe["WRITE_SIZE"] * 1024.0)
+    for fam, (path, sub, what) in COUNTERS.items():
+        got = {}
+        for name, disp in per.items():
+            grids = [gs for k, gs, _ in disp.values() if sub in k]
+            if not grids:
+                raise SystemExit(f"{name}: no {sub} dispatch")
+            top = max(grids)
+            v = [c for k, gs, c in disp.values() if sub in k and gs == top]
+            got[name] = (sum(v) / len(v), len(v), top)
+        (f_k, nf, grid), (w_k, nw, _) = got["FETCH_SIZE"], got["WRITE_SIZE"]
+        traffic = f_k * 1024.0 * k_fetch + w_k * 1024.0 * k_write
+        lines = [
+            f"# HBM traffic of {what}",
+            "# from two rocprofv3 --pmc runs of bench.py:",
+            "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- \\",
+            "#       python3 bench.py --no-cpu --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2",
+            "#   (the same with --pmc WRITE_SIZE into <W>), then",
+            "#   python3 bench.py --summarize-pmc <F> <W>",
+            "# Counters read KiB per dispatch (summed over instances); each is scaled by what",
+            f"# it reads for a copy kernel of known size (torch.neg over {COPY_PROBE_BYTES >> 20} MiB",
+            "# fp32: reads and writes that many bytes).",
+            f"source_hash {kernel_source_hash()}",
+            f"grid_threads {grid}",
+            f"dispatches_fetch {nf}",
+            f"dispatches_write {nw}",
+            f"fetch_kib_mean {f_k:.3f}",
+            f"write_kib_mean {w_k:.3f}",
+            f"probe_fetch_kib {probe['FETCH_SIZE']:.3f}",
+            f"probe_write_kib {probe['WRITE_SIZE']:.3f}",
+            f"fetch_scale {k_fetch:.5f}",
+            f"write_scale {k_write:.5f}",
+            f"traffic_bytes_per_launch {traffic:.1f}",
+        ]
+        path.parent.mkdir(exist_ok=True)
+        path.write_text("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
 TRACE_FILE = ROOT / "profiles" / "kernels_7b_decode_prefill_trace.txt"
@@ -336,18 +358,20 @@ def summarize_trace(d: str) -> None:
     print("\n".join(lines))
 
 
-def stored_traffic():
-    """Traffic per launch from the committed counters, if taken on these kernels."""
-    if not COUNTERS_FILE.exists():
+def stored_traffic(family):
+    """Traffic per launch from the committed counters of a kernel family
+    ("decode", "prefill"), if they were taken on these kernel sources."""
+    path = COUNTERS[family][0]
+    if not path.exists():
         return None
     kv = {}
-    for ln in COUNTERS_FILE.read_text().splitlines():
+    for ln in path.read_text().splitlines():
         if ln and not ln.startswith("#"):
             k, v = ln.split(None, 1)
             kv[k] = v.strip()
     if kv.get("source_hash") != kernel_source_hash():
         return None
-    return float(kv["gemv_traffic_bytes_per_launch"])
+    return float(kv["traffic_bytes_per_launch"])
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -437,7 +461,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=10,
+                    help="untimed prefill steps first (clocks settle under sustained MFMA load)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
@@ -490,11 +516,12 @@ def main():
         shapes_out[s.name] = {"N": s.N, "K": s.K, "us": round(dur[j] * 1e6, 3),
                               "GBps": round(b / dur[j] / 1e9, 1),
                               "frac": round(b / dur[j] / 1e9 / HBM_PEAK_GBPS, 4)}
-    traffic = stored_traffic()
+    traffic = stored_traffic("decode")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if traffic is None else round(traffic, 1),
-                "kernel": "gemv_kernel<bf16, per-channel>: one fused launch of the 7 projections",
+                "kernel": "gemv_stream_kernel<bf16, per-channel, M=1>: one fused launch of the "
+                          "7 projections",
                 "alg_bytes_per_launch": step_bytes,
                 "mean_launch_us": round(mean_dur * 1e6, 3)}
     log(f"[bench] decode per-launch {shapes_out}")
@@ -504,9 +531,14 @@ def main():
 
     log("[bench] building the prefill layer (config 3, M=2048)")
     pre = Layer(tl, PREFILL_CFG, 2048, copies=2)
-    t_pre = time_region(tl, pre, args.prefill_steps, 2, separate=True)
     pre_flops = sum(pre.flops_per_launch(j) for j in range(len(pre.shapes)))
+    # One step = one ternary_linear_batch call = one grouped GEMM launch (the
+    # layer has enough tiles that no K range is split): events on the launch
+    # stream around the steps give the launch's mean duration.
+    t_pre = time_region(tl, pre, args.prefill_steps, args.prefill_warmup)
     pre_value = pre_flops * args.prefill_steps / t_pre / 1e12
+    t_pre_sep = time_region(tl, pre, args.prefill_steps, args.prefill_warmup, separate=True)
+    pre_sep_value = pre_flops * args.prefill_steps / t_pre_sep / 1e12
     per_p = time_launches(tl, pre, args.prefill_steps)
     dur_p = [sum(per_p[i][j] for i in range(args.prefill_steps)) / args.prefill_steps
              for j in range(len(pre.shapes))]
@@ -514,19 +546,34 @@ def main():
     for j, s in enumerate(pre.shapes):
         f = pre.flops_per_launch(j)
         pre_shapes[s.name] = {"N": s.N, "K": s.K, "us": round(dur_p[j] * 1e6, 2),
-                              "TFLOPs": round(f / dur_p[j] / 1e12, 1)}
-    ach_p = (pre_flops / len(pre.shapes)) / (sum(dur_p) / len(pre.shapes)) / 1e12
+                              "TFLOPs": round(f / dur_p[j] / 1e12, 1),
+                              "frac": round(f / dur_p[j] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    mean_pre = t_pre / args.prefill_steps
+    ach_p = pre_flops / mean_pre / 1e12
+    traffic_p = stored_traffic("prefill")
     prefill = {
         "metric": "ternary_linear TFLOP/s at M=2048 (7B prefill layer, per-channel)",
         "value": round(pre_value, 1), "unit": "TFLOP/s",
-        "ms_per_layer": round(t_pre / args.prefill_steps * 1e3, 4),
+        "frac_of_mfma_peak": round(pre_value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "ms_per_layer": round(mean_pre * 1e3, 4),
+        "timing": f"eager, {args.prefill_warmup} untimed steps first (sustained clocks), one "
+                  "ternary_linear_batch call per step (one grouped GEMM launch); seven separate "
+                  "calls per step and per-projection launches beside",
+        "separate_launches_value": round(pre_sep_value, 1),
         "path": tl.select_path(2048, 4096, 4096, -1),
         "roofline": {"bound": "mfma", "achieved": round(ach_p, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach_p / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_kernel (bf16 MFMA, per-channel)"},
+                     "traffic": None if traffic_p is None else round(traffic_p, 1),
+                     "kernel": "gemm_dma_kernel<bf16, per-channel>: one grouped launch of the "
+                               "7 projections",
+                     "alg_flops_per_launch": pre_flops,
+                     "alg_bytes_per_launch": sum(pre.bytes_per_launch(j)
+                                                 for j in range(len(pre.shapes))),
+                     "mean_launch_us": round(mean_pre * 1e6, 2)},
         "shapes": pre_shapes,
     }
-    log(f"[bench] prefill {pre_value:.1f} TFLOP/s {pre_shapes}")
+    log(f"[bench] prefill {pre_value:.1f} TFLOP/s (separate calls {pre_sep_value:.1f}) "
+        f"{pre_shapes}")
     pack = bench_pack(tl)
     log(f"[bench] pack {pack}")
 
