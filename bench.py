@@ -22,6 +22,9 @@ Printed (one JSON line on stdout):
                ternary_linear_batch call per step (one grouped GEMM launch):
                TFLOP/s and its own roofline against 2.5 PFLOP/s bf16 MFMA, with
                seven separate calls per step and per-projection launches beside;
+  configs      every other (config, shape, M) of the five workloads: per-launch time on
+               the automatic path as GB/s and TFLOP/s with both roofline fractions;
+  crossover    config 4 at each M: forced GEMV and GEMM launch times (GEMV -> GEMM);
   pack         ternary_pack / ternary_unpack throughput on the 18944 x 4096 weight;
   cpu_baseline the CPU oracle (fp64, OpenMP) on the full decode layer at
                M = 1 on this host's cores, same algorithmic bytes.
@@ -282,7 +285,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
             f"# HBM traffic of {what}",
             "# from two rocprofv3 --pmc runs of bench.py:",
             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- \\",
-            "#       python3 bench.py --no-cpu --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2",
+            "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2",
             "#   (the same with --pmc WRITE_SIZE into <W>), then",
             "#   python3 bench.py --summarize-pmc <F> <W>",
             "# Counters read KiB per dispatch (summed over instances); each is scaled by what",
@@ -444,6 +447,96 @@ def bench_pack(tl):
             "unpack_GBps": round(nbytes / tu / 1e9, 1), "roundtrip_exact": ok}
 
 
+def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
+    """Every (config, shape, M) of the five workloads that the headline lines do
+    not already time: per-launch time on the automatic path, as GB/s and
+    TFLOP/s with both roofline fractions; for config 4 also the forced GEMV and
+    GEMM paths at each M the GEMV takes, to place the GEMV -> GEMM crossover.
+
+    Timing: the weights of the shape's first case (drawn as for that case; x
+    per M from the M's own generator) are copied R times into one allocation,
+    R * weight bytes >= 1 GiB where R <= max_copies, and a HIP graph of R
+    launches (one per copy), captured after a warm-up on its capture stream,
+    is replayed between events on the stream it replays on."""
+    import torch
+    import numpy as np
+    import synth
+    out, cross = {}, {}
+    cap = torch.cuda.Stream()
+
+    def graph_us(fn, R):
+        with torch.cuda.stream(cap):
+            for r in range(2):
+                fn(r)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for r in range(R):
+                fn(r)
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(2):
+            # the replay runs on the current stream: the events go there too
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / R
+            best = t if best is None else min(best, t)
+        del g
+        return best
+
+    for ci in (0, 1, 2, 4):
+        cfg = synth.CONFIGS[ci]
+        out[str(ci)] = {}
+        for si, shp in enumerate(cfg.shapes):
+            ms = [m for m in cfg.Ms if not (ci == 2 and m == 1)]  # M=1 is the headline
+            if not ms:
+                continue
+            case = synth.make_case(ci, si, cfg.Ms[0])
+            q = to_dev(case.codes)
+            p1 = tl.pack(q)
+            del q
+            s1 = to_dev(case.scale, torch.float16)
+            wbytes = p1.numel() + 2 * s1.numel()
+            R = int(min(max_copies, max(1, math.ceil(min_rotate / wbytes))))
+            P = p1.unsqueeze(0).expand(R, *p1.shape).contiguous()
+            S = s1.unsqueeze(0).expand(R, *s1.shape).contiguous()
+            del p1, s1
+            res = {}
+            for M in ms:
+                rng = synth.rng_for(ci, si, M)
+                x = to_dev(synth.draw_x(rng, M, shp.K, "bf16"), torch.bfloat16)
+                y = torch.empty((M, shp.N), dtype=torch.bfloat16, device="cuda:0")
+                b, f = alg_bytes(shp.N, shp.K, M, cfg.group_size), 2 * M * shp.N * shp.K
+
+                def run(path):
+                    return graph_us(lambda r: tl.linear(x, P[r], S[r], cfg.group_size,
+                                                        path=path, out=y), R)
+
+                t = run("auto")
+                res[str(M)] = {"path": tl.select_path(M, shp.N, shp.K, cfg.group_size),
+                               "us": round(t * 1e6, 3), "GBps": round(b / t / 1e9, 1),
+                               "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4),
+                               "TFLOPs": round(f / t / 1e12, 2),
+                               "mfma_frac": round(f / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "copies": R}
+                if ci == 4:
+                    c = {"gemm_us": round(run("gemm") * 1e6, 3)}
+                    if M <= tl.gemv_max_m():
+                        c["gemv_us"] = round(run("gemv") * 1e6, 3)
+                    cross.setdefault(shp.name, {})[str(M)] = c
+                del x, y
+            out[str(ci)][shp.name] = res
+            del P, S
+            torch.cuda.empty_cache()
+            log(f"[bench] config {ci} {shp.name}: {res}")
+    return out, cross
+
+
 def copy_probe():
     """A plain read+write kernel of known size, for counter calibration."""
     import torch
@@ -465,6 +558,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed prefill steps first (clocks settle under sustained MFMA load)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--detail", type=str, default=None, help="write per-shape results here")
@@ -576,6 +671,7 @@ def main():
         f"{pre_shapes}")
     pack = bench_pack(tl)
     log(f"[bench] pack {pack}")
+    configs, crossover = (None, None) if args.no_sweep else sweep_configs(tl)
 
     cpu = None
     if not args.no_cpu:
@@ -614,6 +710,8 @@ def main():
         "roofline": roofline,
         "decode_shapes": shapes_out,
         "prefill": prefill,
+        "configs": configs,
+        "crossover": crossover,
         "pack": pack,
         "cpu_baseline": cpu,
         "kernels_hash": kernel_source_hash(),
