@@ -225,7 +225,7 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
         if (ternary::gemv_takes(p.M, p.K)) {
             fused[nf++] = a;
         } else if (ternary::gemm_takes(p.M, p.K) &&
-                   ternary::gemm_big_takes(a.M, a.N, a.K, a.grouped)) {
+                   ternary::gemm_big_takes(a.M, a.N, a.K, a.grouped, a.scale)) {
             grouped_gemm[ng++] = a;
         } else {
             const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,

@@ -293,10 +293,14 @@ struct BigBatch {
     BigProblem p[kGemvMaxBatch];
 };
 
-template <bool FP16, class C>
+template <bool FP16, bool GROUPED, class C>
 __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigBatch batch)
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
+    // Group-128 scales: every stage also carries one dword per channel, the
+    // scales of the two groups of the 4-step round it belongs to.
+    static_assert(!GROUPED || (C::TN == THREADS && NS == 4), "one scale dword per thread");
+    constexpr int VPS = C::VPS + (GROUPED ? 1 : 0);  // vector memory ops per thread and stage
     // One LDS object per stage: the compiler then knows that a DMA into one
     // stage does not write the stage being read and waits for nothing there.
     __shared__ __attribute__((aligned(16))) uint4 sx0[C::XSTAGE], sx1[C::XSTAGE],
@@ -305,6 +309,10 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         sw2[NS > 2 ? C::WSTAGE : 1], sw3[NS > 3 ? C::WSTAGE : 1];
     lds_u4 *const lx[4] = {(lds_u4 *)sx0, (lds_u4 *)sx1, (lds_u4 *)sx2, (lds_u4 *)sx3};
     lds_u32 *const lw[4] = {(lds_u32 *)sw0, (lds_u32 *)sw1, (lds_u32 *)sw2, (lds_u32 *)sw3};
+    constexpr int SSTAGE = GROUPED ? C::TN : 1;
+    __shared__ __attribute__((aligned(16))) uint32_t sc0[SSTAGE], sc1[SSTAGE], sc2[SSTAGE],
+        sc3[SSTAGE];
+    lds_u32 *const lsc[4] = {(lds_u32 *)sc0, (lds_u32 *)sc1, (lds_u32 *)sc2, (lds_u32 *)sc3};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -312,11 +320,6 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     const int wn = wave % C::WGN;
     const int wm = wave / C::WGN;
 
-    // Tile order: workgroup b runs on XCD b % 8.  Without a K split, when the
-    // token tiles split evenly over the 8 XCDs, XCD k takes token tiles k,
-    // k+8, ... and walks every channel tile of each, so its L2 keeps that
-    // token tile's x.  With a K split of `ksplit` slices, the slices of one
-    // tile go to one XCD when the tiles split evenly over the XCDs.
     // This workgroup's problem: one round of scalar loads and compares.
     int pi = 0;
 #pragma unroll
@@ -330,6 +333,11 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     float4 *__restrict__ partial = P.partial;
     const int M = P.M, N = P.N, K = P.K, ksplit = P.ksplit;
 
+    // Tile order: workgroup b runs on XCD b % 8.  Without a K split, when the
+    // token tiles split evenly over the 8 XCDs, XCD k takes token tiles k,
+    // k+8, ... and walks every channel tile of each, so its L2 keeps that
+    // token tile's x.  With a K split of `ksplit` slices, the slices of one
+    // tile go to one XCD when the tiles split evenly over the XCDs.
     const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
     int tn, tm, tile = 0, slice = 0;
     const int bid = (int)blockIdx.x - batch.wg0[pi];
@@ -379,6 +387,11 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         const int row = d >> 2;
         woff[i] = n0 + row < N ? (n0 + row) * (K >> 2) + 4 * (d & 3) : kOOB;
     }
+    // Scales: thread t loads channel n0 + t's pair of groups.
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(scale), (short)0,
+        GROUPED ? (int)((uint32_t)N * (uint32_t)(K >> 7) * 2u) : 0, 0x00020000);
+    const int soff = GROUPED && n0 + tid < N ? (n0 + tid) * (K >> 7) * 2 : kOOB;
     // Wave-uniform LDS destinations of this wave's DMAs (kept in SGPRs).
     const int wave_chunk = __builtin_amdgcn_readfirstlane(wave) * 64;
 
@@ -394,14 +407,18 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
         for (int i = 0; i < C::WI; ++i)
             dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * (TK / 4));
+        if constexpr (GROUPED)
+            dma_to_lds<4>(sr, (void *)(lsc[s] + wave_chunk), soff, (kc >> 2) * 4);
     };
 
     f32x4_t acc[FN][FM];
+    f32x4_t part[GROUPED ? FN : 1][GROUPED ? FM : 1];  // the current group's sums
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // Per-lane LDS read offsets.  x: token row (lane & 15) of each fragment,
     // logical chunk 2g + kk; packed: dword g of channel row (lane & 15).
@@ -431,8 +448,31 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
                 const uint4 a = kk ? make_uint4(d[4], d[5], d[6], d[7])
                                    : make_uint4(d[0], d[1], d[2], d[3]);
 #pragma unroll
-                for (int j = 0; j < FM; ++j)
-                    acc[f][j] = mfma<FP16>(a, xf[j], acc[f][j]);
+                for (int j = 0; j < FM; ++j) {
+                    if constexpr (GROUPED)  // a group starts at even steps (slices are whole rounds)
+                        part[f][j] = mfma<FP16>(a, xf[j], (s % 2 == 0 && kk == 0) ? zero4 : part[f][j]);
+                    else
+                        acc[f][j] = mfma<FP16>(a, xf[j], acc[f][j]);
+                }
+            }
+        }
+        if constexpr (GROUPED) {
+            if constexpr (s % 2 == 1) {
+                // End of a 128-K group: fold its sums with the group's scales
+                // (low half of the stage's dwords for the round's first
+                // group, high half for its second).
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    const u32x4_t w = *reinterpret_cast<const lds_u4 *>(
+                        lsc[s] + wn * FN * 16 + f * 16 + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sc = f16_bits_to_f32((uint16_t)(s == 1 ? w[r] : w[r] >> 16));
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            acc[f][j][r] += sc * part[f][j][r];
+                    }
+                }
             }
         }
     };
@@ -442,7 +482,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     // of step kt+NS-1 into the stage kt-1 used, then compute stage kt.
     auto step = [&](auto S, int kt) {
         constexpr int s = decltype(S)::value;
-        wait_and_barrier<(NS - 2) * C::VPS>();
+        wait_and_barrier<(NS - 2) * VPS>();
         issue(std::integral_constant<int, (s + NS - 1) % NS>{}, kt + NS - 1);
         compute(S);
     };
@@ -488,8 +528,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         const int n = n0 + (wn * FN + f) * 16 + 4 * g;
         float post[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            post[r] = n + r < N ? 0.5f * f16_bits_to_f32(scale[n + r]) : 0.f;  // weights are +-2
+        for (int r = 0; r < 4; ++r)  // weights are +-2; group scales are already in
+            post[r] = n + r >= N ? 0.f : GROUPED ? 0.5f : 0.5f * f16_bits_to_f32(scale[n + r]);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int m = m0 + (wm * FM + j) * 16 + fr;
@@ -514,9 +554,9 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 
 // Second half of a split-K product: thread t of the grid takes float4 t of
 // the partial tiles (the layout gemm_dma_kernel stores), adds the `ksplit`
-// slices in slice order, applies the per-channel scale and writes four
-// outputs of one token.
-template <bool FP16, class C>
+// slices in slice order, applies the per-channel scale (group scales are
+// already in the partials) and writes four outputs of one token.
+template <bool FP16, bool GROUPED, class C>
 __global__ void __launch_bounds__(256)
     gemm_split_reduce(const float4 *__restrict__ partial, const uint16_t *__restrict__ scale,
                       uint16_t *__restrict__ y, int M, int N, int ksplit)
@@ -548,13 +588,13 @@ __global__ void __launch_bounds__(256)
         uint32_t o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            o[r] = round_out<FP16>(a[r] * (0.5f * f16_bits_to_f32(scale[n + r])));
+            o[r] = round_out<FP16>(a[r] * (GROUPED ? 0.5f : 0.5f * f16_bits_to_f32(scale[n + r])));
         *reinterpret_cast<uint2 *>(yr + n) = make_uint2(o[0] | o[1] << 16, o[2] | o[3] << 16);
     } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (n + r < N)
-                yr[n + r] = round_out<FP16>(a[r] * (0.5f * f16_bits_to_f32(scale[n + r])));
+                yr[n + r] = round_out<FP16>(a[r] * (GROUPED ? 0.5f : 0.5f * f16_bits_to_f32(scale[n + r])));
     }
 }
 
@@ -572,16 +612,21 @@ hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *
 
 }  // namespace
 
-// Tile shape, wave grid, stage count and waves per SIMD of the pipelined kernel.
+// Tile shape, wave grid, stage count and waves per SIMD of the pipelined
+// kernel: per-channel problems run two workgroups per CU; group-scaled ones
+// keep a second set of accumulators (the current group's sums) and run one.
 typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;
+typedef dma::Cfg<256, 128, 4, 1, 4, 1> BigCfgG;
 
-// The pipelined kernel takes per-channel problems whose K is a whole number
-// of 64-wide steps and that fill its tiles.
-bool gemm_big_takes(int M, int N, int K, bool grouped)
+// The pipelined kernel takes problems whose K is a whole number of 4-step
+// rounds (256), whose buffer offsets stay below the out-of-range marker, and
+// (group scales) whose scale array is 4-byte aligned: it loads a channel's
+// two scales of a round as one dword.
+bool gemm_big_takes(int M, int N, int K, bool grouped, const void *scale)
 {
-    // buffer offsets are 32-bit and must stay below the out-of-range marker
-    return !grouped && M >= 256 && N >= 256 && K % (dma::TK * BigCfg::NS) == 0 &&
-           (int64_t)M * K * 2 < dma::kOOB && (int64_t)N * (K / 4) < dma::kOOB;
+    return M >= 1 && N >= 1 && K % (dma::TK * BigCfg::NS) == 0 &&
+           (int64_t)M * K * 2 < dma::kOOB && (int64_t)N * (K / 4) < dma::kOOB &&
+           (!grouped || (((uintptr_t)scale & 3) == 0 && (int64_t)N * (K / 128) * 2 < dma::kOOB));
 }
 
 // Compute units of the current device (cached per device).
@@ -601,46 +646,56 @@ int device_cus()
     return cus[dev];
 }
 
-// K slices of the pipelined kernel: doubled while the tiles do not cover the
-// compute units and each slice keeps at least two rounds of NS steps.
+// K slices of the pipelined kernel: the smallest divisor of the problem's
+// number of 4-step rounds that lets tiles x slices cover the compute units,
+// keeping at least two rounds per slice (else the largest divisor that
+// does), within a 2 GiB workspace.
 int big_ksplit(int tiles, int K)
 {
-    const int nk = K / dma::TK, ns = BigCfg::NS, cus = device_cus();
-    int ks = 1;
-    while ((int64_t)tiles * ks < cus && nk % (2 * ks * ns) == 0 && nk / (2 * ks) >= 2 * ns &&
-           (int64_t)tiles * ks * 2 * BigCfg::TN * BigCfg::TM * 4 <= (int64_t(1) << 31))
-        ks *= 2;
-    return ks;
+    const int rounds = K / (dma::TK * BigCfg::NS), cus = device_cus();
+    if ((int64_t)tiles >= cus)
+        return 1;
+    const int64_t want = (cus + tiles - 1) / tiles;
+    int best = 1;
+    for (int d = 2; d <= rounds / 2; ++d) {
+        if (rounds % d != 0 ||
+            (int64_t)tiles * d * BigCfg::TN * BigCfg::TM * 4 > (int64_t(1) << 31))
+            continue;
+        best = d;
+        if (d >= want)
+            break;
+    }
+    return best;
 }
 
-// Launches the problems args[0..count) (all gemm_big_takes()) as one
-// grouped launch of the pipelined kernel, problems with the longest K first
-// so that the longest tiles start first.  When all their tiles together do not
-// cover the compute units, each problem's K range is split as big_ksplit()
-// says and per-problem reduce kernels follow.
-template <bool FP16>
-hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
+// Launches the problems args[idx[0..count)) (all gemm_big_takes(), one scale
+// mode) as one grouped launch of the pipelined kernel, problems with the
+// longest K first so that the longest tiles start first.  When all their
+// tiles together do not cover the compute units, each problem's K range is
+// split as big_ksplit() says and per-problem reduce kernels follow.
+template <bool FP16, bool GROUPED, class C>
+hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipStream_t stream)
 {
     int order[kGemvMaxBatch];
     int tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
     int64_t total = 0;
     for (int i = 0; i < count; ++i) {
         order[i] = i;
-        const GemvArgs &a = args[i];
-        tiles[i] = ((a.N + BigCfg::TN - 1) / BigCfg::TN) * ((a.M + BigCfg::TM - 1) / BigCfg::TM);
+        const GemvArgs &a = args[idx[i]];
+        tiles[i] = ((a.N + C::TN - 1) / C::TN) * ((a.M + C::TM - 1) / C::TM);
         total += tiles[i];
     }
     for (int i = 1; i < count; ++i)  // stable insertion sort, K descending
-        for (int j = i; j > 0 && args[order[j]].K > args[order[j - 1]].K; --j) {
+        for (int j = i; j > 0 && args[idx[order[j]]].K > args[idx[order[j - 1]]].K; --j) {
             const int t = order[j];
             order[j] = order[j - 1];
             order[j - 1] = t;
         }
     size_t ws_bytes = 0;
     for (int i = 0; i < count; ++i) {
-        ks[i] = total < device_cus() ? big_ksplit(tiles[i], args[i].K) : 1;
+        ks[i] = total < device_cus() ? big_ksplit(tiles[i], args[idx[i]].K) : 1;
         if (ks[i] > 1)
-            ws_bytes += (size_t)tiles[i] * ks[i] * BigCfg::TN * BigCfg::TM * 4;
+            ws_bytes += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
     }
     char *ws = nullptr;
     if (ws_bytes) {
@@ -659,7 +714,7 @@ hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t st
     size_t off = 0;
     for (int r = 0; r < count; ++r) {
         const int i = order[r];
-        const GemvArgs &a = args[i];
+        const GemvArgs &a = args[idx[i]];
         dma::BigProblem &p = b.p[r];
         p.x = a.x;
         p.packed = a.packed;
@@ -668,7 +723,7 @@ hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t st
         p.partial = nullptr;
         if (ks[i] > 1) {
             p.partial = reinterpret_cast<float4 *>(ws + off);
-            off += (size_t)tiles[i] * ks[i] * BigCfg::TN * BigCfg::TM * 4;
+            off += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
         }
         p.M = a.M;
         p.N = a.N;
@@ -677,7 +732,7 @@ hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t st
         b.wg0[r] = wg;
         wg += tiles[i] * ks[i];
     }
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, BigCfg>), dim3(wg), dim3(BigCfg::THREADS), 0,
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, GROUPED, C>), dim3(wg), dim3(C::THREADS), 0,
                        stream, b);
     hipError_t e = hipGetLastError();
     for (int r = 0; r < count && e == hipSuccess; ++r) {
@@ -685,12 +740,31 @@ hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t st
         if (p.ksplit == 1)
             continue;
         const int i = order[r];
-        const int64_t n4 = (int64_t)tiles[i] * (BigCfg::TN * BigCfg::TM / 4);
-        hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, BigCfg>), dim3((unsigned)((n4 + 255) / 256)),
-                           dim3(256), 0, stream, p.partial, p.scale, p.y, p.M, p.N, p.ksplit);
+        const int64_t n4 = (int64_t)tiles[i] * (C::TN * C::TM / 4);
+        hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, GROUPED, C>),
+                           dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p.partial,
+                           p.scale, p.y, p.M, p.N, p.ksplit);
         e = hipGetLastError();
     }
     return e;
+}
+
+template <bool FP16>
+hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
+{
+    int idx[2][kGemvMaxBatch], n[2] = {0, 0};
+    for (int i = 0; i < count; ++i) {
+        const int m = args[i].grouped ? 1 : 0;
+        idx[m][n[m]++] = i;
+    }
+    if (n[0]) {
+        const hipError_t e = launch_big_mode<FP16, false, BigCfg>(args, idx[0], n[0], stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (n[1])
+        return launch_big_mode<FP16, true, BigCfgG>(args, idx[1], n[1], stream);
+    return hipSuccess;
 }
 
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
@@ -702,8 +776,8 @@ hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStre
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
 {
-    if (gemm_big_takes(M, N, K, grouped)) {
-        const GemvArgs a = {x, packed, scale, y, M, N, K, false};
+    if (gemm_big_takes(M, N, K, grouped, scale)) {
+        const GemvArgs a = {x, packed, scale, y, M, N, K, grouped};
         return launch_gemm_batch(&a, 1, fp16, stream);
     }
     if (fp16)

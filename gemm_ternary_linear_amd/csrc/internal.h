@@ -41,10 +41,11 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
                               bool grouped, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
-// Whether the pipelined (grouped) prefill kernel takes a shape.
-bool gemm_big_takes(int M, int N, int K, bool grouped);
+// Whether the pipelined (grouped) prefill kernel takes a problem.
+bool gemm_big_takes(int M, int N, int K, bool grouped, const void *scale);
 // Up to kGemvMaxBatch prefill problems (all gemm_big_takes()) in one grouped
-// launch (plus one reduce launch per problem whose K range is split).
+// launch per scale mode (plus one reduce launch per problem whose K range is
+// split).
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream);
 
 // Library-owned scratch of at least `bytes` for work on `stream` of the

@@ -275,7 +275,7 @@ def test_linear_gemm_large_tiles(tl, M, N, K, dtype):
 
 
 # Prefill shapes with too few 256x128 tiles for the CUs: the K range is split
-# over several workgroups (8, 2 and 16 slices here) that store fp32 partial
+# over several workgroups (8, 4 and 16 slices here) that store fp32 partial
 # tiles, and a second kernel adds them in slice order.  Ragged tiles, tile
 # counts that do and do not split over the 8 XCDs, both dtypes; every call is
 # repeated (once on another stream, with its own workspace) to check that the
@@ -302,6 +302,40 @@ def test_linear_gemm_split_k(tl, M, N, K, dtype):
     b1, b2, b3 = (bits_of(t) for t in (y1, y2, y3))
     assert np.array_equal(b1, b2) and np.array_equal(b1, b3), "split-K result not repeatable"
     check_within(widen(b1, dtype), y_ref, bound, f"split-K M={M} N={N} K={K} {dtype}")
+
+
+# Group-128 prefill shapes on the pipelined kernel (K % 256 == 0): the group
+# sums fold with the two scales of each 4-step round.  Ragged tiles, config 1
+# at M=64, config 4's down shape at M=16 (K split over many slices), a split
+# small problem, both dtypes.  A scale array that is only 2-byte aligned runs
+# the 128x128 kernel instead and must give the same bound.
+GROUPED_BIG = [(300, 1100, 768), (64, 3072, 1024), (256, 300, 2048), (16, 5120, 25600),
+               (130, 257, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K", GROUPED_BIG)
+def test_linear_gemm_grouped_pipelined(tl, M, N, K, dtype):
+    import torch
+    say(f"linear grouped pipelined gemm M={M} N={N} K={K} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr(("gbig", M, N, K, dtype)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, 128, dtype)
+    y_ref, bound = oracle.linear(x, packed, scale, 128, dtype=dtype)
+    xd, pd = to_dev(x, _tdt(dtype)), to_dev(packed, None)
+    sd = to_dev(scale, torch.float16)
+    y1 = tl.linear(xd, pd, sd, 128, path="gemm")
+    y2 = tl.linear(xd, pd, sd, 128, path="gemm")
+    # the same scales at an address that is 2 (mod 4) bytes aligned
+    buf = torch.empty(scale.size + 1, dtype=torch.float16, device="cuda:0")
+    buf[1:] = sd.reshape(-1)
+    sd_odd = buf[1:].view(sd.shape)
+    y3 = tl.linear(xd, pd, sd_odd, 128, path="gemm")
+    torch.cuda.synchronize()
+    b1, b2 = bits_of(y1), bits_of(y2)
+    assert np.array_equal(b1, b2), "not repeatable"
+    check_within(widen(b1, dtype), y_ref, bound, f"grouped M={M} N={N} K={K} {dtype}")
+    check_within(widen(bits_of(y3), dtype), y_ref, bound,
+                 f"grouped (2-byte aligned scales) M={M} N={N} K={K} {dtype}")
 
 
 # Shapes large enough that the streaming kernel keeps several channel blocks
