@@ -334,18 +334,20 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     const int M = P.M, N = P.N, K = P.K, ksplit = P.ksplit;
 
     // Tile order: workgroup b runs on XCD b % 8.  Without a K split, when the
-    // token tiles split evenly over the 8 XCDs, XCD k takes token tiles k,
-    // k+8, ... and walks every channel tile of each, so its L2 keeps that
-    // token tile's x.  With a K split of `ksplit` slices, the slices of one
-    // tile go to one XCD when the tiles split evenly over the XCDs.
+    // token tiles split evenly over the 8 XCDs, XCD k owns token tiles k,
+    // k+8, ... (their x stays in its L2) and walks the channel tiles, running
+    // all its token tiles of one channel tile back to back so that each
+    // weight tile is read once per XCD.  With a K split of `ksplit` slices,
+    // the slices of one tile go to one XCD when the tiles split evenly over
+    // the XCDs.
     const int ntn = (N + C::TN - 1) / C::TN, ntm = (M + C::TM - 1) / C::TM;
     int tn, tm, tile = 0, slice = 0;
     const int bid = (int)blockIdx.x - batch.wg0[pi];
     if (ksplit == 1) {
         if (ntm % 8 == 0) {
-            const int xcd = bid & 7, slot = bid >> 3;
-            tm = xcd + 8 * (slot / ntn);
-            tn = slot % ntn;
+            const int xcd = bid & 7, slot = bid >> 3, own = ntm >> 3;
+            tm = xcd + 8 * (slot % own);
+            tn = slot / own;
         } else {
             tm = bid / ntn;
             tn = bid % ntn;

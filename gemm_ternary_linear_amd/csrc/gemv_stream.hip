@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxS = 6;             // slabs per wave (all its loads in flight at once)
+constexpr int kMaxS = 8;             // slabs per wave (all its loads in flight at once)
 // Preferred slabs per wave: 4 (measured best for launches that fill the chip
 // several times over), 2 when that leaves fewer than kFewUnits workgroups.
 constexpr int kTargetS = 4;
@@ -235,9 +235,20 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
     return acc;
 }
 
-template <bool FP16, bool GROUPED, int MT>
+// Parts of up to kMaxS slabs; the kernel for parts of at most kShortS slabs
+// (every problem with K <= kShortS * 16 * 256) is a separate instance, because
+// the longer parts' loads need more registers than 8 waves per SIMD allow.
+constexpr int kShortS = 6;
+
+template <bool FP16, bool GROUPED, int MT, bool LONG>
 __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int S)
 {
+    if constexpr (LONG) {
+        if (S == 7)
+            return run_part<FP16, GROUPED, MT, 7>(c);
+        if (S == 8)
+            return run_part<FP16, GROUPED, MT, 8>(c);
+    }
     switch (S) {
     case 1: return run_part<FP16, GROUPED, MT, 1>(c);
     case 2: return run_part<FP16, GROUPED, MT, 2>(c);
@@ -248,9 +259,10 @@ __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int S)
     default: return f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
-static_assert(kMaxS == 6, "run_part_n covers S = 1..kMaxS");
+static_assert(kMaxS == 8 && kShortS == 6, "run_part_n covers S = 1..kMaxS");
 
-template <bool FP16, bool GROUPED, int MT>
+template <bool FP16, bool GROUPED, int MT, bool LONG>
+
 __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch batch)
 {
     // LDS: per wave [2][M*256] x buffers + [2*kMaxS][16] group scales; the
@@ -314,7 +326,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (S > 0)
-        acc = run_part_n<FP16, GROUPED, MT>(c, S);
+        acc = run_part_n<FP16, GROUPED, MT, LONG>(c, S);
 
     // ---- K-part reduction (fixed order) and epilogue ------------------------
     f32x4_t sum = acc;
@@ -380,12 +392,23 @@ bool gemv_stream_takes(int64_t M, int64_t K, bool grouped)
 
 namespace {
 template <bool FP16, bool GROUPED>
-void launch_m(int mt, dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
+void launch_m(int mt, bool long_parts, dim3 grid, dim3 block, hipStream_t stream,
+              const StreamBatch &b)
 {
-    if (mt == 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1>), grid, block, kLdsBytes, stream, b);
-    else
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2>), grid, block, kLdsBytes, stream, b);
+    if (long_parts) {
+        if (mt == 1)
+            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1, true>), grid, block, kLdsBytes,
+                               stream, b);
+        else
+            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2, true>), grid, block, kLdsBytes,
+                               stream, b);
+    } else if (mt == 1) {
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1, false>), grid, block, kLdsBytes,
+                           stream, b);
+    } else {
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2, false>), grid, block, kLdsBytes,
+                           stream, b);
+    }
 }
 }  // namespace
 
@@ -435,17 +458,20 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
     }
     if (b.count == 0)
         return hipSuccess;
+    bool long_parts = false;
+    for (int i = 0; i < b.count; ++i)
+        long_parts = long_parts || b.p[i].spart > kShortS;
     const dim3 grid(units), block(kThreads);
     if (fp16) {
         if (grouped)
-            launch_m<true, true>(mt, grid, block, stream, b);
+            launch_m<true, true>(mt, long_parts, grid, block, stream, b);
         else
-            launch_m<true, false>(mt, grid, block, stream, b);
+            launch_m<true, false>(mt, long_parts, grid, block, stream, b);
     } else {
         if (grouped)
-            launch_m<false, true>(mt, grid, block, stream, b);
+            launch_m<false, true>(mt, long_parts, grid, block, stream, b);
         else
-            launch_m<false, false>(mt, grid, block, stream, b);
+            launch_m<false, false>(mt, long_parts, grid, block, stream, b);
     }
     return hipGetLastError();
 }
