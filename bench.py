@@ -24,7 +24,8 @@ Printed (one JSON line on stdout):
                seven separate calls per step and per-projection launches beside;
   configs      every other (config, shape, M) of the five workloads: per-launch time on
                the automatic path as GB/s and TFLOP/s with both roofline fractions;
-  crossover    config 4 at each M: forced GEMV and GEMM launch times (GEMV -> GEMM);
+  crossover    forced GEMV and GEMM launch times for every swept case the GEMV takes,
+               and for config 4 at each M (where the GEMV -> GEMM crossover lies);
   pack         ternary_pack / ternary_unpack throughput on the 18944 x 4096 weight;
   cpu_baseline the CPU oracle (fp64, OpenMP) on the full decode layer at
                M = 1 on this host's cores, same algorithmic bytes.
@@ -450,8 +451,9 @@ def bench_pack(tl):
 def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
     """Every (config, shape, M) of the five workloads that the headline lines do
     not already time: per-launch time on the automatic path, as GB/s and
-    TFLOP/s with both roofline fractions; for config 4 also the forced GEMV and
-    GEMM paths at each M the GEMV takes, to place the GEMV -> GEMM crossover.
+    TFLOP/s with both roofline fractions; for every case the GEMV takes, and
+    for config 4 at each M, also the forced GEMV and GEMM paths, to place the
+    GEMV -> GEMM crossover.
 
     Timing: the weights of the shape's first case (drawn as for that case; x
     per M from the M's own generator) are copied R times into one allocation,
@@ -524,11 +526,11 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
                                "TFLOPs": round(f / t / 1e12, 2),
                                "mfma_frac": round(f / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                "copies": R}
-                if ci == 4:
+                if ci == 4 or M <= tl.gemv_max_m():
                     c = {"gemm_us": round(run("gemm") * 1e6, 3)}
                     if M <= tl.gemv_max_m():
                         c["gemv_us"] = round(run("gemv") * 1e6, 3)
-                    cross.setdefault(shp.name, {})[str(M)] = c
+                    cross.setdefault(f"{ci}:{shp.name}", {})[str(M)] = c
                 del x, y
             out[str(ci)][shp.name] = res
             del P, S

@@ -16,7 +16,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
     # packed fp32 VALU forms stay off: all fp32 math is emitted as scalar ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

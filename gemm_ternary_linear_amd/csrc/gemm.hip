@@ -15,6 +15,7 @@
 // global loads of step k+1 are in flight while step k runs on the matrix cores.
 // Rows are padded to 72 elements (144 bytes) so the 16 rows a fragment read
 // touches fall on distinct LDS banks.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -224,7 +225,7 @@ struct Cfg {
     static constexpr int XSTAGE = TM * 8;        // 16-byte chunks per x stage
     static constexpr int WSTAGE = TN * 4;        // dwords per packed stage
     static_assert(TM * 8 % THREADS == 0 && TN * 4 % THREADS == 0, "stage split");
-    static_assert(FN >= 1 && FM >= 1 && NS >= 2 && NS <= 4, "tile");
+    static_assert(FN >= 1 && FM >= 1 && NS >= 2 && NS <= 8, "tile");
     static_assert((NS - 2) * VPS <= 63, "vmcnt range");
 };
 
@@ -298,21 +299,26 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
     // Group-128 scales: every stage also carries one dword per channel, the
-    // scales of the two groups of the 4-step round it belongs to.
-    static_assert(!GROUPED || (C::TN == THREADS && NS == 4), "one scale dword per thread");
+    // scales of the two groups of the 4 steps (256 K) it belongs to.
+    static_assert(!GROUPED || (C::TN == THREADS && NS % 4 == 0), "one scale dword per thread");
     constexpr int VPS = C::VPS + (GROUPED ? 1 : 0);  // vector memory ops per thread and stage
     // One LDS object per stage: the compiler then knows that a DMA into one
     // stage does not write the stage being read and waits for nothing there.
-    __shared__ __attribute__((aligned(16))) uint4 sx0[C::XSTAGE], sx1[C::XSTAGE],
-        sx2[NS > 2 ? C::XSTAGE : 1], sx3[NS > 3 ? C::XSTAGE : 1];
-    __shared__ __attribute__((aligned(16))) uint32_t sw0[C::WSTAGE], sw1[C::WSTAGE],
-        sw2[NS > 2 ? C::WSTAGE : 1], sw3[NS > 3 ? C::WSTAGE : 1];
-    lds_u4 *const lx[4] = {(lds_u4 *)sx0, (lds_u4 *)sx1, (lds_u4 *)sx2, (lds_u4 *)sx3};
-    lds_u32 *const lw[4] = {(lds_u32 *)sw0, (lds_u32 *)sw1, (lds_u32 *)sw2, (lds_u32 *)sw3};
-    constexpr int SSTAGE = GROUPED ? C::TN : 1;
-    __shared__ __attribute__((aligned(16))) uint32_t sc0[SSTAGE], sc1[SSTAGE], sc2[SSTAGE],
-        sc3[SSTAGE];
-    lds_u32 *const lsc[4] = {(lds_u32 *)sc0, (lds_u32 *)sc1, (lds_u32 *)sc2, (lds_u32 *)sc3};
+    constexpr int XS = C::XSTAGE, WS = C::WSTAGE, SS = GROUPED ? C::TN : 1;
+#define TERNARY_STAGES(T, name, n)                                                               \
+    __shared__ __attribute__((aligned(16))) T name##0[n], name##1[n], name##2[NS > 2 ? n : 1],  \
+        name##3[NS > 3 ? n : 1], name##4[NS > 4 ? n : 1], name##5[NS > 5 ? n : 1],            \
+        name##6[NS > 6 ? n : 1], name##7[NS > 7 ? n : 1]
+    TERNARY_STAGES(uint4, sx, XS);
+    TERNARY_STAGES(uint32_t, sw, WS);
+    TERNARY_STAGES(uint32_t, sc, SS);
+#undef TERNARY_STAGES
+    lds_u4 *const lx[8] = {(lds_u4 *)sx0, (lds_u4 *)sx1, (lds_u4 *)sx2, (lds_u4 *)sx3,
+                           (lds_u4 *)sx4, (lds_u4 *)sx5, (lds_u4 *)sx6, (lds_u4 *)sx7};
+    lds_u32 *const lw[8] = {(lds_u32 *)sw0, (lds_u32 *)sw1, (lds_u32 *)sw2, (lds_u32 *)sw3,
+                            (lds_u32 *)sw4, (lds_u32 *)sw5, (lds_u32 *)sw6, (lds_u32 *)sw7};
+    lds_u32 *const lsc[8] = {(lds_u32 *)sc0, (lds_u32 *)sc1, (lds_u32 *)sc2, (lds_u32 *)sc3,
+                             (lds_u32 *)sc4, (lds_u32 *)sc5, (lds_u32 *)sc6, (lds_u32 *)sc7};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -366,8 +372,13 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     }
     const int n0 = tn * C::TN;
     const int m0 = tm * C::TM;
-    const int nk = K / TK / ksplit;  // K steps of this workgroup's slice
-    const int kbase = slice * nk;
+    // This slice's K steps: rounds [r0, r1) of NS steps (slices differ by at
+    // most one round).
+    const int rounds = K / (TK * NS);
+    const int r0 = (int)((int64_t)slice * rounds / ksplit);
+    const int r1 = (int)((int64_t)(slice + 1) * rounds / ksplit);
+    const int nk = (r1 - r0) * NS;
+    const int kbase = r0 * NS;
 
     // DMA sources.  x DMA i of this thread fills physical chunk p = i*THREADS
     // + tid of the stage (lanes of a wave write consecutive chunks).
@@ -469,7 +480,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
                         lsc[s] + wn * FN * 16 + f * 16 + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sc = f16_bits_to_f32((uint16_t)(s == 1 ? w[r] : w[r] >> 16));
+                        const float sc =
+                            f16_bits_to_f32((uint16_t)(((s >> 1) & 1) == 0 ? w[r] : w[r] >> 16));
 #pragma unroll
                         for (int j = 0; j < FM; ++j)
                             acc[f][j][r] += sc * part[f][j][r];
@@ -490,21 +502,16 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     };
 
     // Prologue: stages 0 .. NS-2.
-    issue(std::integral_constant<int, 0>{}, 0);
-    if constexpr (NS > 2)
-        issue(std::integral_constant<int, 1>{}, 1);
-    if constexpr (NS > 3)
-        issue(std::integral_constant<int, 2>{}, 2);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        (issue(std::integral_constant<int, I>{}, I), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
 
     // K is a whole number of NS-step rounds (the host checks), so every
     // stage index below is a constant.
     for (int kt = 0; kt < nk; kt += NS) {
-        step(std::integral_constant<int, 0>{}, kt);
-        step(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (NS > 2)
-            step(std::integral_constant<int, 2>{}, kt + 2);
-        if constexpr (NS > 3)
-            step(std::integral_constant<int, 3>{}, kt + 3);
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (step(std::integral_constant<int, I>{}, kt + I), ...);
+        }(std::make_integer_sequence<int, NS>{});
     }
     // No DMA may still be writing LDS when the workgroup ends.
     wait_vm<0>();
@@ -617,8 +624,22 @@ hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *
 // Tile shape, wave grid, stage count and waves per SIMD of the pipelined
 // kernel: per-channel problems run two workgroups per CU; group-scaled ones
 // keep a second set of accumulators (the current group's sums) and run one.
-typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;
-typedef dma::Cfg<256, 128, 4, 1, 4, 1> BigCfgG;
+typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;  // per-channel, M > 64
+// Few tokens: the MFMAs are not the limit, the weight stream is, so the
+// tiles take fewer tokens and (M <= 32) the pipeline runs 8 stages deep to
+// keep more weight bytes in flight per CU.  Group-scaled problems, which keep
+// a second set of accumulators, use these at every M so that they still run
+// two workgroups per CU.
+typedef dma::Cfg<256, 64, 4, 1, 4, 2> MidCfg;   // 32 < M <= 64 (or K % 512 != 0)
+typedef dma::Cfg<256, 32, 4, 1, 8, 2> SmallCfg; // M <= 32, K % 512 == 0
+
+// Which configuration a problem runs with: 0 small, 1 mid, 2 large.
+int big_cfg_of(int M, int K, bool grouped)
+{
+    if (M <= 32 && K % (dma::TK * SmallCfg::NS) == 0)
+        return 0;
+    return M <= 64 || grouped ? 1 : 2;
+}
 
 // The pipelined kernel takes problems whose K is a whole number of 4-step
 // rounds (256), whose buffer offsets stay below the out-of-range marker, and
@@ -648,26 +669,20 @@ int device_cus()
     return cus[dev];
 }
 
-// K slices of the pipelined kernel: the smallest divisor of the problem's
-// number of 4-step rounds that lets tiles x slices cover the compute units,
-// keeping at least two rounds per slice (else the largest divisor that
-// does), within a 2 GiB workspace.
-int big_ksplit(int tiles, int K)
+// K slices of the pipelined kernel (whole rounds of NS steps each, at most
+// one round apart): enough that tiles x slices cover the compute units once
+// (more slices would add partial-tile traffic), keeping at least two rounds
+// per slice, within a 2 GiB workspace.
+int big_ksplit(int tiles, int K, int ns, int tile_elems)
 {
-    const int rounds = K / (dma::TK * BigCfg::NS), cus = device_cus();
+    const int rounds = K / (dma::TK * ns), cus = device_cus();
     if ((int64_t)tiles >= cus)
         return 1;
-    const int64_t want = (cus + tiles - 1) / tiles;
-    int best = 1;
-    for (int d = 2; d <= rounds / 2; ++d) {
-        if (rounds % d != 0 ||
-            (int64_t)tiles * d * BigCfg::TN * BigCfg::TM * 4 > (int64_t(1) << 31))
-            continue;
-        best = d;
-        if (d >= want)
-            break;
-    }
-    return best;
+    int ks = (cus + tiles - 1) / tiles;
+    ks = std::min(ks, rounds / 2);
+    while (ks > 1 && (int64_t)tiles * ks * tile_elems * 4 > (int64_t(1) << 31))
+        --ks;
+    return std::max(ks, 1);
 }
 
 // Launches the problems args[idx[0..count)) (all gemm_big_takes(), one scale
@@ -695,7 +710,9 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
         }
     size_t ws_bytes = 0;
     for (int i = 0; i < count; ++i) {
-        ks[i] = total < device_cus() ? big_ksplit(tiles[i], args[idx[i]].K) : 1;
+        ks[i] = total < device_cus()
+                    ? big_ksplit(tiles[i], args[idx[i]].K, C::NS, C::TN * C::TM)
+                    : 1;
         if (ks[i] > 1)
             ws_bytes += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
     }
@@ -754,19 +771,25 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
 template <bool FP16>
 hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
 {
-    int idx[2][kGemvMaxBatch], n[2] = {0, 0};
+    // one launch per (scale mode, configuration) present
+    int idx[6][kGemvMaxBatch], n[6] = {};
+    static_assert(kGemvMaxBatch <= 8, "batch table");
     for (int i = 0; i < count; ++i) {
-        const int m = args[i].grouped ? 1 : 0;
+        const int m = (args[i].grouped ? 3 : 0) + big_cfg_of(args[i].M, args[i].K, args[i].grouped);
         idx[m][n[m]++] = i;
     }
-    if (n[0]) {
-        const hipError_t e = launch_big_mode<FP16, false, BigCfg>(args, idx[0], n[0], stream);
-        if (e != hipSuccess)
-            return e;
-    }
-    if (n[1])
-        return launch_big_mode<FP16, true, BigCfgG>(args, idx[1], n[1], stream);
-    return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (n[0] && e == hipSuccess)
+        e = launch_big_mode<FP16, false, SmallCfg>(args, idx[0], n[0], stream);
+    if (n[1] && e == hipSuccess)
+        e = launch_big_mode<FP16, false, MidCfg>(args, idx[1], n[1], stream);
+    if (n[2] && e == hipSuccess)
+        e = launch_big_mode<FP16, false, BigCfg>(args, idx[2], n[2], stream);
+    if (n[3] && e == hipSuccess)
+        e = launch_big_mode<FP16, true, SmallCfg>(args, idx[3], n[3], stream);
+    if (n[4] && e == hipSuccess)
+        e = launch_big_mode<FP16, true, MidCfg>(args, idx[4], n[4], stream);
+    return e;  // (group-scaled problems never take the large configuration)
 }
 
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)

@@ -338,6 +338,23 @@ def test_linear_gemm_grouped_pipelined(tl, M, N, K, dtype):
                  f"grouped (2-byte aligned scales) M={M} N={N} K={K} {dtype}")
 
 
+# Few-token prefill shapes on the pipelined kernel: 32-token tiles 8 stages
+# deep (M <= 32, K % 512 == 0) and 64-token tiles (32 < M <= 64, or K % 512
+# != 0), both scale modes, ragged tiles; the GEMM path forced at M = 1 and 8.
+SMALLM = [(9, 300, 2048, -1), (32, 1100, 1024, -1), (48, 520, 768, -1), (1, 700, 4096, -1),
+          (8, 700, 5120, 128), (33, 200, 1536, 128), (20, 260, 768, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", SMALLM)
+def test_linear_gemm_few_tokens(tl, M, N, K, g):
+    say(f"linear few-token gemm M={M} N={N} K={K} g={g}")
+    rng = np.random.default_rng(zlib.crc32(repr(("fewtok", M, N, K, g)).encode()))
+    codes, packed, scale, x = _case(rng, M, N, K, g, "bf16")
+    y_ref, bound = oracle.linear(x, packed, scale, g, dtype="bf16")
+    y = _run(tl, x, packed, scale, g, "bf16", path="gemm")
+    check_within(y, y_ref, bound, f"few-token gemm M={M} N={N} K={K} g={g}")
+
+
 # Shapes large enough that the streaming kernel keeps several channel blocks
 # per workgroup: the per-channel cases run the full ring of 20 slabs in every
 # wave, the group-scaled one needs more workgroups than CUs.  Raw random bytes
