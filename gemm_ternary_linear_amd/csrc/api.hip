@@ -57,7 +57,7 @@ int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, cons
 
 int select_path(int64_t M, int64_t K)
 {
-    if (ternary::gemv_takes(M, K))
+    if (ternary::gemv_preferred(M, K))
         return TERNARY_PATH_GEMV;
     if (ternary::gemm_takes(M, K))
         return TERNARY_PATH_GEMM;
@@ -222,7 +222,7 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
         const ternary::GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
                                      static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
                                      p.group_size == 128};
-        if (ternary::gemv_takes(p.M, p.K)) {
+        if (ternary::gemv_preferred(p.M, p.K)) {
             fused[nf++] = a;
         } else if (ternary::gemm_takes(p.M, p.K) &&
                    ternary::gemm_big_takes(a.M, a.N, a.K, a.grouped, a.scale)) {

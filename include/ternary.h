@@ -117,7 +117,8 @@ int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipSt
  * each group's (or the row's) fp32 partial sum; y is rounded from fp32 to the
  * output dtype, round-to-nearest-even.  x and s must be finite (results for
  * non-finite inputs are unspecified) and |x| < 2^126.
- * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV, larger M the
+ * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (except M >= 4
+ * with K >= 16384, K % 256 == 0, which runs faster on the GEMM), larger M the
  * MFMA GEMM; shapes neither fast kernel takes (K % 128 != 0) run the plain
  * kernel.  Results of different paths agree within the bound
  * |y - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6, not bitwise.
@@ -156,8 +157,8 @@ typedef struct {
  *   dtype     activation/output dtype shared by all problems.
  * Every problem is validated as by ternary_linear; in addition no output may
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
- * any error nothing is launched.  Problems the decode GEMV takes (1 <= M <=
- * ternary_gemv_max_m(), K % 128 == 0) run together in one launch per scale
+ * any error nothing is launched.  Problems the automatic path sends to the
+ * decode GEMV (see ternary_linear) run together in one launch per scale
  * mode (per-channel, group-128) and kernel class (M <= 2, larger M);
  * per-channel prefill problems with M >= 256, N >= 256 and K % 256 == 0 run
  * together in one grouped GEMM launch (longest K first); the others run as

@@ -126,6 +126,9 @@ def test_pack_unpack_reject(tl):
 @pytest.mark.parametrize("M,K,g,path", [
     (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "gemm"),
     (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
+    # long K from M = 4: the GEMM is faster (measured crossover)
+    (8, 18944, -1, "gemm"), (4, 25600, 128, "gemm"), (3, 18944, -1, "gemv"),
+    (8, 16256, 128, "gemv"),
     (0, 128, 128, "gemv"),
 ])
 def test_select_path(tl, M, K, g, path):
