@@ -287,8 +287,16 @@ size_t plan(GemvProblem &p)
 {
     const int nslabs = (p.K + 255) / 256;
     int kp = nslabs >= 32 ? 4 : (nslabs >= 8 ? 2 : 1);
-    if (p.M >= 3 && kp > 1)
-        kp = p.M >= 5 ? 1 : 2;
+    if (p.M >= 3) {
+        // From M = 3 the x a workgroup stages grows to a multiple of its
+        // weights: share it over more channel blocks when there are blocks to
+        // spare (2 for M <= 4, 4 beyond), but keep one block per workgroup
+        // when fewer than 512 blocks would otherwise leave CUs idle
+        // (measured on the 7B and 0.6B shapes at M = 8).
+        const int nblocks = (p.N + 15) / 16;
+        const int rb = nblocks >= 1024 ? (p.M >= 5 ? 4 : 2) : (nblocks >= 512 ? 2 : 1);
+        kp = nslabs >= 8 ? 4 / rb : 1;
+    }
     p.rb = 4 / kp;
     int kc = ((nslabs + 3) / 4) * 1024;  // whole K, padded to a multiple of 1024
     if ((size_t)p.M * kc * 2 > (size_t)kXLdsBytes) {
