@@ -48,11 +48,6 @@ namespace {
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxS = 8;             // slabs per wave (all its loads in flight at once)
-// Preferred slabs per wave: 4 (measured best for launches that fill the chip
-// several times over), 2 when that leaves fewer than kFewUnits workgroups.
-constexpr int kTargetS = 4;
-constexpr int kTargetSmall = 2;
-constexpr int kFewUnits = 512;
 constexpr int kOOB = 0x40000000;     // buffer offset past every resource: reads zero
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 
@@ -387,7 +382,7 @@ bool gemv_stream_takes(int64_t M, int64_t K, bool grouped)
 {
     (void)grouped;
     int kp = 0, spart = 0;
-    return K % 128 == 0 && K <= kGemvMaxK && split_k((int)M, (int)K, kTargetSmall, kp, spart);
+    return K % 128 == 0 && K <= kGemvMaxK && split_k((int)M, (int)K, 2, kp, spart);
 }
 
 namespace {
@@ -412,18 +407,55 @@ void launch_m(int mt, bool long_parts, dim3 grid, dim3 block, hipStream_t stream
 }
 }  // namespace
 
+namespace {
+
+// Workgroups of one kernel instance that fit on a CU (cached).
+int stream_slots_per_cu(int mt, bool long_parts, bool grouped)
+{
+    static int cache[2][2][2] = {};
+    int &v = cache[mt - 1][long_parts][grouped];
+    if (v == 0) {
+        const void *k = nullptr;
+        if (grouped)
+            k = long_parts ? (mt == 1 ? (const void *)gemv_stream_kernel<false, true, 1, true>
+                                      : (const void *)gemv_stream_kernel<false, true, 2, true>)
+                           : (mt == 1 ? (const void *)gemv_stream_kernel<false, true, 1, false>
+                                      : (const void *)gemv_stream_kernel<false, true, 2, false>);
+        else
+            k = long_parts ? (mt == 1 ? (const void *)gemv_stream_kernel<false, false, 1, true>
+                                      : (const void *)gemv_stream_kernel<false, false, 2, true>)
+                           : (mt == 1 ? (const void *)gemv_stream_kernel<false, false, 1, false>
+                                      : (const void *)gemv_stream_kernel<false, false, 2, false>);
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, kLdsBytes) != hipSuccess ||
+            n < 1)
+            n = 1;
+        v = n;
+    }
+    return v;
+}
+
+}  // namespace
+
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
                               bool grouped, hipStream_t stream)
 {
-    // The plan with parts of kTargetS slabs, or of kTargetSmall when that
-    // yields few workgroups (a function of the whole batch, so deterministic).
+    // The part length (slabs per wave) of the whole batch, a function of the
+    // batch only (so deterministic): 4 slabs, or 2 when 4 leaves fewer than
+    // 512 workgroups (both measured best on MI355X); and when the workgroups
+    // exceed the resident slots by less than a quarter of a round, the
+    // shortest longer part (up to kShortS slabs) that removes that round
+    // while still filling three quarters of the remaining rounds' slots,
+    // since the few left-over workgroups would cost a round of their own
+    // (27B up at M=1: 534 workgroups at 4 slabs, 14.5 us; 400 at 5, 12.8 us;
+    // 7B gate: 592 at 2 slabs, 9.5 us, beats 296 at 4, 9.9 us).
     StreamBatch b;
-    int units = 0, mt = 0;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        const int target = attempt == 0 ? kTargetS : kTargetSmall;
+    int units = 0, mt = 0, max_spart = 0;
+    auto build = [&](int target) -> bool {
         b.count = 0;
         units = 0;
         mt = 0;
+        max_spart = 0;
         for (int oi = 0; oi < count; ++oi) {
             const GemvArgs &a = args[order[oi]];
             if (a.M == 0 || a.N == 0)
@@ -431,7 +463,7 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             StreamProblem &p = b.p[b.count];
             if (a.grouped != grouped || (mt != 0 && a.M != mt) ||
                 !split_k(a.M, a.K, target, p.kp, p.spart))
-                return hipErrorInvalidValue;
+                return false;
             mt = a.M;
             p.x = a.x;
             p.packed = a.packed;
@@ -451,10 +483,31 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             p.unit0 = units;
             b.unit0[b.count] = units;
             units += (nblocks + p.rb - 1) / p.rb;
+            max_spart = std::max(max_spart, p.spart);
             ++b.count;
         }
-        if (units >= kFewUnits)
-            break;
+        return true;
+    };
+    int base_target = 4;
+    if (!build(base_target))
+        return hipErrorInvalidValue;
+    if (units < 512) {
+        base_target = 2;
+        if (!build(base_target))
+            return hipErrorInvalidValue;
+    }
+    if (b.count > 0 && max_spart <= kShortS) {
+        const int slots = device_cus() * stream_slots_per_cu(mt, false, grouped);
+        const int rounds = (units + slots - 1) / slots;
+        if (rounds > 1 && units - (rounds - 1) * slots < slots / 4) {
+            int pick = 0;
+            for (int t = base_target + 1; t <= kShortS && !pick; ++t)
+                if (build(t) && max_spart <= kShortS &&
+                    (units + slots - 1) / slots < rounds && 4 * units >= 3 * (rounds - 1) * slots)
+                    pick = t;
+            if (!build(pick ? pick : base_target))
+                return hipErrorInvalidValue;
+        }
     }
     if (b.count == 0)
         return hipSuccess;

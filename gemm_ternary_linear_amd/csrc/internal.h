@@ -39,6 +39,8 @@ bool gemv_stream_takes(int64_t M, int64_t K, bool grouped);
 // one M) in one launch of the streaming decode kernel.
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
                               bool grouped, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cus();
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
 // Whether the pipelined (grouped) prefill kernel takes a problem.
