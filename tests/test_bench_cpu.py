@@ -1,0 +1,96 @@
+"""Host logic of bench.py on the CPU: the rocprofv3 counter and trace digests.
+
+Synthetic counter files stand in for two --pmc runs: a copy probe of known
+size fixes each counter's scale, and the digest must report, for the largest
+dispatch of each kernel family, the scaled bytes per launch; a kernel-trace
+digest must group dispatches by launch shape.
+"""
+
+import csv
+
+import pytest
+
+import bench
+
+COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+        "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+        "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+        "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write_counters(d, name, rows):
+    d.mkdir(parents=True)
+    with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        for i, (kernel, grid, values) in enumerate(rows):
+            for v in values:  # one row per counter instance, summed by the digest
+                w.writerow({c: 0 for c in COLS} | {
+                    "Dispatch_Id": i + 1, "Kernel_Name": kernel, "Grid_Size": grid,
+                    "Counter_Name": name, "Counter_Value": v})
+
+
+def test_summarize_pmc_scales_by_copy_probe(tmp_path, monkeypatch):
+    probe_kib = bench.COPY_PROBE_BYTES / 1024
+    fam = {k: (tmp_path / f"{k}.txt", sub, what) for k, (_, sub, what) in bench.COUNTERS.items()}
+    monkeypatch.setattr(bench, "COUNTERS", fam)
+    neg = "at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda"
+    gemv = "ternary::gemv_stream_kernel<false, false, 1, false>(StreamBatch)"
+    gemm = "ternary::dma::gemm_dma_kernel<false, false, Cfg<256, 128, 4, 1, 4, 2> >(BigBatch)"
+    # FETCH_SIZE reads half the bytes (scale 2), WRITE_SIZE all of them (scale 1)
+    _write_counters(tmp_path / "F", "FETCH_SIZE", [
+        (neg, 1 << 20, [probe_kib / 4, probe_kib / 4]),
+        (gemv, 16384, [10.0]),                 # a smaller launch: ignored
+        (gemv, 1015808, [30000.0, 3000.0]),    # the fused launch, two instances
+        (gemm, 819200, [400000.0]),
+        (gemm, 65536, [9.0])])
+    _write_counters(tmp_path / "W", "WRITE_SIZE", [
+        (neg, 1 << 20, [probe_kib]),
+        (gemv, 1015808, [100.0]),
+        (gemm, 819200, [200000.0])])
+    bench.summarize_pmc(str(tmp_path / "F"), str(tmp_path / "W"))
+    kv = {}
+    for ln in (tmp_path / "decode.txt").read_text().splitlines():
+        if ln and not ln.startswith("#"):
+            k, v = ln.split(None, 1)
+            kv[k] = v
+    assert float(kv["fetch_scale"]) == pytest.approx(2.0)
+    assert float(kv["write_scale"]) == pytest.approx(1.0)
+    assert int(kv["grid_threads"]) == 1015808
+    assert float(kv["traffic_bytes_per_launch"]) == pytest.approx(33000 * 1024 * 2 + 100 * 1024)
+    assert kv["source_hash"] == bench.kernel_source_hash()
+    assert bench.stored_traffic("decode") == pytest.approx(33000 * 1024 * 2 + 100 * 1024)
+    assert bench.stored_traffic("prefill") == pytest.approx(400000 * 1024 * 2 + 200000 * 1024)
+
+
+def test_stored_traffic_is_null_for_other_sources(tmp_path, monkeypatch):
+    p = tmp_path / "c.txt"
+    p.write_text("source_hash 0000000000000000\ntraffic_bytes_per_launch 1.0\n")
+    monkeypatch.setattr(bench, "COUNTERS", {"decode": (p, "gemv", "x")})
+    assert bench.stored_traffic("decode") is None
+
+
+def test_summarize_trace_groups_by_shape(tmp_path, monkeypatch):
+    d = tmp_path / "T"
+    d.mkdir()
+    with open(d / "bench_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        w.writerow(["ternary::gemv_stream_kernel<false, false, 1, false>(x)", 3, 60000, 20000,
+                    100, 19000, 21000, 0])
+    with open(d / "bench_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Workgroup_Size_X",
+                    "Start_Timestamp", "End_Timestamp"])
+        for t0, dt in ((0, 19000), (50000, 21000), (90000, 20000)):
+            w.writerow(["ternary::gemv_stream_kernel<false, false, 1, false>(x)", 1015808, 1,
+                        1024, t0, t0 + dt])
+    out = tmp_path / "trace.txt"
+    monkeypatch.setattr(bench, "TRACE_FILE", out)
+    bench.summarize_trace(str(d))
+    text = out.read_text()
+    assert "grid=1015808 wg=1024" in text
+    line = [ln for ln in text.splitlines() if "grid=1015808" in ln][0]
+    calls, median, mean = line.split()[:3]
+    assert int(calls) == 3 and float(median) == pytest.approx(20.0) and float(mean) == pytest.approx(20.0)

@@ -304,6 +304,31 @@ def test_linear_gemm_split_k(tl, M, N, K, dtype):
     check_within(widen(b1, dtype), y_ref, bound, f"split-K M={M} N={N} K={K} {dtype}")
 
 
+def test_workspace_shutdown_and_regrow(tl):
+    # ternary_shutdown frees the per-stream workspaces after their streams
+    # drain; the next split-K call allocates again, and a larger problem grows
+    # the workspace; every result keeps its bits.
+    import torch
+    say("workspace shutdown / regrow")
+    rng = np.random.default_rng(7)
+    small = _case(rng, 256, 256, 4096, -1, "bf16")
+    large = _case(rng, 512, 1024, 8192, -1, "bf16")
+    dev = [(to_dev(x, torch.bfloat16), to_dev(p, None), to_dev(s, torch.float16))
+           for (_, p, s, x) in (small, large)]
+    first = [bits_of(tl.linear(*d, -1)) for d in dev]
+    tl.shutdown()
+    again_small = bits_of(tl.linear(*dev[0], -1))
+    again_large = bits_of(tl.linear(*dev[1], -1))  # grows the fresh workspace
+    tl.shutdown()
+    tl.shutdown()  # nothing left to free: still fine
+    last = bits_of(tl.linear(*dev[1], -1))
+    torch.cuda.synchronize()
+    assert np.array_equal(first[0], again_small)
+    assert np.array_equal(first[1], again_large) and np.array_equal(first[1], last)
+    y_ref, bound = oracle.linear(small[3], small[1], small[2], -1, dtype="bf16")
+    check_within(widen(first[0], "bf16"), y_ref, bound, "workspace small")
+
+
 # Group-128 prefill shapes on the pipelined kernel (K % 256 == 0): the group
 # sums fold with the two scales of each 4-step round.  Ragged tiles, config 1
 # at M=64, config 4's down shape at M=16 (K split over many slices), a split
