@@ -67,6 +67,7 @@ COUNTERS = {
                 "M=2048)"),
 }
 DECODE_CFG, PREFILL_CFG = 2, 3
+PROBE_ITERS = {512: 8192, 1024: 4096, 2048: 2048}   # MFMA loop probe: workgroups -> iters
 
 
 def log(*a):
@@ -309,6 +310,91 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
         print("\n".join(lines))
 
 
+MFMA_FILE = ROOT / "profiles" / "gemm_dma_7b_prefill_m2048_mfma.txt"
+MFMA_PASSES = (
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+     "SQ_INSTS_VALU_MFMA_MOPS_BF16"),
+    ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_INSTS_VALU"),
+)
+
+
+def summarize_mfma(*dirs) -> None:
+    """Digest the MFMA/LDS counter runs of bench.py for the grouped prefill GEMM
+    launch (largest-grid gemm_dma_kernel dispatch) beside the MFMA loop probe
+    (probe_mfma_kernel, whose matrix cores are busy for its whole duration and
+    whose flop count is known), which calibrates the counters."""
+    vals = {}
+    for d in dirs:
+        for r in read_counter_csv(Path(d)):
+            key = (r["Kernel_Name"], int(r.get("Grid_Size", 0)), r["Dispatch_Id"])
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+            vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no counter_collection.csv under {dirs}")
+
+    def family(sub):
+        keys = [k for k in vals if sub in k[0]]
+        if not keys:
+            raise SystemExit(f"no {sub} dispatch")
+        top = max(k[1] for k in keys)
+        keys = [k for k in keys if k[1] == top]
+        mean = {}
+        for c in {c for k in keys for c in vals[k]}:
+            v = [vals[k][c] for k in keys if c in vals[k]]
+            mean[c] = (sum(v) / len(v), len(v))
+        return top, mean
+
+    g_grid, g = family("gemm_dma_kernel")
+    p_grid, pr = family("probe_mfma_kernel")
+    lines = [
+        "# MFMA and LDS counters of the grouped prefill GEMM launch (all 7 projections of the",
+        "# 7B layer at M=2048, one gemm_dma_kernel dispatch) beside the MFMA loop probe",
+        "# (probe_mfma_kernel: 4 waves per SIMD, four independent bf16 MFMA chains each,",
+        "# no memory traffic), from rocprofv3 --pmc runs of bench.py, one per counter set:",
+    ]
+    for cs in MFMA_PASSES:
+        lines.append(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <D> -o bench -- \\")
+        lines.append("#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
+                     "--prefill-steps 1 --prefill-warmup 2")
+    lines += [
+        "#   python3 bench.py --summarize-mfma <D1> <D2>",
+        "# Values are per dispatch (summed over counter instances), mean over the dispatches",
+        "# of that launch shape.  mfma_busy_per_gui = SQ_VALU_MFMA_BUSY_CYCLES /",
+        "# GRBM_GUI_ACTIVE; mfma_busy_vs_probe divides it by the probe's, i.e. the share of",
+        "# the launch's duration in which the matrix cores are as busy as in the probe.",
+        "# mfma_flops = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 (checked on the probe, whose",
+        "# flops are known).",
+        f"source_hash {kernel_source_hash()}",
+        f"gemm_grid_threads {g_grid}",
+        f"probe_grid_threads {p_grid}",
+    ]
+    for c in sorted(set(g) | set(pr)):
+        gv = g.get(c, (float("nan"), 0))
+        pv = pr.get(c, (float("nan"), 0))
+        lines.append(f"{c:<32} gemm {gv[0]:>18.1f} (n={gv[1]})   probe {pv[0]:>18.1f} (n={pv[1]})")
+
+    def get(m, c):
+        return m[c][0] if c in m else float("nan")
+
+    rg = get(g, "SQ_VALU_MFMA_BUSY_CYCLES") / get(g, "GRBM_GUI_ACTIVE")
+    rp = get(pr, "SQ_VALU_MFMA_BUSY_CYCLES") / get(pr, "GRBM_GUI_ACTIVE")
+    wg = p_grid // 256
+    probe_flops = wg * 4 * 4 * 16384 * PROBE_ITERS.get(wg, 0)
+    lines += [
+        f"gemm_mfma_busy_per_gui {rg:.4f}",
+        f"probe_mfma_busy_per_gui {rp:.4f}",
+        f"gemm_mfma_busy_vs_probe {rg / rp:.4f}",
+        f"gemm_mfma_flops {512 * get(g, 'SQ_INSTS_VALU_MFMA_MOPS_BF16'):.6e}",
+        f"probe_mfma_flops {512 * get(pr, 'SQ_INSTS_VALU_MFMA_MOPS_BF16'):.6e}",
+        f"probe_flops_issued {probe_flops:.6e}",
+        f"gemm_lds_bank_conflict_per_active "
+        f"{get(g, 'SQ_LDS_BANK_CONFLICT') / get(g, 'SQ_LDS_IDX_ACTIVE'):.4f}",
+    ]
+    MFMA_FILE.parent.mkdir(exist_ok=True)
+    MFMA_FILE.write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 TRACE_FILE = ROOT / "profiles" / "kernels_7b_decode_prefill_trace.txt"
 
 
@@ -326,11 +412,11 @@ def summarize_trace(d: str) -> None:
     if not stats or not trace:
         raise SystemExit(f"no kernel_stats/kernel_trace csv under {d}")
     lines = [
-        "# rocprofv3 kernel trace of `python3 bench.py --no-cpu` (7B decode layer at M=1 as",
-        "# one fused ternary_linear_batch launch per step, per-projection launches, and the",
-        "# 7B prefill layer at M=2048), made by:",
+        "# rocprofv3 kernel trace of `python3 bench.py --no-cpu --no-sweep` (7B decode layer",
+        "# at M=1 as one fused ternary_linear_batch launch per step, per-projection launches,",
+        "# the 7B prefill layer at M=2048, and the probe kernels), made by:",
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d <D> -o bench -- \\",
-        "#       python3 bench.py --no-cpu",
+        "#       python3 bench.py --no-cpu --no-sweep",
         "#   python3 bench.py --summarize-trace <D>",
         f"source_hash {kernel_source_hash()}",
         "",
@@ -342,12 +428,12 @@ def summarize_trace(d: str) -> None:
         short = nm.split("(")[0].replace("void ", "")
         lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.3f} "
                      f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f}  {short[:90]}")
-    lines += ["", "## ternary kernels by launch shape (grid threads x workgroup threads)",
+    lines += ["", "## ternary and probe kernels by launch shape (grid threads x workgroup threads)",
               f"{'calls':>6} {'median_us':>10} {'mean_us':>9}  kernel grid"]
     groups = {}
     for r in trace:
         k = r["Kernel_Name"].replace("(anonymous namespace)::", "")
-        if "ternary" not in k:
+        if "ternary" not in k and "probe_" not in k:
             continue
         short = k.split("(")[0].replace("void ", "").replace("ternary::", "")
         key = (short, int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1),
@@ -376,6 +462,21 @@ def stored_traffic(family):
     if kv.get("source_hash") != kernel_source_hash():
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def stored_mfma():
+    """MFMA busy share of the grouped prefill launch (relative to the MFMA loop
+    probe) from the committed counters, if taken on these kernel sources."""
+    if not MFMA_FILE.exists():
+        return None
+    kv = {}
+    for ln in MFMA_FILE.read_text().splitlines():
+        if ln and not ln.startswith("#"):
+            k, v = ln.split(None, 1)
+            kv[k] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash() or "gemm_mfma_busy_vs_probe" not in kv:
+        return None
+    return float(kv["gemm_mfma_busy_vs_probe"])
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -551,6 +652,92 @@ def copy_probe():
     del a, b
 
 
+def measure_ceilings(tl, layer_bytes, steps):
+    """Achievable rates of this device, from the probe kernels of
+    include/ternary_probe.h, each at its best launch size from a short list:
+
+    - read_1GiB: one 16-byte-load streaming read of 1 GiB;
+    - read_layer_size: `steps` reads of `layer_bytes` each (the decode layer's
+      algorithmic bytes), rotating over 1 GiB and replayed from one HIP graph,
+      timed like the decode step;
+    - copy_512MiB: a 512 MiB -> 512 MiB copy (reads plus writes);
+    - mfma_loop: four independent bf16 MFMA chains per wave on register
+      operands, 1.1e12 flops per launch; cold (the first launches) and
+      sustained (after 10 untimed launches, like the prefill step)."""
+    import torch
+
+    def ev_time(fn, reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(r)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    big = torch.ones(ROTATE_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    best = (0.0, None)
+    for wg in (1024, 2048, 4096, 8192):
+        tl.probe_read(big, sink, wg)
+        t = ev_time(lambda r: tl.probe_read(big, sink, wg), 5)
+        best = max(best, (ROTATE_BYTES / t / 1e9, wg), key=lambda b: b[0])
+    out["read_1GiB"] = {"GBps": round(best[0], 1), "workgroups": best[1],
+                        "frac": round(best[0] / HBM_PEAK_GBPS, 4)}
+
+    chunk = layer_bytes // 16 * 4               # int32 elements, 16-byte multiple
+    nchunk = big.numel() // chunk
+    views = [big[i * chunk:(i + 1) * chunk] for i in range(nchunk)]
+    best = (0.0, None)
+    for wg in (512, 1024, 2048):
+        tl.probe_read(views[0], sink, wg)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                tl.probe_read(views[i % nchunk], sink, wg)
+        g.replay()
+        torch.cuda.synchronize()
+        t = ev_time(lambda r: g.replay(), 1) / steps
+        del g
+        best = max(best, (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
+    out["read_layer_size"] = {"GBps": round(best[0], 1), "workgroups": best[1],
+                              "bytes": chunk * 4, "us": round(chunk * 4 / best[0] / 1e3, 3),
+                              "frac": round(best[0] / HBM_PEAK_GBPS, 4)}
+    del views
+
+    half = big.numel() // 2
+    src, dst = big[:half], big[half:]
+    best = (0.0, None)
+    for wg in (1024, 2048, 4096):
+        tl.probe_copy(src, dst, wg)
+        t = ev_time(lambda r: tl.probe_copy(src, dst, wg), 5)
+        best = max(best, (2 * half * 4 / t / 1e9, wg), key=lambda b: b[0])
+    out["copy_512MiB"] = {"GBps": round(best[0], 1), "workgroups": best[1],
+                          "frac": round(best[0] / HBM_PEAK_GBPS, 4)}
+    del src, dst, big
+
+    mf = {}
+    for wg, iters in PROBE_ITERS.items():
+        buf = torch.empty(wg * tl.PROBE_THREADS, dtype=torch.float32, device="cuda:0")
+        flops = tl.probe_mfma_flops(wg, iters)
+        torch.cuda.synchronize()
+        cold = ev_time(lambda r: tl.probe_mfma(wg, iters, buf), 2)
+        for _ in range(10):
+            tl.probe_mfma(wg, iters, buf)
+        warm = ev_time(lambda r: tl.probe_mfma(wg, iters, buf), 10)
+        mf[wg] = (flops / warm / 1e12, flops / cold / 1e12, wg, iters)
+        del buf
+    sus, cold, wg, iters = max(mf.values(), key=lambda v: v[0])
+    out["mfma_loop"] = {"TFLOPs_sustained": round(sus, 1), "TFLOPs_cold": round(cold, 1),
+                        "workgroups": wg, "iters": iters,
+                        "frac": round(sus / MFMA_BF16_PEAK_TFLOPS, 4)}
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,6 +751,7 @@ def main():
                     help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "LDS_DIR"))
     ap.add_argument("--detail", type=str, default=None, help="write per-shape results here")
     args = ap.parse_args()
 
@@ -572,6 +760,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -661,6 +852,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ach_p, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach_p / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None if traffic_p is None else round(traffic_p, 1),
+                     "mfma_busy_vs_probe": stored_mfma(),
                      "kernel": "gemm_dma_kernel<bf16, per-channel>: one grouped launch of the "
                                "7 projections",
                      "alg_flops_per_launch": pre_flops,
@@ -673,6 +865,12 @@ def main():
         f"{pre_shapes}")
     pack = bench_pack(tl)
     log(f"[bench] pack {pack}")
+    ceilings = measure_ceilings(tl, step_bytes, min(args.steps, 200))
+    log(f"[bench] ceilings {ceilings}")
+    roofline["frac_of_measured_read"] = round(
+        achieved / ceilings["read_layer_size"]["GBps"], 4)
+    prefill["roofline"]["frac_of_mfma_loop"] = round(
+        ach_p / ceilings["mfma_loop"]["TFLOPs_sustained"], 4)
     configs, crossover = (None, None) if args.no_sweep else sweep_configs(tl)
 
     cpu = None
@@ -715,6 +913,7 @@ def main():
         "configs": configs,
         "crossover": crossover,
         "pack": pack,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         "kernels_hash": kernel_source_hash(),
     }

@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
-    "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH",
+    "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH", "probe_read", "probe_copy",
+    "probe_mfma", "probe_mfma_flops",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
@@ -38,7 +39,10 @@ EXPORTS = (
     "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
     "ternary_status_string", "ternary_abi_version", "ternary_shutdown",
 )
+# Every symbol include/ternary_probe.h declares (measurement probes).
+PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_copy", "ternary_probe_mfma")
 MAX_BATCH = 8
+PROBE_THREADS = 256
 
 
 class Problem(ctypes.Structure):
@@ -73,11 +77,14 @@ def lib() -> ctypes.CDLL:
     L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
     L.ternary_linear_batch.argtypes = [p, i32, i32, p]
     L.ternary_select_path.argtypes = [i64, i64, i64, i64]
+    L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
+    L.ternary_probe_copy.argtypes = [p, p, i64, i32, p]
+    L.ternary_probe_mfma.argtypes = [i32, i32, p, p]
     L.ternary_status_string.argtypes = [i32]
     L.ternary_status_string.restype = ctypes.c_char_p
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
-               "ternary_abi_version", "ternary_shutdown"):
+               "ternary_abi_version", "ternary_shutdown", *PROBE_EXPORTS):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -243,3 +250,44 @@ def linear_batch(problems) -> list:
     if st:
         raise TernaryError(st, "ternary_linear_batch")
     return outs
+
+
+# ---------------------------------------------------------------- probes
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int) -> None:
+    """Read all bytes of ``buf`` once (ternary_probe_read); ``sink`` is a
+    one-element int32 device tensor."""
+    _dev(buf, "buf")
+    _dev(sink, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check(int(lib().ternary_probe_read(buf.data_ptr(), nbytes, workgroups, sink.data_ptr(),
+                                        _stream(buf))), "ternary_probe_read")
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> None:
+    """Copy ``src`` into ``dst`` (same byte size) with ternary_probe_copy."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _check(int(lib().ternary_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, workgroups,
+                                        _stream(src))), "ternary_probe_copy")
+
+
+def probe_mfma(workgroups: int, iters: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Run the MFMA loop probe; returns its float32 [workgroups * 256] output.
+    The launch performs workgroups * 4 * iters * 4 * 16384 flops."""
+    n = workgroups * PROBE_THREADS
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    elif out.dtype != torch.float32 or out.numel() < n:
+        raise ValueError(f"out must be float32 with at least {n} elements")
+    _dev(out, "out")
+    _check(int(lib().ternary_probe_mfma(workgroups, iters, out.data_ptr(), _stream(out))),
+           "ternary_probe_mfma")
+    return out
+
+
+def probe_mfma_flops(workgroups: int, iters: int) -> int:
+    return workgroups * 4 * iters * 4 * 16384

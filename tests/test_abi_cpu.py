@@ -1,5 +1,6 @@
 """The C-ABI library without a GPU: it loads, exports what include/ternary.h
-declares, and rejects invalid arguments on the host before any launch.
+and include/ternary_probe.h declare, and rejects invalid arguments on the
+host before any launch.
 
 None of these calls reach the device: every case fails host-side validation
 (or is an M == 0 / N == 0 no-op), so the pointers passed are never used.
@@ -12,6 +13,7 @@ import pytest
 
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "ternary.h"
+PROBE_HEADER = ROOT / "include" / "ternary_probe.h"
 
 
 @pytest.fixture(scope="module")
@@ -23,14 +25,17 @@ def tl():
     return tl
 
 
-def declared_functions():
-    text = HEADER.read_text()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ternary_[a-z_0-9]+)\s*\(", text)))
+def declared_functions(headers=(HEADER, PROBE_HEADER)):
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"\b(ternary_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_expected(tl):
-    assert declared_functions() == sorted(tl.EXPORTS)
+    assert declared_functions((HEADER,)) == sorted(tl.EXPORTS)
+    assert declared_functions((PROBE_HEADER,)) == sorted(tl.PROBE_EXPORTS)
 
 
 def test_library_exports_every_declared_symbol(tl):
@@ -172,3 +177,26 @@ def test_batch_rejects(tl):
     # all members empty: success without any launch
     empty = (P * 2)(_prob(tl, 0, 0, 0, 0, M=0), _prob(tl, 0, 0, 0, 0, N=0))
     assert L.ternary_linear_batch(empty, 2, 0, None) == 0
+
+
+def test_probe_rejects(tl):
+    L = tl.lib()
+    A, B = 1 << 20, 1 << 21   # 16-byte aligned, never dereferenced
+    SHAPE, NULL, ALIGN, ALIAS = -2, -1, -5, -6
+    assert L.ternary_probe_read(A, 17, 64, A, None) == SHAPE
+    assert L.ternary_probe_read(A, -16, 64, A, None) == SHAPE
+    assert L.ternary_probe_read(A, 1024, 0, A, None) == SHAPE
+    assert L.ternary_probe_read(A, 1024, 65537, A, None) == SHAPE
+    assert L.ternary_probe_read(A, 0, 64, None, None) == 0
+    assert L.ternary_probe_read(None, 1024, 64, A, None) == NULL
+    assert L.ternary_probe_read(A + 4, 1024, 64, A, None) == ALIGN
+    assert L.ternary_probe_copy(A, B, 24, 64, None) == SHAPE
+    assert L.ternary_probe_copy(A, None, 1024, 64, None) == NULL
+    assert L.ternary_probe_copy(A, B + 8, 1024, 64, None) == ALIGN
+    assert L.ternary_probe_copy(A, A + 512, 1024, 64, None) == ALIAS
+    assert L.ternary_probe_copy(A, B, 0, 64, None) == 0
+    assert L.ternary_probe_mfma(0, 4, A, None) == SHAPE
+    assert L.ternary_probe_mfma(64, 0, A, None) == SHAPE
+    assert L.ternary_probe_mfma(64, (1 << 20) + 1, A, None) == SHAPE
+    assert L.ternary_probe_mfma(64, 4, None, None) == NULL
+    assert L.ternary_probe_mfma(64, 4, A + 2, None) == ALIGN

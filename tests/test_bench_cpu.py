@@ -3,7 +3,8 @@
 Synthetic counter files stand in for two --pmc runs: a copy probe of known
 size fixes each counter's scale, and the digest must report, for the largest
 dispatch of each kernel family, the scaled bytes per launch; a kernel-trace
-digest must group dispatches by launch shape.
+digest must group dispatches by launch shape; the MFMA counter digest must
+relate the GEMM's MFMA busy cycles to those of the MFMA loop probe.
 """
 
 import csv
@@ -94,3 +95,56 @@ def test_summarize_trace_groups_by_shape(tmp_path, monkeypatch):
     line = [ln for ln in text.splitlines() if "grid=1015808" in ln][0]
     calls, median, mean = line.split()[:3]
     assert int(calls) == 3 and float(median) == pytest.approx(20.0) and float(mean) == pytest.approx(20.0)
+
+
+def test_summarize_mfma_relates_gemm_to_probe(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "MFMA_FILE", tmp_path / "mfma.txt")
+    gemm = "ternary::dma::gemm_dma_kernel<false, false, Cfg<256, 128, 4, 1, 4, 2> >(BigBatch)"
+    probe = "(anonymous namespace)::probe_mfma_kernel(int, float*)"
+    wg = 2048
+    iters = bench.PROBE_ITERS[wg]
+    flops = wg * 4 * 4 * 16384 * iters
+    d1, d2 = tmp_path / "A", tmp_path / "B"
+    d1.mkdir()
+    d2.mkdir()
+    with open(d1 / "bench_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        rows = [(1, gemm, 819200, {"SQ_VALU_MFMA_BUSY_CYCLES": [300.0, 300.0],
+                                   "GRBM_GUI_ACTIVE": [1000.0],
+                                   "SQ_INSTS_VALU_MFMA_MOPS_BF16": [2.0e9]}),
+                (2, gemm, 4096, {"SQ_VALU_MFMA_BUSY_CYCLES": [1.0], "GRBM_GUI_ACTIVE": [1.0]}),
+                (3, probe, wg * 256, {"SQ_VALU_MFMA_BUSY_CYCLES": [800.0],
+                                      "GRBM_GUI_ACTIVE": [1000.0],
+                                      "SQ_INSTS_VALU_MFMA_MOPS_BF16": [flops / 512]})]
+        for did, k, grid, cs in rows:
+            for c, vs in cs.items():
+                for v in vs:
+                    w.writerow({c2: 0 for c2 in COLS} | {
+                        "Dispatch_Id": did, "Kernel_Name": k, "Grid_Size": grid,
+                        "Counter_Name": c, "Counter_Value": v})
+    with open(d2 / "bench_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        for c, v in (("SQ_LDS_BANK_CONFLICT", 10.0), ("SQ_LDS_IDX_ACTIVE", 400.0)):
+            w.writerow({c2: 0 for c2 in COLS} | {"Dispatch_Id": 1, "Kernel_Name": gemm,
+                                                 "Grid_Size": 819200, "Counter_Name": c,
+                                                 "Counter_Value": v})
+        w.writerow({c2: 0 for c2 in COLS} | {"Dispatch_Id": 3, "Kernel_Name": probe,
+                                             "Grid_Size": wg * 256,
+                                             "Counter_Name": "SQ_LDS_IDX_ACTIVE",
+                                             "Counter_Value": 0.0})
+    bench.summarize_mfma(str(d1), str(d2))
+    kv = {}
+    for ln in (tmp_path / "mfma.txt").read_text().splitlines():
+        if ln and not ln.startswith("#"):
+            k, v = ln.split(None, 1)
+            kv[k] = v
+    assert float(kv["gemm_mfma_busy_per_gui"]) == pytest.approx(0.6)
+    assert float(kv["probe_mfma_busy_per_gui"]) == pytest.approx(0.8)
+    assert float(kv["gemm_mfma_busy_vs_probe"]) == pytest.approx(0.75)
+    assert float(kv["probe_mfma_flops"]) == pytest.approx(flops)
+    assert float(kv["probe_flops_issued"]) == pytest.approx(flops)
+    assert float(kv["gemm_mfma_flops"]) == pytest.approx(1.024e12)
+    assert float(kv["gemm_lds_bank_conflict_per_active"]) == pytest.approx(0.025)
+    assert bench.stored_mfma() == pytest.approx(0.75)
