@@ -2,7 +2,8 @@
 
     y = x @ (q * s)^T,  q in {-1, 0, +1} packed 4 codes per byte (2 bits each,
     00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0, first weight in the lowest bits),
-    s an fp16 scale per output channel or per 128 consecutive K weights.
+    s an fp16 scale per output channel or per group of 32, 64, 128 or 256
+    consecutive K weights.
 
 The format is the one stated on trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战"
 (§3.1) and m.nxbn.cn/news/169761 (§2.2); the layer's interface (x, weight,
@@ -215,7 +216,7 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
            out: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] = x [M, K] @ (q * s)^T in x's dtype (bf16 or fp16).
 
-    ``scale`` is fp16 [N] (per channel) or [N, K/128]; ``group_size`` is
+    ``scale`` is fp16 [N] (per channel) or [N, K/group_size]; ``group_size`` is
     inferred from its shape when not given.  ``path`` forces a kernel
     ("gemv", "gemm", "simple"); "auto" picks by M.  Shapes are checked here
     against each other, so the sizes passed to the C ABI match the tensors.

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -30,17 +30,39 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TERNARY_OK : TERNARY_ERR
 // launch limits.
 constexpr int64_t kMaxDim = (int64_t)1 << 24;
 
+// The library's group value of a group_size (-1 -> 0), or -1 if unsupported.
+int group_of(int64_t group_size)
+{
+    if (group_size == -1)
+        return 0;
+    return group_size > 0 && ternary::group_valid(group_size) ? (int)group_size : -1;
+}
+
+// Scale elements of one problem.
+int64_t scale_elems(int64_t N, int64_t K, int64_t group_size)
+{
+    return group_size == -1 ? N : N * (K / group_size);
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K, int64_t group_size)
+{
+    if (group_of(group_size) < 0)
+        return TERNARY_ERR_GROUP;
+    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return TERNARY_ERR_SHAPE;
+    if (group_size > 0 && K % group_size != 0)
+        return TERNARY_ERR_SHAPE;
+    return TERNARY_OK;
+}
+
 int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
                  const uint16_t *scale, int64_t group_size, const void *y)
 {
     if (dtype != TERNARY_BF16 && dtype != TERNARY_FP16)
         return TERNARY_ERR_DTYPE;
-    if (group_size != -1 && group_size != 128)
-        return TERNARY_ERR_GROUP;
-    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
-        return TERNARY_ERR_SHAPE;
-    if (group_size == 128 && K % 128 != 0)
-        return TERNARY_ERR_SHAPE;
+    const int sh = check_shape(M, N, K, group_size);
+    if (sh != TERNARY_OK)
+        return sh;
     if (M == 0 || N == 0)
         return TERNARY_OK;
     if (!x || !packed || !scale || !y)
@@ -48,18 +70,18 @@ int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, cons
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(packed, 16) || !aligned(scale, 2))
         return TERNARY_ERR_ALIGN;
     const int64_t ybytes = 2 * M * N;
-    const int64_t sbytes = 2 * (group_size == -1 ? N : N * (K / 128));
+    const int64_t sbytes = 2 * scale_elems(N, K, group_size);
     if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, packed, N * (K / 4)) ||
         overlap(y, ybytes, scale, sbytes))
         return TERNARY_ERR_ALIAS;
     return TERNARY_OK;
 }
 
-int select_path(int64_t M, int64_t K)
+int select_path(int64_t M, int64_t K, int group)
 {
-    if (ternary::gemv_preferred(M, K))
+    if (ternary::gemv_preferred(M, K, group))
         return TERNARY_PATH_GEMV;
-    if (ternary::gemm_takes(M, K))
+    if (ternary::gemm_takes(M, K, group))
         return TERNARY_PATH_GEMM;
     return TERNARY_PATH_SIMPLE;
 }
@@ -82,8 +104,8 @@ const char *ternary_status_string(int status)
     switch (status) {
     case TERNARY_OK: return "ok";
     case TERNARY_ERR_NULL: return "null pointer argument";
-    case TERNARY_ERR_SHAPE: return "invalid shape (negative size, K % 4 != 0, or K % 128 != 0 in group mode)";
-    case TERNARY_ERR_GROUP: return "group_size must be -1 (per channel) or 128";
+    case TERNARY_ERR_SHAPE: return "invalid shape (negative size, K % 4 != 0, or K not a multiple of the group size)";
+    case TERNARY_ERR_GROUP: return "group_size must be -1 (per channel), 32, 64, 128 or 256";
     case TERNARY_ERR_DTYPE: return "activation dtype must be TERNARY_BF16 or TERNARY_FP16";
     case TERNARY_ERR_ALIGN: return "pointer not aligned (data 16 bytes, scale 2 bytes)";
     case TERNARY_ERR_ALIAS: return "output overlaps an input";
@@ -133,12 +155,10 @@ int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipSt
 
 int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size)
 {
-    if (group_size != -1 && group_size != 128)
-        return TERNARY_ERR_GROUP;
-    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
-        (group_size == 128 && K % 128 != 0))
-        return TERNARY_ERR_SHAPE;
-    return select_path(M, K);
+    const int sh = check_shape(M, N, K, group_size);
+    if (sh != TERNARY_OK)
+        return sh;
+    return select_path(M, K, group_of(group_size));
 }
 
 int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
@@ -148,15 +168,16 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     const int st = check_linear(x, dtype, M, N, K, packed, scale, group_size, y);
     if (st != TERNARY_OK)
         return st;
+    const int group = group_of(group_size);
     if (path == TERNARY_PATH_AUTO)
-        path = select_path(M, K);
+        path = select_path(M, K, group);
     switch (path) {
     case TERNARY_PATH_GEMV:
-        if (!(M == 0 || N == 0 || ternary::gemv_takes(M, K)))
+        if (!(M == 0 || N == 0 || ternary::gemv_takes(M, K, group)))
             return TERNARY_ERR_PATH;
         break;
     case TERNARY_PATH_GEMM:
-        if (!(M == 0 || N == 0 || ternary::gemm_takes(M, K)))
+        if (!(M == 0 || N == 0 || ternary::gemm_takes(M, K, group)))
             return TERNARY_ERR_PATH;
         break;
     case TERNARY_PATH_SIMPLE: break;
@@ -165,19 +186,18 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     if (M == 0 || N == 0)
         return TERNARY_OK;
     const bool fp16 = dtype == TERNARY_FP16;
-    const bool grouped = group_size == 128;
     const uint16_t *xv = static_cast<const uint16_t *>(x);
     uint16_t *yv = static_cast<uint16_t *>(y);
     hipError_t e;
     switch (path) {
     case TERNARY_PATH_GEMV:
-        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv, stream);
+        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream);
         break;
     case TERNARY_PATH_GEMM:
-        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv, stream);
+        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream);
         break;
     default:
-        e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, grouped, yv,
+        e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv,
                                    stream);
         break;
     }
@@ -205,7 +225,7 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
             if (i == j)
                 continue;
             const ternary_problem &b = problems[j];
-            const int64_t sb = 2 * (b.group_size == -1 ? b.N : b.N * (b.K / 128));
+            const int64_t sb = 2 * scale_elems(b.N, b.K, b.group_size);
             if (overlap(a.y, ya, b.x, 2 * b.M * b.K) ||
                 overlap(a.y, ya, b.packed, b.N * (b.K / 4)) || overlap(a.y, ya, b.scale, sb) ||
                 overlap(a.y, ya, b.y, 2 * b.M * b.N))
@@ -221,11 +241,11 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
             continue;
         const ternary::GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
                                      static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
-                                     p.group_size == 128};
-        if (ternary::gemv_preferred(p.M, p.K)) {
+                                     group_of(p.group_size)};
+        if (ternary::gemv_preferred(p.M, p.K, a.group)) {
             fused[nf++] = a;
-        } else if (ternary::gemm_takes(p.M, p.K) &&
-                   ternary::gemm_big_takes(a.M, a.N, a.K, a.grouped, a.scale)) {
+        } else if (ternary::gemm_takes(p.M, p.K, a.group) &&
+                   ternary::gemm_big_takes(a.M, a.N, a.K, a.group, a.scale)) {
             grouped_gemm[ng++] = a;
         } else {
             const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,

@@ -7,8 +7,9 @@
 // (never to HBM: no dense weight copy exists outside LDS), and both operands
 // feed v_mfma_f32_16x16x32_{bf16,f16} with fp32 accumulation.  Scales follow
 // [trdm] trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1/§4.2
-// (group of 128 K, multiplied at the group boundary) and [nxbn] §3.2/§4.2
-// (per output channel, multiplied in the epilogue).
+// (group of 128 K, multiplied at the group boundary; groups of 64 in [xxqk]
+// §4.2, of 32 and 256 in the yangyitao.com vLLM book, chapter 13, §13.3.3)
+// and [nxbn] §3.2/§4.2 (per output channel, multiplied in the epilogue).
 //
 // Tiling: 128 tokens x 128 channels x 64 K per workgroup step, 256 threads as
 // 2x2 waves of 64x64 (4x4 MFMA tiles each).  Two LDS buffers per operand: the
@@ -81,10 +82,13 @@ __device__ __forceinline__ void store_tile(const TileRegs &r, uint16_t *sA, uint
         dst[v] = make_uint4(d[4 * v], d[4 * v + 1], d[4 * v + 2], d[4 * v + 3]);
 }
 
+// glog: log2 of the group size (group-scaled instances, groups of 32 K or
+// more: every 32-K MFMA step lies inside one group).
 template <bool FP16, bool GROUPED>
 __global__ void __launch_bounds__(THREADS)
     gemm_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N, int K)
+                const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N, int K,
+                int glog)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
@@ -97,7 +101,7 @@ __global__ void __launch_bounds__(THREADS)
     const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * BM;
     const int nk = K / BK;
-    const int ngroups = K >> 7;
+    const int ngroups = K >> glog;
 
     f32x4_t acc[4][4];
     f32x4_t part[4][4];
@@ -143,22 +147,24 @@ __global__ void __launch_bounds__(THREADS)
                     else
                         acc[i][j] = mfma<FP16>(af[i], bf[j], acc[i][j]);
                 }
-        }
-
-        if constexpr (GROUPED) {
-            if (kt & 1) {  // end of a 128-wide group: fold with its scale
-                const int grp = kt >> 1;
+            if constexpr (GROUPED) {
+                const int kend = kt * BK + kk + 32;  // K covered so far
+                if ((kend & ((1 << glog) - 1)) == 0) {
+                    // end of a group: fold its sums with the group's scales
+                    const int grp = (kend >> glog) - 1;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 64 + j * 16 + frow;
-                    const float sc = n < N ? f16_bits_to_f32(scale[(int64_t)n * ngroups + grp]) : 0.f;
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = n0 + wn * 64 + j * 16 + frow;
+                        const float sc =
+                            n < N ? f16_bits_to_f32(scale[(int64_t)n * ngroups + grp]) : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            acc[i][j][r] += sc * part[i][j][r];
-                            part[i][j][r] = 0.f;
-                        }
+                            for (int r = 0; r < 4; ++r) {
+                                acc[i][j][r] += sc * part[i][j][r];
+                                part[i][j][r] = 0.f;
+                            }
+                    }
                 }
             }
         }
@@ -294,13 +300,20 @@ struct BigBatch {
     BigProblem p[kGemvMaxBatch];
 };
 
-template <bool FP16, bool GROUPED, class C>
+// GS: 0 for per-channel scales, else the group size (64, 128 or 256 K: one,
+// two or four K steps).
+template <bool FP16, int GS, class C>
 __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigBatch batch)
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
-    // Group-128 scales: every stage also carries one dword per channel, the
-    // scales of the two groups of the 4 steps (256 K) it belongs to.
-    static_assert(!GROUPED || (C::TN == THREADS && NS % 4 == 0), "one scale dword per thread");
+    constexpr bool GROUPED = GS != 0;
+    constexpr int SPG = GROUPED ? GS / TK : 1;  // K steps per group
+    constexpr int GSH = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);
+    // Group scales: every stage also carries one dword per channel, the
+    // scales of the pair of groups its K step belongs to.
+    static_assert(!GROUPED || (C::TN == THREADS && NS % 4 == 0 && (GS == 64 || GS == 128 ||
+                                                                   GS == 256)),
+                  "one scale dword per thread; groups of 1, 2 or 4 steps");
     constexpr int VPS = C::VPS + (GROUPED ? 1 : 0);  // vector memory ops per thread and stage
     // One LDS object per stage: the compiler then knows that a DMA into one
     // stage does not write the stage being read and waits for nothing there.
@@ -401,10 +414,11 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         woff[i] = n0 + row < N ? (n0 + row) * (K >> 2) + 4 * (d & 3) : kOOB;
     }
     // Scales: thread t loads channel n0 + t's pair of groups.
+    const int ngroups = K / (GROUPED ? GS : 1);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(scale), (short)0,
-        GROUPED ? (int)((uint32_t)N * (uint32_t)(K >> 7) * 2u) : 0, 0x00020000);
-    const int soff = GROUPED && n0 + tid < N ? (n0 + tid) * (K >> 7) * 2 : kOOB;
+        GROUPED ? (int)((uint32_t)N * (uint32_t)ngroups * 2u) : 0, 0x00020000);
+    const int soff = GROUPED && n0 + tid < N ? (n0 + tid) * ngroups * 2 : kOOB;
     // Wave-uniform LDS destinations of this wave's DMAs (kept in SGPRs).
     const int wave_chunk = __builtin_amdgcn_readfirstlane(wave) * 64;
 
@@ -420,8 +434,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
         for (int i = 0; i < C::WI; ++i)
             dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * (TK / 4));
-        if constexpr (GROUPED)
-            dma_to_lds<4>(sr, (void *)(lsc[s] + wave_chunk), soff, (kc >> 2) * 4);
+        if constexpr (GROUPED)  // the dword holding group kc / SPG
+            dma_to_lds<4>(sr, (void *)(lsc[s] + wave_chunk), soff, ((kc >> GSH) >> 1) * 4);
     };
 
     f32x4_t acc[FN][FM];
@@ -442,7 +456,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     const int xa1 = xa0 ^ 1;
     const int wa = (wn * FN * 16 + fr) * 4 + g;
 
-    auto compute = [&](auto S) {
+    auto compute = [&](auto S, int kt) {
         constexpr int s = decltype(S)::value;
         uint32_t wv[FN];
 #pragma unroll
@@ -462,26 +476,31 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
                                    : make_uint4(d[0], d[1], d[2], d[3]);
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
-                    if constexpr (GROUPED)  // a group starts at even steps (slices are whole rounds)
-                        part[f][j] = mfma<FP16>(a, xf[j], (s % 2 == 0 && kk == 0) ? zero4 : part[f][j]);
+                    if constexpr (GROUPED)  // steps kt = s mod NS (slices are whole rounds)
+                        part[f][j] =
+                            mfma<FP16>(a, xf[j], (s % SPG == 0 && kk == 0) ? zero4 : part[f][j]);
                     else
                         acc[f][j] = mfma<FP16>(a, xf[j], acc[f][j]);
                 }
             }
         }
         if constexpr (GROUPED) {
-            if constexpr (s % 2 == 1) {
-                // End of a 128-K group: fold its sums with the group's scales
-                // (low half of the stage's dwords for the round's first
-                // group, high half for its second).
+            if constexpr (s % SPG == SPG - 1) {
+                // End of a group: fold its sums with the group's scales (low
+                // half of the stage's dwords for an even group, high half for
+                // an odd one; known from s alone when NS spans two groups).
+                int odd;
+                if constexpr (NS % (2 * SPG) == 0)
+                    odd = (s >> GSH) & 1;
+                else
+                    odd = ((kbase + kt) >> GSH) & 1;
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     const u32x4_t w = *reinterpret_cast<const lds_u4 *>(
                         lsc[s] + wn * FN * 16 + f * 16 + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sc =
-                            f16_bits_to_f32((uint16_t)(((s >> 1) & 1) == 0 ? w[r] : w[r] >> 16));
+                        const float sc = f16_bits_to_f32((uint16_t)(odd ? w[r] >> 16 : w[r]));
 #pragma unroll
                         for (int j = 0; j < FM; ++j)
                             acc[f][j][r] += sc * part[f][j][r];
@@ -498,7 +517,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         constexpr int s = decltype(S)::value;
         wait_and_barrier<(NS - 2) * VPS>();
         issue(std::integral_constant<int, (s + NS - 1) % NS>{}, kt + NS - 1);
-        compute(S);
+        compute(S, kt);
     };
 
     // Prologue: stages 0 .. NS-2.
@@ -611,11 +630,11 @@ __global__ void __launch_bounds__(256)
 
 template <bool FP16, bool GROUPED>
 hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
-                         const uint16_t *scale, uint16_t *y, hipStream_t stream)
+                         const uint16_t *scale, int glog, uint16_t *y, hipStream_t stream)
 {
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
     hipLaunchKernelGGL((gemm_kernel<FP16, GROUPED>), grid, dim3(THREADS), 0, stream, x, packed,
-                       scale, y, M, N, K);
+                       scale, y, M, N, K, glog);
     return hipGetLastError();
 }
 
@@ -634,8 +653,9 @@ typedef dma::Cfg<256, 64, 4, 1, 4, 2> MidCfg;   // 32 < M <= 64 (or K % 512 != 0
 typedef dma::Cfg<256, 32, 4, 1, 8, 2> SmallCfg; // M <= 32, K % 512 == 0
 
 // Which configuration a problem runs with: 0 small, 1 mid, 2 large.
-int big_cfg_of(int M, int K, bool grouped)
+int big_cfg_of(int M, int K, int group)
 {
+    const bool grouped = group != 0;
     if (M <= 32 && K % (dma::TK * SmallCfg::NS) == 0)
         return 0;
     return M <= 64 || grouped ? 1 : 2;
@@ -643,13 +663,18 @@ int big_cfg_of(int M, int K, bool grouped)
 
 // The pipelined kernel takes problems whose K is a whole number of 4-step
 // rounds (256), whose buffer offsets stay below the out-of-range marker, and
-// (group scales) whose scale array is 4-byte aligned: it loads a channel's
-// two scales of a round as one dword.
-bool gemm_big_takes(int M, int N, int K, bool grouped, const void *scale)
+// (group scales) groups of 64, 128 or 256 K whose scale array is 4-byte
+// aligned with an even number of groups per row: it loads a channel's scales
+// of two consecutive groups as one dword.
+bool gemm_big_takes(int M, int N, int K, int group, const void *scale)
 {
-    return M >= 1 && N >= 1 && K % (dma::TK * BigCfg::NS) == 0 &&
-           (int64_t)M * K * 2 < dma::kOOB && (int64_t)N * (K / 4) < dma::kOOB &&
-           (!grouped || (((uintptr_t)scale & 3) == 0 && (int64_t)N * (K / 128) * 2 < dma::kOOB));
+    if (M < 1 || N < 1 || K % (dma::TK * BigCfg::NS) != 0 || (int64_t)M * K * 2 >= dma::kOOB ||
+        (int64_t)N * (K / 4) >= dma::kOOB)
+        return false;
+    if (group == 0)
+        return true;
+    return (group == 64 || group == 128 || group == 256) && (K / group) % 2 == 0 &&
+           ((uintptr_t)scale & 3) == 0 && (int64_t)N * (K / group) * 2 < dma::kOOB;
 }
 
 // Compute units of the current device (cached per device).
@@ -690,7 +715,7 @@ int big_ksplit(int tiles, int K, int ns, int tile_elems)
 // longest K first so that the longest tiles start first.  When all their
 // tiles together do not cover the compute units, each problem's K range is
 // split as big_ksplit() says and per-problem reduce kernels follow.
-template <bool FP16, bool GROUPED, class C>
+template <bool FP16, int GS, class C>
 hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipStream_t stream)
 {
     int order[kGemvMaxBatch];
@@ -751,7 +776,7 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
         b.wg0[r] = wg;
         wg += tiles[i] * ks[i];
     }
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, GROUPED, C>), dim3(wg), dim3(C::THREADS), 0,
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, GS, C>), dim3(wg), dim3(C::THREADS), 0,
                        stream, b);
     hipError_t e = hipGetLastError();
     for (int r = 0; r < count && e == hipSuccess; ++r) {
@@ -760,7 +785,7 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
             continue;
         const int i = order[r];
         const int64_t n4 = (int64_t)tiles[i] * (C::TN * C::TM / 4);
-        hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, GROUPED, C>),
+        hipLaunchKernelGGL((dma::gemm_split_reduce<FP16, GS != 0, C>),
                            dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p.partial,
                            p.scale, p.y, p.M, p.N, p.ksplit);
         e = hipGetLastError();
@@ -768,28 +793,41 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
     return e;
 }
 
+template <bool FP16, int GS>
+hipError_t launch_big_group(const GemvArgs *args, const int (*idx)[kGemvMaxBatch], const int *n,
+                            hipStream_t stream)
+{
+    hipError_t e = hipSuccess;
+    if (n[0] && e == hipSuccess)
+        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[0], n[0], stream);
+    if (n[1] && e == hipSuccess)
+        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[1], n[1], stream);
+    if constexpr (GS == 0)  // group-scaled problems never take the large configuration
+        if (n[2] && e == hipSuccess)
+            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[2], n[2], stream);
+    return e;
+}
+
 template <bool FP16>
 hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
 {
-    // one launch per (scale mode, configuration) present
-    int idx[6][kGemvMaxBatch], n[6] = {};
+    // one launch per (group size, configuration) present
+    int idx[4][3][kGemvMaxBatch], n[4][3] = {};
     static_assert(kGemvMaxBatch <= 8, "batch table");
     for (int i = 0; i < count; ++i) {
-        const int m = (args[i].grouped ? 3 : 0) + big_cfg_of(args[i].M, args[i].K, args[i].grouped);
-        idx[m][n[m]++] = i;
+        const int g = args[i].group;
+        const int mode = g == 0 ? 0 : (g == 64 ? 1 : (g == 128 ? 2 : 3));
+        const int c = big_cfg_of(args[i].M, args[i].K, g);
+        idx[mode][c][n[mode][c]++] = i;
     }
-    hipError_t e = hipSuccess;
-    if (n[0] && e == hipSuccess)
-        e = launch_big_mode<FP16, false, SmallCfg>(args, idx[0], n[0], stream);
-    if (n[1] && e == hipSuccess)
-        e = launch_big_mode<FP16, false, MidCfg>(args, idx[1], n[1], stream);
-    if (n[2] && e == hipSuccess)
-        e = launch_big_mode<FP16, false, BigCfg>(args, idx[2], n[2], stream);
-    if (n[3] && e == hipSuccess)
-        e = launch_big_mode<FP16, true, SmallCfg>(args, idx[3], n[3], stream);
-    if (n[4] && e == hipSuccess)
-        e = launch_big_mode<FP16, true, MidCfg>(args, idx[4], n[4], stream);
-    return e;  // (group-scaled problems never take the large configuration)
+    hipError_t e = launch_big_group<FP16, 0>(args, idx[0], n[0], stream);
+    if (e == hipSuccess)
+        e = launch_big_group<FP16, 64>(args, idx[1], n[1], stream);
+    if (e == hipSuccess)
+        e = launch_big_group<FP16, 128>(args, idx[2], n[2], stream);
+    if (e == hipSuccess)
+        e = launch_big_group<FP16, 256>(args, idx[3], n[3], stream);
+    return e;
 }
 
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
@@ -799,17 +837,18 @@ hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStre
 }
 
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream)
 {
-    if (gemm_big_takes(M, N, K, grouped, scale)) {
-        const GemvArgs a = {x, packed, scale, y, M, N, K, grouped};
+    if (gemm_big_takes(M, N, K, group, scale)) {
+        const GemvArgs a = {x, packed, scale, y, M, N, K, group};
         return launch_gemm_batch(&a, 1, fp16, stream);
     }
+    const int glog = group ? group_log2(group) : 0;
     if (fp16)
-        return grouped ? launch_gemm_t<true, true>(x, M, N, K, packed, scale, y, stream)
-                       : launch_gemm_t<true, false>(x, M, N, K, packed, scale, y, stream);
-    return grouped ? launch_gemm_t<false, true>(x, M, N, K, packed, scale, y, stream)
-                   : launch_gemm_t<false, false>(x, M, N, K, packed, scale, y, stream);
+        return group ? launch_gemm_t<true, true>(x, M, N, K, packed, scale, glog, y, stream)
+                     : launch_gemm_t<true, false>(x, M, N, K, packed, scale, 0, y, stream);
+    return group ? launch_gemm_t<false, true>(x, M, N, K, packed, scale, glog, y, stream)
+                 : launch_gemm_t<false, false>(x, M, N, K, packed, scale, 0, y, stream);
 }
 
 }  // namespace ternary

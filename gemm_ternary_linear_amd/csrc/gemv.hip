@@ -5,9 +5,11 @@
 // small M is bound by the HBM stream of packed weights ([nxbn]
 // m.nxbn.cn/news/169761 §4.1/§4.4: decode is memory-bound, the 2-bit packing
 // is what cuts the bytes).  Scale granularity: one fp16 per output channel
-// ([nxbn] §3.2) or per 128 consecutive K weights ([trdm] trdm.cn
-// "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1), applied to the
-// finished partial sum of its block ([trdm] §4.2).  Several projections (for
+// ([nxbn] §3.2) or per group of 128 consecutive K weights ([trdm] trdm.cn
+// "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1; 64 in [xxqk]
+// m.xxqk.cn/news/593501 §4.2, 32 and 256 in the yangyitao.com vLLM book,
+// chapter 13, §13.3.3), applied to the finished partial sum of its group
+// ([trdm] §4.2).  Several projections (for
 // instance the segments of a fused QKV weight, [trdm] §2.2) can share one
 // launch, which pays the fixed launch and first-byte latency once.
 //
@@ -22,13 +24,15 @@
 //    is decoded.
 //  * The codes are decoded in registers (decode16, branch-free byte permutes)
 //    into the A operand of v_mfma_f32_16x16x32_{bf16,f16}: rows = channels,
-//    k in natural order.  The B operand is the activation: column 2t+p holds
-//    token t restricted to 128-group p of the slab (lanes of the other group
-//    keep zeros), so one MFMA chain yields both groups' partial sums
-//    separately and each is scaled by its own fp16 scale before it joins the
-//    fp32 accumulator.  Only the lanes that own real B entries read x.
-//  * Per-channel and group-scaled problems are separate kernel instances, so
-//    a batch that holds both takes two launches.
+//    k in natural order.  The B operand is the activation: column GC*t + p
+//    holds token t restricted to group p of the slab (GC = 2 halves of 128
+//    for per-channel scales and groups of 128 or 256, 4 groups of 64, 8 of
+//    32; lanes of the other groups keep zeros), so one MFMA chain yields every
+//    group's partial sum separately and each is scaled by its own fp16 scale
+//    before it joins the fp32 accumulator.  Only the lanes that own real B
+//    entries read x.
+//  * Each scale mode (per channel, each group size) is a separate kernel
+//    instance, so a batch that mixes them takes one launch per mode.
 //  * x (all M tokens) is copied into LDS with direct global->LDS loads, whole
 //    K when it fits 64 KB, otherwise in K chunks (then KP = 1 and the waves
 //    walk the chunks together).  Group scales of the workgroup's channels are
@@ -55,7 +59,7 @@ struct GemvProblem {
     const uint16_t *scale;
     uint16_t *y;
     int M, N, K;
-    int grouped;  // group-128 scales
+    int group;    // 0 (per channel) or the group size
     int rb;       // 16-channel blocks per workgroup: 1, 2 or 4
     int spart;    // slabs per wave (one K part)
     int kc;       // K elements staged in LDS at once (multiple of 1024)
@@ -105,11 +109,15 @@ __device__ __forceinline__ void stage_x(const uint16_t *x, uint16_t *xs, int M, 
     }
 }
 
-template <bool FP16, bool GROUPED>
+// GC: MFMA B columns per token (gemv_cols of the group size): 2 for
+// per-channel scales and groups of 128 K or more, 4 for groups of 64, 8 for
+// groups of 32.  Column GC*t + p holds token t restricted to group p of each
+// slab (to half p of it when GC = 2).
+template <bool FP16, bool GROUPED, int GC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8)))
 gemv_kernel(const GemvBatch batch)
 {
-    // LDS: [4][64] fp32x4 reduction tiles | scales ([RB][K/128][16] grouped,
+    // LDS: [4][64] fp32x4 reduction tiles | scales ([RB][K/group][16] grouped,
     // [RB*16] per channel, 128 bytes) | x [M][kc]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -133,13 +141,16 @@ gemv_kernel(const GemvBatch batch)
     const int rb = blk0 + rbi;
     const int g = lane >> 4;          // lane group: which 64-code quarter of a slab
     const int col = lane & 15;        // MFMA column (B) and row (A) index of this lane
-    const int tok = col >> 1;         // token of this B column
-    const int par = col & 1;          // 128-group of the slab this column collects
+    const int tok = col / GC;         // token of this B column
+    const int par = col % GC;         // group (or half) of the slab this column collects
     const int row = rb * 16 + col;    // channel whose codes this lane loads (A row)
     const bool row_ok = row < N;
-    const bool b_lane = tok < M && (g >> 1) == par;
+    // Lane group g holds codes 64g .. 64g+63 of a slab, word d of them codes
+    // 64g + 16d .. +15: in half g/2, in 64-group g, in 32-group 2g + d/2.
+    const bool b_lane = tok < M && (GC == 2 ? (g >> 1) == par : (GC == 4 ? g == par : true));
     const int nslabs = (K + 255) >> 8;
-    const int ngroups = K >> 7;
+    const int glog = GROUPED ? 31 - __builtin_clz((unsigned)P.group) : 7;
+    const int ngroups = K >> glog;
     const int s_begin = kp * P.spart;
     const int s_end = s_begin + P.spart < nslabs ? s_begin + P.spart : nslabs;
     const int chunk_slabs = kc >> 8;
@@ -147,6 +158,7 @@ gemv_kernel(const GemvBatch batch)
     f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
     uint16_t *sc = reinterpret_cast<uint16_t *>(smem + 4 * 1024);
     uint16_t *xs = sc + (GROUPED ? ((RB * ngroups * 16 + 7) & ~7) : 64);
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
     // Packed codes: every load is in bounds.  Rows past N read row N-1 (their
     // C rows are never stored); slabs past this wave's range repeat its last
@@ -214,7 +226,16 @@ gemv_kernel(const GemvBatch batch)
             f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                if (b_lane) {
+                if constexpr (GC == 8) {
+                    // the 32-groups change with d: every lane rewrites both
+                    if (b_lane && par == 2 * g + (d >> 1)) {
+                        b0 = xb[2 * d];
+                        b1 = xb[2 * d + 1];
+                    } else {
+                        b0 = zero4;
+                        b1 = zero4;
+                    }
+                } else if (b_lane) {
                     b0 = xb[2 * d];
                     b1 = xb[2 * d + 1];
                 }
@@ -224,8 +245,10 @@ gemv_kernel(const GemvBatch batch)
                 part = mfma16x16x32<FP16>(a + 4, b1, part);
             }
             if constexpr (GROUPED) {
-                // C rows of this lane: channels rb*16 + 4g + r; column group `par`.
-                const int grp = 2 * s + par;
+                // C rows of this lane: channels rb*16 + 4g + r; column group
+                // `par` (for GC = 2 a half slab: 128 K, within group
+                // (2s + par) * 128 / group when groups are longer).
+                const int grp = GC == 2 ? (2 * s + par) >> (glog - 7) : GC * s + par;
                 if (grp < ngroups) {
                     const uint2 s4 = *reinterpret_cast<const uint2 *>(
                         sc + (rbi * ngroups + grp) * 16 + 4 * g);
@@ -268,7 +291,12 @@ gemv_kernel(const GemvBatch batch)
     uint16_t *__restrict__ y = P.y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float tot = sum[r] + __shfl_xor(sum[r], 1);
+        // the GC columns of a token (adjacent lanes) hold disjoint K sets
+        float tot = sum[r] + __shfl_xor(sum[r], 1);
+        if constexpr (GC >= 4)
+            tot += __shfl_xor(tot, 2);
+        if constexpr (GC >= 8)
+            tot += __shfl_xor(tot, 4);
         const int ch = rb * 16 + 4 * g + r;
         if (par == 0 && tok < M && ch < N) {
             float o = 0.5f * tot;  // decoded weights are +-2
@@ -307,7 +335,7 @@ size_t plan(GemvProblem &p)
     p.kc = kc;
     const int KP = 4 / p.rb;
     p.spart = (nslabs + KP - 1) / KP;
-    return 4 * 1024 + (p.grouped ? (size_t)((p.rb * (p.K / 128) * 16 + 7) & ~7) * 2 : 128) +
+    return 4 * 1024 + (p.group ? (size_t)((p.rb * (p.K / p.group) * 16 + 7) & ~7) * 2 : 128) +
            (size_t)p.M * kc * 2;
 }
 
@@ -317,8 +345,21 @@ int units_of(const GemvProblem &p) { return ((p.N + 15) / 16 + p.rb - 1) / p.rb;
 
 namespace {
 
-// One launch for the problems of one scale mode.
-hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool fp16, bool grouped,
+// One launch for the problems of one group value.
+template <bool FP16>
+void launch_kernel(int group, int units, size_t lds, hipStream_t stream, const GemvBatch &b)
+{
+    if (group == 0)
+        hipLaunchKernelGGL((gemv_kernel<FP16, false, 2>), dim3(units), dim3(kThreads), lds, stream, b);
+    else if (group == 32)
+        hipLaunchKernelGGL((gemv_kernel<FP16, true, 8>), dim3(units), dim3(kThreads), lds, stream, b);
+    else if (group == 64)
+        hipLaunchKernelGGL((gemv_kernel<FP16, true, 4>), dim3(units), dim3(kThreads), lds, stream, b);
+    else
+        hipLaunchKernelGGL((gemv_kernel<FP16, true, 2>), dim3(units), dim3(kThreads), lds, stream, b);
+}
+
+hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool fp16, int group,
                        hipStream_t stream)
 {
     GemvBatch b;
@@ -327,7 +368,7 @@ hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool f
     int units = 0;
     for (int oi = 0; oi < count; ++oi) {
         const GemvArgs &a = args[order[oi]];
-        if (a.M == 0 || a.N == 0 || a.grouped != grouped)
+        if (a.M == 0 || a.N == 0 || a.group != group)
             continue;
         GemvProblem &p = b.p[b.count++];
         p.x = a.x;
@@ -337,7 +378,7 @@ hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool f
         p.M = a.M;
         p.N = a.N;
         p.K = a.K;
-        p.grouped = grouped ? 1 : 0;
+        p.group = group;
         const size_t l = plan(p);
         lds = l > lds ? l : lds;
         p.unit0 = units;
@@ -345,18 +386,10 @@ hipError_t launch_mode(const GemvArgs *args, const int *order, int count, bool f
     }
     if (b.count == 0)
         return hipSuccess;
-    if (fp16) {
-        if (grouped)
-            hipLaunchKernelGGL((gemv_kernel<true, true>), dim3(units), dim3(kThreads), lds, stream, b);
-        else
-            hipLaunchKernelGGL((gemv_kernel<true, false>), dim3(units), dim3(kThreads), lds, stream, b);
-    } else {
-        if (grouped)
-            hipLaunchKernelGGL((gemv_kernel<false, true>), dim3(units), dim3(kThreads), lds, stream, b);
-        else
-            hipLaunchKernelGGL((gemv_kernel<false, false>), dim3(units), dim3(kThreads), lds, stream,
-                               b);
-    }
+    if (fp16)
+        launch_kernel<true>(group, units, lds, stream, b);
+    else
+        launch_kernel<false>(group, units, lds, stream, b);
     return hipGetLastError();
 }
 
@@ -377,18 +410,18 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             order[j] = order[j - 1];
             order[j - 1] = t;
         }
-    // Per-channel and group-scaled problems are separate kernels, and so are
-    // the problems the streaming kernel takes (M = 1, M = 2) and the others:
-    // one launch per non-empty class.
-    for (int mode = 0; mode < 2; ++mode) {
-        const bool grouped = mode == 1;
+    // Each group value (per channel, 32, 64, 128, 256) is a separate kernel
+    // instance, and so are the problems the streaming kernel takes (M = 1,
+    // M = 2) and the others: one launch per non-empty class.
+    static const int kGroups[] = {0, 32, 64, 128, 256};
+    for (const int group : kGroups) {
         int stream_idx[kGemvStreamMaxM][kGemvMaxBatch], other_idx[kGemvMaxBatch];
         int ns[kGemvStreamMaxM] = {}, no = 0;
         for (int oi = 0; oi < count; ++oi) {
             const GemvArgs &a = args[order[oi]];
-            if (a.grouped != grouped || a.M == 0 || a.N == 0)
+            if (a.group != group || a.M == 0 || a.N == 0)
                 continue;
-            if (gemv_stream_takes(a.M, a.K, grouped))
+            if (gemv_stream_takes(a.M, a.K, group))
                 stream_idx[a.M - 1][ns[a.M - 1]++] = order[oi];
             else
                 other_idx[no++] = order[oi];
@@ -396,12 +429,12 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
         for (int m = 0; m < kGemvStreamMaxM; ++m) {
             if (ns[m] == 0)
                 continue;
-            const hipError_t e = launch_gemv_stream(args, stream_idx[m], ns[m], fp16, grouped, stream);
+            const hipError_t e = launch_gemv_stream(args, stream_idx[m], ns[m], fp16, group, stream);
             if (e != hipSuccess)
                 return e;
         }
         if (no > 0) {
-            const hipError_t e = launch_mode(args, other_idx, no, fp16, grouped, stream);
+            const hipError_t e = launch_mode(args, other_idx, no, fp16, group, stream);
             if (e != hipSuccess)
                 return e;
         }
@@ -410,9 +443,9 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
 }
 
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream)
 {
-    const GemvArgs a = {x, packed, scale, y, M, N, K, grouped};
+    const GemvArgs a = {x, packed, scale, y, M, N, K, group};
     return launch_gemv_batch(&a, 1, fp16, stream);
 }
 

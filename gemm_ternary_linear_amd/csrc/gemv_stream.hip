@@ -28,11 +28,13 @@
 //    matrix and x past K read as zeros.
 //  * Decoding and MFMA: each 32-bit word of codes becomes 16 bf16/fp16
 //    weights of +-2 or 0 in registers (decode16), the A operand of
-//    v_mfma_f32_16x16x32_{bf16,f16} (rows = channels); B column 2t+p holds
-//    token t restricted to 128-group p of the slab, so group-128 scales
-//    ([trdm] trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战"
-//    §3.1/§4.2) apply to each group's fp32 partial, and per-channel scales
-//    ([nxbn] §3.2) to the final sum.
+//    v_mfma_f32_16x16x32_{bf16,f16} (rows = channels); B column GC*t + p
+//    holds token t restricted to group p of the slab (GC = 2 halves of 128,
+//    4 groups of 64, 8 groups of 32), so group scales ([trdm] trdm.cn
+//    "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1/§4.2: 128;
+//    [xxqk] m.xxqk.cn/news/593501 §4.2: 64; yangyitao.com vLLM book, chapter
+//    13, §13.3.3: 32, 256) apply to each group's fp32 partial, and
+//    per-channel scales ([nxbn] §3.2) to the final sum.
 //  * A workgroup holds RB channel blocks x KP K parts (RB * KP <= 16 waves);
 //    the K parts of a block are reduced through LDS in a fixed order.
 #include "common.h"
@@ -60,6 +62,7 @@ struct StreamProblem {
     const uint16_t *scale;
     uint16_t *y;
     int N, K;
+    int group;  // 0 (per channel) or the group size
     int rb;     // 16-channel blocks per workgroup
     int kp;     // K parts (waves) per block, rb * kp <= kWaves
     int spart;  // slabs per K part (<= kMaxS)
@@ -79,9 +82,14 @@ struct StreamBatch {
 };
 
 // LDS per wave: two x buffers of M*256 elements, then (group-scaled) the
-// scales of the wave's 2*kMaxS groups x 16 channels.
+// scales of the wave's GC*kMaxS column groups x 16 channels (GC: B columns
+// per token, gemv_cols of the group size).
 constexpr int kXBufElems = kGemvStreamMaxM * 256;
-constexpr int kWaveLdsElems = 2 * kXBufElems + 2 * kMaxS * 16;
+template <int GC>
+constexpr int wave_lds_elems()
+{
+    return 2 * kXBufElems + GC * kMaxS * 16;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -106,12 +114,13 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f3
 struct WaveCtx {
     __amdgpu_buffer_rsrc_t xr, wr, sr;
     int K, ngroups;
+    int gsh;       // GC = 2 with groups: column group (128 K) -> scale index shift
     int s_begin;   // first slab of the part
     int woff;      // this lane's byte offset of slab 0 in the block resource
     int lane, g, tok, par;
     bool b_lane;
     uint16_t *xbuf;  // this wave's two x buffers
-    uint16_t *sbuf;  // this wave's group scales [2*kMaxS][16]
+    uint16_t *sbuf;  // this wave's group scales [GC*kMaxS][16]
     int srow_off;    // grouped: scale offset (bytes) of this lane's row, group 0; < 0: none
 };
 
@@ -154,20 +163,21 @@ __device__ __forceinline__ XPiece<MT> x_piece_load(const WaveCtx &c, int s)
 }
 
 // Run a K part of exactly S slabs; returns this lane's fp32 accumulator
-// (C rows 4g..4g+3 of the block, column 2*tok + par).
-template <bool FP16, bool GROUPED, int MT, int S>
+// (C rows 4g..4g+3 of the block, column GC*tok + par).
+template <bool FP16, bool GROUPED, int GC, int MT, int S>
 __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
 {
     // ---- issue every load of the part: scales, then (x, codes) per slab ----
-    constexpr int kSL = GROUPED ? (2 * S + 3) / 4 : 0;  // scale loads per lane
+    constexpr int kSL = GROUPED ? (GC * S + 3) / 4 : 0;  // scale loads per lane
     uint32_t sv[kSL > 0 ? kSL : 1];
 #pragma unroll
     for (int j = 0; j < kSL; ++j) {
-        // lane l: row l & 15, local group (l >> 4) + 4j of the part's 2S groups
+        // lane l: row l & 15, local column group (l >> 4) + 4j of the part's
+        // GC*S; its scale is that of group gr (of half slab gr when GC = 2)
         const int lg = (c.lane >> 4) + 4 * j;
-        const int gr = 2 * c.s_begin + lg;
-        const int off = (c.srow_off >= 0 && lg < 2 * S && gr < c.ngroups) ? c.srow_off + gr * 2
-                                                                          : kOOB;
+        const int gr = (GC * c.s_begin + lg) >> (GC == 2 ? c.gsh : 0);
+        const int off = (c.srow_off >= 0 && lg < GC * S && gr < c.ngroups) ? c.srow_off + gr * 2
+                                                                           : kOOB;
         sv[j] = __builtin_amdgcn_raw_buffer_load_b16(c.sr, off, 0, 0);
     }
     XPiece<MT> xv[S];
@@ -183,14 +193,16 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
 #pragma unroll
     for (int j = 0; j < kSL; ++j) {
         const int lg = (c.lane >> 4) + 4 * j;
-        if (lg < 2 * S)
+        if (lg < GC * S)
             c.sbuf[lg * 16 + (c.lane & 15)] = (uint16_t)sv[j];
     }
     x_piece_store<MT>(c, 0, xv[0]);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // B operand pieces: lanes without real B entries keep zeros throughout.
-    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
+    // B operand pieces: lanes without real B entries keep zeros throughout
+    // (GC = 8: every lane rewrites both, the 32-groups change with d).
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    uint4 b0 = zero4, b1 = zero4;
 #pragma unroll
     for (int i = 0; i < S; ++i) {
         // the next slab's x goes into the other buffer while this slab runs
@@ -203,7 +215,15 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
         f32x4_t part = GROUPED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            if (c.b_lane) {
+            if constexpr (GC == 8) {
+                if (c.b_lane && c.par == 2 * c.g + (d >> 1)) {
+                    b0 = xb[2 * d];
+                    b1 = xb[2 * d + 1];
+                } else {
+                    b0 = zero4;
+                    b1 = zero4;
+                }
+            } else if (c.b_lane) {
                 b0 = xb[2 * d];
                 b1 = xb[2 * d + 1];
             }
@@ -213,10 +233,10 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
             part = mfma16x16x32<FP16>(a + 4, b1, part);
         }
         if constexpr (GROUPED) {
-            // C rows of this lane: channels 4g + r of the block; group 2i + par
-            // of the part (scales past K or N were loaded as zeros).
+            // C rows of this lane: channels 4g + r of the block; column group
+            // GC*i + par of the part (scales past K or N were loaded as zeros).
             const uint2 s4 =
-                *reinterpret_cast<const uint2 *>(c.sbuf + (2 * i + c.par) * 16 + 4 * c.g);
+                *reinterpret_cast<const uint2 *>(c.sbuf + (GC * i + c.par) * 16 + 4 * c.g);
             acc[0] += f16_bits_to_f32((uint16_t)s4.x) * part[0];
             acc[1] += f16_bits_to_f32((uint16_t)(s4.x >> 16)) * part[1];
             acc[2] += f16_bits_to_f32((uint16_t)s4.y) * part[2];
@@ -235,28 +255,31 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c)
 // the longer parts' loads need more registers than 8 waves per SIMD allow.
 constexpr int kShortS = 6;
 
-template <bool FP16, bool GROUPED, int MT, bool LONG>
+template <bool FP16, bool GROUPED, int GC, int MT, bool LONG>
 __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int S)
 {
     if constexpr (LONG) {
         if (S == 7)
-            return run_part<FP16, GROUPED, MT, 7>(c);
+            return run_part<FP16, GROUPED, GC, MT, 7>(c);
         if (S == 8)
-            return run_part<FP16, GROUPED, MT, 8>(c);
+            return run_part<FP16, GROUPED, GC, MT, 8>(c);
     }
     switch (S) {
-    case 1: return run_part<FP16, GROUPED, MT, 1>(c);
-    case 2: return run_part<FP16, GROUPED, MT, 2>(c);
-    case 3: return run_part<FP16, GROUPED, MT, 3>(c);
-    case 4: return run_part<FP16, GROUPED, MT, 4>(c);
-    case 5: return run_part<FP16, GROUPED, MT, 5>(c);
-    case 6: return run_part<FP16, GROUPED, MT, 6>(c);
+    case 1: return run_part<FP16, GROUPED, GC, MT, 1>(c);
+    case 2: return run_part<FP16, GROUPED, GC, MT, 2>(c);
+    case 3: return run_part<FP16, GROUPED, GC, MT, 3>(c);
+    case 4: return run_part<FP16, GROUPED, GC, MT, 4>(c);
+    case 5: return run_part<FP16, GROUPED, GC, MT, 5>(c);
+    case 6: return run_part<FP16, GROUPED, GC, MT, 6>(c);
     default: return f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
 static_assert(kMaxS == 8 && kShortS == 6, "run_part_n covers S = 1..kMaxS");
 
-template <bool FP16, bool GROUPED, int MT, bool LONG>
+// GC: B columns per token (gemv_cols of the group size: 2 for per-channel
+// scales and groups of 128 K or more, 4 for 64, 8 for 32); column GC*t + p
+// holds token t restricted to group p of each slab (half p when GC = 2).
+template <bool FP16, bool GROUPED, int GC, int MT, bool LONG>
 
 __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch batch)
 {
@@ -281,18 +304,22 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
     const bool active = kpi < KP;        // waves past RB*KP hold no part
     const int rb = ((int)blockIdx.x - P.unit0) * RB + rbi;
     const int nslabs = (K + 255) >> 8;
-    const int ngroups = K >> 7;
+    const int glog = GROUPED ? 31 - __builtin_clz((unsigned)P.group) : 7;
+    const int ngroups = K >> glog;
     const int rowbytes = K >> 2;
 
     WaveCtx c;
     c.K = K;
     c.ngroups = ngroups;
+    c.gsh = glog >= 7 ? glog - 7 : 0;
     c.lane = lane;
     c.g = lane >> 4;                // lane group: which 64-code quarter of a slab
     const int col = lane & 15;      // A row / B column / C column of this lane
-    c.tok = col >> 1;               // token of this B column
-    c.par = col & 1;                // 128-group of the slab this column collects
-    c.b_lane = c.tok < M && (c.g >> 1) == c.par;
+    c.tok = col / GC;               // token of this B column
+    c.par = col % GC;               // column group of the slab this column collects
+    // Lane group g holds codes 64g .. 64g+63 of a slab, word d of them codes
+    // 64g + 16d .. +15: in half g/2, in 64-group g, in 32-group 2g + d/2.
+    c.b_lane = c.tok < M && (GC == 2 ? (c.g >> 1) == c.par : (GC == 4 ? c.g == c.par : true));
     c.s_begin = kpi * P.spart;
     const int S = active ? min(P.spart, nslabs - c.s_begin) : 0;
     // (readfirstlane: the clamp lowers to a vector op, and a descriptor in
@@ -304,7 +331,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
     c.xr = make_rsrc(P.x, (uint32_t)M * (uint32_t)K * 2u);
     c.sr = make_rsrc(P.scale, (uint32_t)N * (uint32_t)(GROUPED ? ngroups : 1) * 2u);
     c.srow_off = (lane & 15) < nrows ? (rb * 16 + (lane & 15)) * ngroups * 2 : -1;
-    uint16_t *wlds = reinterpret_cast<uint16_t *>(smem) + wave * kWaveLdsElems;
+    uint16_t *wlds = reinterpret_cast<uint16_t *>(smem) + wave * wave_lds_elems<GC>();
     c.xbuf = wlds;
     c.sbuf = wlds + 2 * kXBufElems;
 
@@ -321,7 +348,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (S > 0)
-        acc = run_part_n<FP16, GROUPED, MT, LONG>(c, S);
+        acc = run_part_n<FP16, GROUPED, GC, MT, LONG>(c, S);
 
     // ---- K-part reduction (fixed order) and epilogue ------------------------
     f32x4_t sum = acc;
@@ -346,7 +373,12 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
     uint16_t *__restrict__ y = P.y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float tot = sum[r] + __shfl_xor(sum[r], 1);
+        // the GC columns of a token (adjacent lanes) hold disjoint K sets
+        float tot = sum[r] + __shfl_xor(sum[r], 1);
+        if constexpr (GC >= 4)
+            tot += __shfl_xor(tot, 2);
+        if constexpr (GC >= 8)
+            tot += __shfl_xor(tot, 4);
         const int ch = rb * 16 + 4 * c.g + r;
         float o = 0.5f * tot;  // decoded weights are +-2
         if constexpr (!GROUPED)
@@ -358,8 +390,11 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
 
 // LDS bytes of a workgroup: the per-wave buffers, or the K-part reduction
 // area if larger.
-constexpr size_t kLdsBytes = std::max<size_t>((size_t)kWaves * kWaveLdsElems * 2,
-                                              (size_t)kWaves * 64 * 16);
+template <int GC>
+constexpr size_t lds_bytes()
+{
+    return std::max<size_t>((size_t)kWaves * wave_lds_elems<GC>() * 2, (size_t)kWaves * 64 * 16);
+}
 
 // K split of one problem: parts of about `target` slabs, at most kMaxS, on at
 // most kWaves waves per block.  Returns false when this kernel cannot take it.
@@ -378,67 +413,83 @@ bool split_k(int M, int K, int target, int &kp, int &spart)
 
 }  // namespace
 
-bool gemv_stream_takes(int64_t M, int64_t K, bool grouped)
+bool gemv_stream_takes(int64_t M, int64_t K, int group)
 {
-    (void)grouped;
     int kp = 0, spart = 0;
-    return K % 128 == 0 && K <= kGemvMaxK && split_k((int)M, (int)K, 2, kp, spart);
+    return K % 128 == 0 && K <= kGemvMaxK && M * gemv_cols(group) <= 16 &&
+           (group == 0 || K % group == 0) && split_k((int)M, (int)K, 2, kp, spart);
 }
 
 namespace {
-template <bool FP16, bool GROUPED>
+template <bool FP16, bool GROUPED, int GC>
 void launch_m(int mt, bool long_parts, dim3 grid, dim3 block, hipStream_t stream,
               const StreamBatch &b)
 {
+    constexpr size_t lds = lds_bytes<GC>();
     if (long_parts) {
         if (mt == 1)
-            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1, true>), grid, block, kLdsBytes,
+            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 1, true>), grid, block, lds,
                                stream, b);
         else
-            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2, true>), grid, block, kLdsBytes,
+            hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 2, true>), grid, block, lds,
                                stream, b);
     } else if (mt == 1) {
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 1, false>), grid, block, kLdsBytes,
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 1, false>), grid, block, lds,
                            stream, b);
     } else {
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, 2, false>), grid, block, kLdsBytes,
+        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 2, false>), grid, block, lds,
                            stream, b);
     }
 }
-}  // namespace
 
-namespace {
+template <bool FP16>
+void launch_group(int group, int mt, bool long_parts, dim3 grid, dim3 block, hipStream_t stream,
+                  const StreamBatch &b)
+{
+    if (group == 0)
+        launch_m<FP16, false, 2>(mt, long_parts, grid, block, stream, b);
+    else if (group == 32)
+        launch_m<FP16, true, 8>(mt, long_parts, grid, block, stream, b);
+    else if (group == 64)
+        launch_m<FP16, true, 4>(mt, long_parts, grid, block, stream, b);
+    else
+        launch_m<FP16, true, 2>(mt, long_parts, grid, block, stream, b);
+}
+
+template <bool GROUPED, int GC>
+int occupancy(int mt, bool long_parts)
+{
+    const void *k = long_parts
+                        ? (mt == 1 ? (const void *)gemv_stream_kernel<false, GROUPED, GC, 1, true>
+                                   : (const void *)gemv_stream_kernel<false, GROUPED, GC, 2, true>)
+                        : (mt == 1 ? (const void *)gemv_stream_kernel<false, GROUPED, GC, 1, false>
+                                   : (const void *)gemv_stream_kernel<false, GROUPED, GC, 2, false>);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, lds_bytes<GC>()) !=
+            hipSuccess ||
+        n < 1)
+        n = 1;
+    return n;
+}
 
 // Workgroups of one kernel instance that fit on a CU (cached).
-int stream_slots_per_cu(int mt, bool long_parts, bool grouped)
+int stream_slots_per_cu(int mt, bool long_parts, int group)
 {
-    static int cache[2][2][2] = {};
-    int &v = cache[mt - 1][long_parts][grouped];
-    if (v == 0) {
-        const void *k = nullptr;
-        if (grouped)
-            k = long_parts ? (mt == 1 ? (const void *)gemv_stream_kernel<false, true, 1, true>
-                                      : (const void *)gemv_stream_kernel<false, true, 2, true>)
-                           : (mt == 1 ? (const void *)gemv_stream_kernel<false, true, 1, false>
-                                      : (const void *)gemv_stream_kernel<false, true, 2, false>);
-        else
-            k = long_parts ? (mt == 1 ? (const void *)gemv_stream_kernel<false, false, 1, true>
-                                      : (const void *)gemv_stream_kernel<false, false, 2, true>)
-                           : (mt == 1 ? (const void *)gemv_stream_kernel<false, false, 1, false>
-                                      : (const void *)gemv_stream_kernel<false, false, 2, false>);
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, kLdsBytes) != hipSuccess ||
-            n < 1)
-            n = 1;
-        v = n;
-    }
+    const int gi = group == 0 ? 0 : (group == 32 ? 1 : (group == 64 ? 2 : 3));
+    static int cache[2][2][4] = {};
+    int &v = cache[mt - 1][long_parts][gi];
+    if (v == 0)
+        v = gi == 0   ? occupancy<false, 2>(mt, long_parts)
+            : gi == 1 ? occupancy<true, 8>(mt, long_parts)
+            : gi == 2 ? occupancy<true, 4>(mt, long_parts)
+                      : occupancy<true, 2>(mt, long_parts);
     return v;
 }
 
 }  // namespace
 
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
-                              bool grouped, hipStream_t stream)
+                              int group, hipStream_t stream)
 {
     // The part length (slabs per wave) of the whole batch, a function of the
     // batch only (so deterministic): 4 slabs, or 2 when 4 leaves fewer than
@@ -461,7 +512,7 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             if (a.M == 0 || a.N == 0)
                 continue;
             StreamProblem &p = b.p[b.count];
-            if (a.grouped != grouped || (mt != 0 && a.M != mt) ||
+            if (a.group != group || (mt != 0 && a.M != mt) ||
                 !split_k(a.M, a.K, target, p.kp, p.spart))
                 return false;
             mt = a.M;
@@ -471,6 +522,7 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             p.y = a.y;
             p.N = a.N;
             p.K = a.K;
+            p.group = group;
             const int nblocks = (a.N + 15) / 16;
             p.rb = std::min(kWaves / p.kp, nblocks);
             p.rbi_map = 0;
@@ -497,7 +549,7 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             return hipErrorInvalidValue;
     }
     if (b.count > 0 && max_spart <= kShortS) {
-        const int slots = device_cus() * stream_slots_per_cu(mt, false, grouped);
+        const int slots = device_cus() * stream_slots_per_cu(mt, false, group);
         const int rounds = (units + slots - 1) / slots;
         if (rounds > 1 && units - (rounds - 1) * slots < slots / 4) {
             int pick = 0;
@@ -515,17 +567,10 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
     for (int i = 0; i < b.count; ++i)
         long_parts = long_parts || b.p[i].spart > kShortS;
     const dim3 grid(units), block(kThreads);
-    if (fp16) {
-        if (grouped)
-            launch_m<true, true>(mt, long_parts, grid, block, stream, b);
-        else
-            launch_m<true, false>(mt, long_parts, grid, block, stream, b);
-    } else {
-        if (grouped)
-            launch_m<false, true>(mt, long_parts, grid, block, stream, b);
-        else
-            launch_m<false, false>(mt, long_parts, grid, block, stream, b);
-    }
+    if (fp16)
+        launch_group<true>(group, mt, long_parts, grid, block, stream, b);
+    else
+        launch_group<false>(group, mt, long_parts, grid, block, stream, b);
     return hipGetLastError();
 }
 

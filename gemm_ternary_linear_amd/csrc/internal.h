@@ -11,6 +11,19 @@ constexpr int kGemvMaxM = 8;
 // Most projections one fused decode launch takes.
 constexpr int kGemvMaxBatch = 8;
 
+// Scale granularity of a problem: 0 = one scale per output channel, else the
+// group size along K (32, 64, 128 or 256; scales [N, K/group]).
+inline bool group_valid(int64_t group)
+{
+    return group == 0 || group == 32 || group == 64 || group == 128 || group == 256;
+}
+inline int group_log2(int group) { return 31 - __builtin_clz((unsigned)group); }
+
+// The decode GEMVs hand each token GEMV_COLS MFMA B columns, one per group of
+// a 256-code slab (two halves for per-channel scales and groups of 128 or
+// more), so a token takes 2, 4 or 8 of the 16 columns.
+constexpr int gemv_cols(int group) { return group == 32 ? 8 : (group == 64 ? 4 : 2); }
+
 // One decode GEMV problem (shapes already validated).
 struct GemvArgs {
     const uint16_t *x;
@@ -18,7 +31,7 @@ struct GemvArgs {
     const uint16_t *scale;
     uint16_t *y;
     int M, N, K;
-    bool grouped;
+    int group;  // 0 (per channel) or the group size
 };
 
 hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,
@@ -26,25 +39,25 @@ hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t
 hipError_t launch_unpack(const uint8_t *packed, int64_t nbytes, int8_t *q, hipStream_t stream);
 
 // All linear launchers: x/y are 2-byte elements (bf16 or fp16 by `fp16`),
-// group_size is -1 or 128, shapes already validated by the caller.
+// `group` as in GemvArgs, shapes already validated by the caller.
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 // Up to kGemvMaxBatch decode problems in one launch (all gemv_takes()).
 hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream);
 // Largest M the streaming decode kernel takes.
 constexpr int kGemvStreamMaxM = 2;
 // Whether the streaming decode kernel takes a gemv_takes() shape.
-bool gemv_stream_takes(int64_t M, int64_t K, bool grouped);
-// The problems args[order[0..count)] (all gemv_stream_takes(), one scale mode,
-// one M) in one launch of the streaming decode kernel.
+bool gemv_stream_takes(int64_t M, int64_t K, int group);
+// The problems args[order[0..count)] (all gemv_stream_takes(), one group
+// value, one M) in one launch of the streaming decode kernel.
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
-                              bool grouped, hipStream_t stream);
+                              int group, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 // Whether the pipelined (grouped) prefill kernel takes a problem.
-bool gemm_big_takes(int M, int N, int K, bool grouped, const void *scale);
+bool gemm_big_takes(int M, int N, int K, int group, const void *scale);
 // Up to kGemvMaxBatch prefill problems (all gemm_big_takes()) in one grouped
 // launch per scale mode (plus one reduce launch per problem whose K range is
 // split).
@@ -59,24 +72,30 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void **out);
 hipError_t release_workspaces();
 
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                         const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream);
+                         const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 
 // Shape requirements of the fast kernels.
-// The GEMV stages a workgroup's group scales (K/4 bytes) in LDS, so K is capped.
+// The GEMV stages a workgroup's group scales in LDS, so K (and the number of
+// groups per row) is capped; a token's B columns times M fit the 16 columns.
 constexpr int64_t kGemvMaxK = 65536;
-inline bool gemv_takes(int64_t M, int64_t K)
+constexpr int64_t kGemvMaxGroups = 512;
+inline bool gemv_takes(int64_t M, int64_t K, int group)
 {
-    return M >= 1 && M <= kGemvMaxM && K % 128 == 0 && K <= kGemvMaxK;
+    return M >= 1 && M <= kGemvMaxM && M * gemv_cols(group) <= 16 && K % 128 == 0 &&
+           K <= kGemvMaxK && (group == 0 || (K % group == 0 && K / group <= kGemvMaxGroups));
 }
-inline bool gemm_takes(int64_t M, int64_t K) { return M >= 1 && K % 128 == 0; }
+inline bool gemm_takes(int64_t M, int64_t K, int group)
+{
+    return M >= 1 && K % 128 == 0 && (group == 0 || K % group == 0);
+}
 // The automatic choice: the decode GEMV wherever it takes the shape, except
 // that from M = 4 on a K of 16384 or more (a multiple of 256) runs faster on
 // the pipelined GEMM, because the GEMV reads all of x once per 16-channel
 // block (measured: 7B down at M = 8, 23.7 vs 42.6 us; 27B down at M = 4, 50
 // vs 77 us; shorter K keeps the GEMV ahead).
-inline bool gemv_preferred(int64_t M, int64_t K)
+inline bool gemv_preferred(int64_t M, int64_t K, int group)
 {
-    return gemv_takes(M, K) && !(M >= 4 && K >= 16384 && K % 256 == 0);
+    return gemv_takes(M, K, group) && !(M >= 4 && K >= 16384 && K % 256 == 0);
 }
 
 }  // namespace ternary

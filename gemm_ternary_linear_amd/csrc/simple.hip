@@ -6,7 +6,8 @@
 // +x for code 01, -x for code 10, nothing for 00 and the reserved 11
 // ([nxbn] m.nxbn.cn/news/169761 §4.1; code table [trdm] trdm.cn
 // "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §3.1), with the sum kept
-// in fp32 partials of 128 K so no fp32 chain grows longer than 128 + K/128.
+// in fp32 partials of 128 K (of one group when groups are shorter) so no
+// fp32 chain grows longer than 128 + K/32.
 #include "common.h"
 #include "internal.h"
 
@@ -24,21 +25,24 @@ __device__ __forceinline__ float load_act(const uint16_t *p)
         return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// glog: log2 of the group size (group-scaled instances).
 template <bool FP16, bool GROUPED>
 __global__ void __launch_bounds__(256)
     simple_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                  const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N, int K)
+                  const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int M, int N, int K,
+                  int glog)
 {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N)
         return;
     const uint8_t *prow = packed + (int64_t)n * (K >> 2);
-    const int ngroups = GROUPED ? K >> 7 : 1;
+    const int ngroups = GROUPED ? K >> glog : 1;
+    const int plen = GROUPED && glog < 7 ? 1 << glog : 128;  // K of one fp32 partial
     for (int m = blockIdx.y; m < M; m += gridDim.y) {
     const uint16_t *xrow = x + (int64_t)m * K;
     float acc = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 128) {
-        const int k1 = k0 + 128 < K ? k0 + 128 : K;
+    for (int k0 = 0; k0 < K; k0 += plen) {
+        const int k1 = k0 + plen < K ? k0 + plen : K;
         float part = 0.f;
         for (int k = k0; k < k1; k += 4) {
             const uint32_t byte = prow[k >> 2];
@@ -50,7 +54,7 @@ __global__ void __launch_bounds__(256)
             }
         }
         if constexpr (GROUPED)
-            acc += f16_bits_to_f32(scale[(int64_t)n * ngroups + (k0 >> 7)]) * part;
+            acc += f16_bits_to_f32(scale[(int64_t)n * ngroups + (k0 >> glog)]) * part;
         else
             acc += part;
     }
@@ -62,24 +66,25 @@ __global__ void __launch_bounds__(256)
 
 template <bool FP16, bool GROUPED>
 hipError_t launch_simple_t(const uint16_t *x, int M, int N, int K, const uint8_t *packed,
-                           const uint16_t *scale, uint16_t *y, hipStream_t stream)
+                           const uint16_t *scale, int glog, uint16_t *y, hipStream_t stream)
 {
     const dim3 grid((N + 255) / 256, M < 65535 ? M : 65535);
     hipLaunchKernelGGL((simple_kernel<FP16, GROUPED>), grid, dim3(256), 0, stream, x, packed,
-                       scale, y, M, N, K);
+                       scale, y, M, N, K, glog);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                         const uint16_t *scale, bool grouped, uint16_t *y, hipStream_t stream)
+                         const uint16_t *scale, int group, uint16_t *y, hipStream_t stream)
 {
+    const int glog = group ? group_log2(group) : 0;
     if (fp16)
-        return grouped ? launch_simple_t<true, true>(x, M, N, K, packed, scale, y, stream)
-                       : launch_simple_t<true, false>(x, M, N, K, packed, scale, y, stream);
-    return grouped ? launch_simple_t<false, true>(x, M, N, K, packed, scale, y, stream)
-                   : launch_simple_t<false, false>(x, M, N, K, packed, scale, y, stream);
+        return group ? launch_simple_t<true, true>(x, M, N, K, packed, scale, glog, y, stream)
+                     : launch_simple_t<true, false>(x, M, N, K, packed, scale, 0, y, stream);
+    return group ? launch_simple_t<false, true>(x, M, N, K, packed, scale, glog, y, stream)
+                 : launch_simple_t<false, false>(x, M, N, K, packed, scale, 0, y, stream);
 }
 
 }  // namespace ternary

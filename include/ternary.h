@@ -10,10 +10,11 @@
  *          §2.2 code table and bit order; §3.2 per-channel scale broadcast
  *          over rows; §5.2 the layer's forward takes (x, weight, scale).
  *   [xxqk] m.xxqk.cn/news/593501 (Bonsai 2 27B into vLLM): §4.3 the layer is
- *          dequantise-then-matmul.
+ *          dequantise-then-matmul; §4.2/§5.2 checkpoints grouped by 64.
  *   [ch13] yangyitao.com vLLM book, "第13章 量化：精度与速度的工程平衡":
- *          §13.3 scale granularity (per channel, per group); §13.8.2
- *          group_size = -1 means one group per row.
+ *          §13.3 scale granularity (per channel, per group; §13.3.3 group
+ *          sizes 128, 32, 256); §13.8.2 group_size = -1 means one group per
+ *          row.
  *
  * Format (fixed by [trdm §3.1] and [nxbn §2.2]):
  *   - each weight is a 2-bit code: 00 -> 0, 01 -> +1, 10 -> -1, 11 -> reserved,
@@ -23,8 +24,9 @@
  *   - packed weights are [N, K/4] bytes, row-major (one row per output channel,
  *     K contiguous);
  *   - scales are IEEE binary16 bit patterns: [N] when group_size == -1 (one per
- *     output channel, [nxbn §3.2]) or [N, K/128] row-major when group_size ==
- *     128 (128 consecutive K weights of a row share one, [trdm §3.1]).
+ *     output channel, [nxbn §3.2]) or [N, K/g] row-major when group_size == g
+ *     (g consecutive K weights of a row share one: g = 128 in [trdm §3.1], 64
+ *     in [xxqk §4.2], 32 and 256 in [ch13 §13.3.3]).
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers, owned by the caller.  The library
@@ -60,7 +62,7 @@ typedef enum {
     TERNARY_OK = 0,
     TERNARY_ERR_NULL = -1,   /* a required pointer is NULL                       */
     TERNARY_ERR_SHAPE = -2,  /* negative size, K % 4 != 0, K % group != 0, ...   */
-    TERNARY_ERR_GROUP = -3,  /* group_size is neither -1 nor 128                 */
+    TERNARY_ERR_GROUP = -3,  /* group_size is not -1, 32, 64, 128 or 256         */
     TERNARY_ERR_DTYPE = -4,  /* activation dtype is not TERNARY_BF16/TERNARY_FP16*/
     TERNARY_ERR_ALIGN = -5,  /* a pointer is not aligned as documented           */
     TERNARY_ERR_ALIAS = -6,  /* the output overlaps an input                     */
@@ -106,12 +108,13 @@ int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipSt
  *   x           [M, K] activations, dtype `dtype`, row-major contiguous
  *               ([trdm §4.4]: callers flatten leading dims to M), 16-byte aligned.
  *   dtype       TERNARY_BF16 or TERNARY_FP16; y has the same dtype.
- *   M, N, K     M >= 0, N >= 0, K > 0, K % 4 == 0; K % 128 == 0 when grouped.
- *               M == 0 or N == 0 is a successful no-op.
+ *   M, N, K     M >= 0, N >= 0, K > 0, K % 4 == 0; K % group_size == 0 when
+ *               grouped.  M == 0 or N == 0 is a successful no-op.
  *   packed      uint8 [N, K/4] codes as above, 16-byte aligned.
- *   scale       fp16 bit patterns, [N] (group_size == -1) or [N, K/128]
- *               (group_size == 128), 2-byte aligned.
- *   group_size  -1 (per output channel) or 128 ([ch13 §13.8.2] convention).
+ *   scale       fp16 bit patterns, [N] (group_size == -1) or [N, K/group_size]
+ *               (grouped), 2-byte aligned.
+ *   group_size  -1 (per output channel, [ch13 §13.8.2] convention) or the
+ *               group size: 32, 64, 128 or 256.
  *   y           [M, N] output, 16-byte aligned, must not overlap any input.
  * Products are formed exactly and accumulated in fp32; the scale multiplies
  * each group's (or the row's) fp32 partial sum; y is rounded from fp32 to the
@@ -120,7 +123,10 @@ int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipSt
  * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (except M >= 4
  * with K >= 16384, K % 256 == 0, which runs faster on the GEMM), larger M the
  * MFMA GEMM; shapes neither fast kernel takes (K % 128 != 0) run the plain
- * kernel.  Results of different paths agree within the bound
+ * kernel.  The GEMV gives each token 2 MFMA columns (per channel, groups of
+ * 128 or 256), 4 (groups of 64) or 8 (groups of 32) of 16, so it takes M <= 4
+ * for groups of 64 and M <= 2 for groups of 32, and at most 512 groups per
+ * row; the GEMM runs the rest.  Results of different paths agree within the bound
  * |y - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6, not bitwise.
  */
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
@@ -141,10 +147,10 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
 typedef struct {
     const void *x;          /* [M, K] activations, 16-byte aligned                  */
     const uint8_t *packed;  /* [N, K/4] codes, 16-byte aligned                      */
-    const uint16_t *scale;  /* fp16 [N] or [N, K/128], 2-byte aligned               */
+    const uint16_t *scale;  /* fp16 [N] or [N, K/group_size], 2-byte aligned        */
     void *y;                /* [M, N] output, 16-byte aligned                       */
     int64_t M, N, K;        /* as for ternary_linear                                */
-    int64_t group_size;     /* -1 or 128                                            */
+    int64_t group_size;     /* -1, 32, 64, 128 or 256                               */
 } ternary_problem;
 
 /*
@@ -159,10 +165,11 @@ typedef struct {
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
  * any error nothing is launched.  Problems the automatic path sends to the
  * decode GEMV (see ternary_linear) run together in one launch per scale
- * mode (per-channel, group-128) and kernel class (M <= 2, larger M);
- * per-channel prefill problems with M >= 256, N >= 256 and K % 256 == 0 run
- * together in one grouped GEMM launch (longest K first); the others run as
- * separate launches on the same stream.  Results are
+ * mode (per channel, or each group size) and kernel class (M <= 2, larger M);
+ * the GEMM problems the pipelined kernel takes (K % 256 == 0; group sizes 64,
+ * 128 or 256 with an even number of groups per row and 4-byte-aligned scales)
+ * run together in one grouped GEMM launch per scale mode and tile shape
+ * (longest K first); the others run as separate launches on the same stream.  Results are
  * deterministic (the same batch gives the same bits) and each satisfies the
  * bound of ternary_linear; they may differ from a single ternary_linear call on
  * the same problem in the last bits, because a batch may split a problem's K

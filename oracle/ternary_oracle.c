@@ -20,7 +20,12 @@
  *           with one fp16 scale per output channel; §4.2 applies the scale to
  *           the finished accumulator.
  *   [xxqk]  m.xxqk.cn/news/593501 (Bonsai 2 27B into vLLM): §4.3 defines the
- *           layer as dequantise-then-matmul, y = x @ (unpack(q) * s)^T.
+ *           layer as dequantise-then-matmul, y = x @ (unpack(q) * s)^T; §4.2
+ *           and §5.2 meet checkpoints whose groups are 64 weights (and the
+ *           garbage that reading them as 128 gives).
+ *   [ch13]  yangyitao.com vLLM book, chapter 13 (quantization): §13.3.3
+ *           per-group scales, group_size 128 the usual default, 32 and 256
+ *           the finer and coarser alternatives.
  *
  * The oracle evaluates exactly that definition in fp64: each product of a
  * bf16/fp16 activation, a ternary value and an fp16 scale is exact in fp64,
@@ -29,7 +34,9 @@
  * Readings where the pages are silent or garbled (also listed in the design doc):
  *   - code 11 decodes to 0 (reserved on [trdm], unused on [nxbn]);
  *   - pack writes 00 for any value outside {-1,0,1} and counts it;
- *   - scale layout is [N] for per-channel, [N, K/128] row-major for groups;
+ *   - scale layout is [N] for per-channel, [N, K/g] row-major for groups of
+ *     g consecutive K weights (any g dividing K; the GPU library takes 32,
+ *     64, 128 and 256);
  *   - the tolerance bound uses B = sum_k |x_k| * |s(n,k)|.
  * Parity for every function below is pinned by tests that do not re-use it
  * (see tests/test_oracle_pins.py).
@@ -148,7 +155,8 @@ static double x_at(const uint16_t *x, int x_fp16, int64_t K, int64_t m, int64_t 
 }
 
 /* s(n,k): one scale per output channel (group_size == -1, [nxbn §3.2]) or one
- * per 128 consecutive K weights of a row ([trdm §3.1], layout [N, K/128]). */
+ * per group_size consecutive K weights of a row ([trdm §3.1] with 128,
+ * [xxqk §4.2] with 64, [ch13 §13.3.3]; layout [N, K/group_size]). */
 static double s_at(const uint16_t *scale, int64_t K, int64_t group_size, int64_t n, int64_t k)
 {
     if (group_size < 0)

@@ -133,32 +133,37 @@ def _ints_bf16(rng, M, K, lo=-8, hi=9):
     return xi, f64_to_bf16_bits(xi)
 
 
+GROUPS = (32, 64, 128, 256)  # group sizes the GPU library takes
+
+
 def pin_linear_all_zero(o):
     rng = np.random.default_rng(7)
     M, N, K = 3, 5, 256
     _, x = _ints_bf16(rng, M, K)
-    s = f64_to_f16_bits(rng.uniform(0.01, 0.05, size=(N, K // 128)))
-    for packed in (_pack_const(o, N, K, 0), np.full((N, K // 4), 0xff, np.uint8)):
-        y, b = o.linear(x, packed, s, 128)
-        assert np.all(y == 0.0)
-        assert np.all(b > 0.0)
+    for g in GROUPS:
+        s = f64_to_f16_bits(rng.uniform(0.01, 0.05, size=(N, K // g)))
+        for packed in (_pack_const(o, N, K, 0), np.full((N, K // 4), 0xff, np.uint8)):
+            y, b = o.linear(x, packed, s, g)
+            assert np.all(y == 0.0)
+            assert np.all(b > 0.0)
 
 
 def pin_linear_all_plus_minus(o):
     rng = np.random.default_rng(8)
-    M, N, K, g = 3, 6, 384, 128
+    M, N, K = 3, 6, 768
     xi, x = _ints_bf16(rng, M, K)
-    e = rng.integers(-9, -3, size=(N, K // g))
-    sv = np.ldexp(1.0, e)  # powers of two: every partial sum is exact in fp64
-    s = f64_to_f16_bits(sv)
-    # closed form: sum over groups of s[n,g] times the group's sum of x
-    gsum = xi.reshape(M, K // g, g).sum(axis=2)          # [M, G]
-    expect = gsum @ sv.T                                  # [M, N]
-    y, b = o.linear(x, _pack_const(o, N, K, 1), s, g)
-    assert np.array_equal(y, expect)
-    y2, _ = o.linear(x, _pack_const(o, N, K, -1), s, g)
-    assert np.array_equal(y2, -expect)
-    assert np.array_equal(b, np.abs(xi).reshape(M, K // g, g).sum(axis=2) @ sv.T)
+    for g in GROUPS:
+        e = rng.integers(-9, -3, size=(N, K // g))
+        sv = np.ldexp(1.0, e)  # powers of two: every partial sum is exact in fp64
+        s = f64_to_f16_bits(sv)
+        # closed form: sum over groups of s[n,g] times the group's sum of x
+        gsum = xi.reshape(M, K // g, g).sum(axis=2)          # [M, G]
+        expect = gsum @ sv.T                                  # [M, N]
+        y, b = o.linear(x, _pack_const(o, N, K, 1), s, g)
+        assert np.array_equal(y, expect), g
+        y2, _ = o.linear(x, _pack_const(o, N, K, -1), s, g)
+        assert np.array_equal(y2, -expect), g
+        assert np.array_equal(b, np.abs(xi).reshape(M, K // g, g).sum(axis=2) @ sv.T), g
 
 
 def pin_linear_per_channel_all_plus(o):
@@ -172,18 +177,20 @@ def pin_linear_per_channel_all_plus(o):
 
 def pin_linear_one_hot(o):
     rng = np.random.default_rng(10)
-    M, N, K, g = 2, 4, 256, 128
+    M, N, K = 2, 4, 256
     xv = rng.standard_normal((M, K))
     x = f64_to_bf16_bits(xv)
     xd = dense.widen_bf16(x)
-    s = f64_to_f16_bits(rng.uniform(0.005, 0.05, size=(N, K // g)))
-    sd = dense.widen_f16(s)
-    for k0, sign in ((0, 1), (131, -1), (255, 1)):
-        q = np.zeros((N, K), np.int8)
-        q[:, k0] = sign
-        p, _ = o.pack(q)
-        y, _ = o.linear(x, p, s, g)
-        assert np.array_equal(y, sign * np.outer(xd[:, k0], sd[:, k0 // g]))
+    for g in GROUPS:
+        s = f64_to_f16_bits(rng.uniform(0.005, 0.05, size=(N, K // g)))
+        sd = dense.widen_f16(s)
+        for k0, sign in ((0, 1), (31, -1), (32, 1), (131, -1), (255, 1)):
+            q = np.zeros((N, K), np.int8)
+            q[:, k0] = sign
+            p, _ = o.pack(q)
+            y, _ = o.linear(x, p, s, g)
+            # only the scale of the group holding k0 may enter
+            assert np.array_equal(y, sign * np.outer(xd[:, k0], sd[:, k0 // g])), (g, k0)
 
 
 # ---------------------------------------------------------------- linear: invariants
@@ -210,10 +217,33 @@ def pin_equal_groups_equal_per_channel(o):
     rng = np.random.default_rng(12)
     q, sc, x = _random_case(rng, 2, 5, 512, -1)
     p, _ = o.pack(q)
-    sg = np.repeat(sc.reshape(5, 1), 4, axis=1)
-    yg, bg = o.linear(x, p, sg, 128)
     yc, bc = o.linear(x, p, sc, -1)
-    assert np.array_equal(yg, yc) and np.array_equal(bg, bc)
+    for g in GROUPS:
+        sg = np.repeat(sc.reshape(5, 1), 512 // g, axis=1)
+        yg, bg = o.linear(x, p, sg, g)
+        assert np.array_equal(yg, yc) and np.array_equal(bg, bc), g
+
+
+def pin_nested_groups(o):
+    """Scales equal on both halves of every 2g-group give the 2g result: the
+    group index must be k // g, not some other split of the row."""
+    rng = np.random.default_rng(17)
+    q, _, x = _random_case(rng, 3, 6, 1024, -1)
+    p, _ = o.pack(q)
+    for g in GROUPS[:-1]:
+        s2 = f64_to_f16_bits(rng.uniform(0.005, 0.05, size=(6, 1024 // (2 * g))))
+        s1 = np.repeat(s2, 2, axis=1)
+        y1, b1 = o.linear(x, p, s1, g)
+        y2, b2 = o.linear(x, p, s2, 2 * g)
+        assert np.array_equal(y1, y2) and np.array_equal(b1, b2), g
+        # and a different scale on one half changes exactly that half's share
+        s1b = s1.copy()
+        s1b[:, 1] = f64_to_f16_bits(2.0 * dense.widen_f16(s1[:, 1]))
+        y3, _ = o.linear(x, p, s1b, g)
+        qd = q.astype(np.float64)
+        xd = dense.widen_bf16(x)
+        share = xd[:, g:2 * g] @ (qd[:, g:2 * g] * dense.widen_f16(s1[:, 1])[:, None]).T
+        assert np.allclose(y3 - y1, share, rtol=0, atol=1e-12 * (1 + np.abs(b1).max())), g
 
 
 def pin_row_permutation(o):
@@ -251,8 +281,8 @@ def pin_sampled_matches_full(o):
 
 def pin_dense_brute_force(o):
     rng = np.random.default_rng(16)
-    for M, N, K in ((1, 1, 4), (2, 3, 128), (4, 16, 256), (3, 5, 132)):
-        for g in (-1, 128):
+    for M, N, K in ((1, 1, 4), (2, 3, 128), (4, 16, 256), (3, 5, 132), (2, 4, 96)):
+        for g in (-1, 32, 64, 128, 256):
             if g > 0 and K % g:
                 continue
             for dtype in ("bf16", "fp16"):

@@ -63,7 +63,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 2
+    assert tl.abi_version() == 3
     assert tl.gemv_max_m() == 8
     for st in range(0, -9, -1):
         s = tl.status_string(st)
@@ -80,11 +80,15 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=2), -4),
-    (dict(g=64), -3),
+    (dict(g=16), -3),
+    (dict(g=512), -3),
+    (dict(g=96), -3),
     (dict(g=0), -3),
     (dict(K=0), -2),
     (dict(K=130, g=-1), -2),
-    (dict(K=132), -2),           # grouped needs K % 128 == 0
+    (dict(K=132), -2),           # grouped needs K % group == 0
+    (dict(K=160, g=64), -2),
+    (dict(K=384, g=256), -2),
     (dict(M=-1), -2),
     (dict(N=-5), -2),
     (dict(M=1 << 25), -2),
@@ -102,6 +106,10 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(M=9, path=1), -8),                  # GEMV takes M <= 8 only
     (dict(K=132, g=-1, path=1), -8),          # fast kernels need K % 128 == 0
     (dict(K=132, g=-1, path=2), -8),
+    (dict(M=3, K=256, g=32, path=1), -8),     # g = 32 leaves 2 tokens per GEMV launch
+    (dict(M=5, K=256, g=64, path=1), -8),     # g = 64 leaves 4
+    (dict(M=1, K=32768, g=32, path=1), -8),   # the GEMV stages at most 512 groups per row
+    (dict(K=160, g=32, path=2), -8),          # fast kernels need K % 128 == 0
 ])
 def test_linear_rejects(tl, kw, status):
     assert _lin(tl, **kw) == status
@@ -135,6 +143,10 @@ def test_pack_unpack_reject(tl):
     (8, 18944, -1, "gemm"), (4, 25600, 128, "gemm"), (3, 18944, -1, "gemv"),
     (8, 16256, 128, "gemv"),
     (0, 128, 128, "gemv"),
+    # other group sizes: the GEMV takes M * columns-per-token <= 16
+    (2, 4096, 32, "gemv"), (3, 4096, 32, "gemm"), (4, 4096, 64, "gemv"), (5, 4096, 64, "gemm"),
+    (8, 4096, 256, "gemv"), (1, 16384, 32, "gemv"), (1, 32768, 32, "gemm"),
+    (64, 4096, 256, "gemm"), (1, 160, 32, "simple"),
 ])
 def test_select_path(tl, M, K, g, path):
     if M == 0:
@@ -146,7 +158,9 @@ def test_select_path(tl, M, K, g, path):
 def test_select_path_rejects(tl):
     L = tl.lib()
     assert L.ternary_select_path(1, 16, 130, -1) == -2
-    assert L.ternary_select_path(1, 16, 256, 64) == -3
+    assert L.ternary_select_path(1, 16, 256, 16) == -3
+    assert L.ternary_select_path(1, 16, 256, 512) == -3
+    assert L.ternary_select_path(1, 16, 384, 256) == -2
 
 
 def _prob(tl, x, p, s, y, M=1, N=16, K=128, g=128):

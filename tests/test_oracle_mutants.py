@@ -30,6 +30,8 @@ MUTANTS = {
     "group_index_off_by_one": ("k / group_size]);", "(k + 1) / group_size % (K / group_size)]);"),
     "group_scale_transposed": ("scale[n * (K / group_size) + k / group_size]",
                                "scale[(k / group_size) * (K / group_size) + n % (K / group_size)]"),
+    "group_fixed_128": ("scale[n * (K / group_size) + k / group_size]",
+                        "scale[n * (K / group_size) + (k / 128) % (K / group_size)]"),
     "per_channel_first_scale": ("return ternary_oracle_f16_to_f64(scale[n]);",
                                 "return ternary_oracle_f16_to_f64(scale[0]);"),
     "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n                    double xv",
