@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
     "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH", "probe_read", "probe_copy",
-    "probe_mfma", "probe_mfma_flops",
+    "probe_mfma", "probe_mfma_flops", "quantize",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
@@ -38,7 +38,7 @@ PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3}
 EXPORTS = (
     "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
     "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
-    "ternary_status_string", "ternary_abi_version", "ternary_shutdown",
+    "ternary_status_string", "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
 )
 # Every symbol include/ternary_probe.h declares (measurement probes).
 PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_copy", "ternary_probe_mfma")
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
     L.ternary_linear.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, p]
     L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
     L.ternary_linear_batch.argtypes = [p, i32, i32, p]
+    L.ternary_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p]
     L.ternary_select_path.argtypes = [i64, i64, i64, i64]
     L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
     L.ternary_probe_copy.argtypes = [p, p, i64, i32, p]
@@ -85,7 +86,8 @@ def lib() -> ctypes.CDLL:
     L.ternary_status_string.restype = ctypes.c_char_p
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
-               "ternary_abi_version", "ternary_shutdown", *PROBE_EXPORTS):
+               "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
+               *PROBE_EXPORTS):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -172,6 +174,23 @@ def unpack(packed: torch.Tensor, K: int | None = None) -> torch.Tensor:
 
 
 _ACT = {torch.bfloat16: BF16, torch.float16: FP16}
+
+
+def quantize(w: torch.Tensor, group_size: int = 128):
+    """bf16/fp16 weights [N, K] -> (packed uint8 [N, K/4], fp16 scales [N] or
+    [N, K/group_size]) by ternary_quantize: per group s = max|w| (fp16),
+    q = round(w / s) in {-1, 0, +1}."""
+    _dev(w, "w")
+    dt = _ACT.get(w.dtype)
+    if dt is None or w.dim() != 2:
+        raise ValueError("w must be a 2-D bfloat16 or float16 tensor")
+    N, K = w.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    sshape = (N,) if group_size == -1 else (N, K // group_size if group_size > 0 else 0)
+    scale = torch.empty(sshape, dtype=torch.float16, device=w.device)
+    _check(int(lib().ternary_quantize(w.data_ptr(), dt, N, K, group_size, packed.data_ptr(),
+                                      scale.data_ptr(), _stream(w))), "ternary_quantize")
+    return packed, scale
 
 
 def _check_problem(x, packed, scale, group_size, out):

@@ -21,7 +21,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_stream.hip", "gemm.hip", "simple.hip",
-           "workspace.hip", "probe.hip"]
+           "workspace.hip", "probe.hip", "quantize.hip"]
 
 
 def _compile(src: str) -> Path:

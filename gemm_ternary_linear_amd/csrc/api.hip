@@ -153,6 +153,30 @@ int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipSt
     return hip_status(ternary::launch_unpack(packed, nbytes, q, stream));
 }
 
+int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t group_size,
+                     uint8_t *packed, uint16_t *scale, hipStream_t stream)
+{
+    if (dtype != TERNARY_BF16 && dtype != TERNARY_FP16)
+        return TERNARY_ERR_DTYPE;
+    const int sh = check_shape(0, N, K, group_size);
+    if (sh != TERNARY_OK)
+        return sh;
+    if (N == 0)
+        return TERNARY_OK;
+    if (!w || !packed || !scale)
+        return TERNARY_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scale, 2))
+        return TERNARY_ERR_ALIGN;
+    const int64_t wbytes = 2 * N * K, pbytes = N * (K / 4),
+                  sbytes = 2 * scale_elems(N, K, group_size);
+    if (overlap(packed, pbytes, w, wbytes) || overlap(scale, sbytes, w, wbytes) ||
+        overlap(scale, sbytes, packed, pbytes))
+        return TERNARY_ERR_ALIAS;
+    return hip_status(ternary::launch_quantize(static_cast<const uint16_t *>(w),
+                                               dtype == TERNARY_FP16, (int)N, (int)K,
+                                               group_of(group_size), packed, scale, stream));
+}
+
 int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size)
 {
     const int sh = check_shape(M, N, K, group_size);

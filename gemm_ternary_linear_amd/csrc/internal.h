@@ -37,6 +37,9 @@ struct GemvArgs {
 hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,
                        hipStream_t stream);
 hipError_t launch_unpack(const uint8_t *packed, int64_t nbytes, int8_t *q, hipStream_t stream);
+// Codes and scales of 16-bit weights w [N, K] (`group` as in GemvArgs).
+hipError_t launch_quantize(const uint16_t *w, bool fp16, int N, int K, int group, uint8_t *packed,
+                           uint16_t *scale, hipStream_t stream);
 
 // All linear launchers: x/y are 2-byte elements (bf16 or fp16 by `fp16`),
 // `group` as in GemvArgs, shapes already validated by the caller.

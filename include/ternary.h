@@ -12,7 +12,8 @@
  *   [xxqk] m.xxqk.cn/news/593501 (Bonsai 2 27B into vLLM): §4.3 the layer is
  *          dequantise-then-matmul; §4.2/§5.2 checkpoints grouped by 64.
  *   [ch13] yangyitao.com vLLM book, "第13章 量化：精度与速度的工程平衡":
- *          §13.3 scale granularity (per channel, per group; §13.3.3 group
+ *          §13.1.3 symmetric linear quantization; §13.1.4 its s/2 error
+ *          bound; §13.3 scale granularity (per channel, per group; §13.3.3 group
  *          sizes 128, 32, 256); §13.8.2 group_size = -1 means one group per
  *          row.
  *
@@ -102,6 +103,27 @@ int ternary_pack(const int8_t *q, int64_t N, int64_t K, uint8_t *packed,
  *   q       int8 [N, K] output, 16-byte aligned, must not overlap packed.
  */
 int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipStream_t stream);
+
+/*
+ * ternary_quantize - codes and scales of 16-bit weights (the step before the
+ * layer: its packed and scale inputs).
+ *   w           [N, K] weights, dtype `dtype` (TERNARY_BF16 or TERNARY_FP16),
+ *               row-major, 16-byte aligned.
+ *   N, K        N >= 0, K > 0, K % 4 == 0, K % group_size == 0 when grouped;
+ *               N == 0 is a successful no-op.
+ *   group_size  -1 (one scale per row) or 32, 64, 128, 256.
+ *   packed      uint8 [N, K/4] output, 16-byte aligned.
+ *   scale       fp16 [N] or [N, K/group_size] output, 2-byte aligned.
+ * No output may overlap w or the other output.  Rule: the symmetric linear
+ * quantizer of [ch13 §13.1.3] with the code range {-1, 0, +1}: per group,
+ * s = max |w| rounded to fp16 (nearest even), and q = round(w / s) with ties
+ * to even, i.e. q = sign(w) where |w| > s/2 and 0 elsewhere; a group with
+ * s == 0 gets q = 0.  Then |w - q*s| <= s/2 for every weight ([ch13 §13.1.4]).
+ * w must be finite with every group's max |w| below 65520 (s finite in
+ * fp16); results are unspecified otherwise.  Deterministic, bit-exact.
+ */
+int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t group_size,
+                     uint8_t *packed, uint16_t *scale, hipStream_t stream);
 
 /*
  * ternary_linear - y = x * (q (.) s)^T ([xxqk §4.3]; operand shapes [trdm §4.2]).

@@ -146,6 +146,19 @@ def draw_x(rng: np.random.Generator, M: int, K: int, dtype: str = "bf16") -> np.
     raise ValueError(f"unknown activation dtype {dtype!r}")
 
 
+def draw_weights(rng: np.random.Generator, N: int, K: int, std: float = 0.02,
+                 dtype: str = "bf16") -> np.ndarray:
+    """Dense weight bit patterns [N, K] (uint16) for the quantizer: N(0, std^2)
+    rounded to bf16 or fp16.  std = 0.02 is a common initialisation scale of
+    linear layers; no trained weights are involved."""
+    v = rng.standard_normal((N, K)) * std
+    if dtype == "bf16":
+        return f64_to_bf16_bits(v)
+    if dtype == "fp16":
+        return f64_to_f16_bits(v)
+    raise ValueError(f"unknown weight dtype {dtype!r}")
+
+
 def draw_bytes(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     """Uniform random bytes [N, K // 4]; these include the reserved 2-bit field."""
     return rng.integers(0, 256, size=(N, K // 4), dtype=np.uint8)

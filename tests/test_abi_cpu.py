@@ -136,6 +136,26 @@ def test_pack_unpack_reject(tl):
     assert L.ternary_unpack(FAKE, 4, 0, 0, None) == 0
 
 
+def test_quantize_reject(tl):
+    L = tl.lib()
+    W, P, S = FAKE, FAKE * 4, FAKE * 8
+    assert L.ternary_quantize(W, 2, 4, 128, 64, P, S, None) == -4      # dtype
+    assert L.ternary_quantize(W, 0, 4, 128, 48, P, S, None) == -3      # group size
+    assert L.ternary_quantize(W, 0, 4, 6, -1, P, S, None) == -2        # K % 4
+    assert L.ternary_quantize(W, 0, 4, 96, 64, P, S, None) == -2       # K % g
+    assert L.ternary_quantize(W, 0, -1, 128, 64, P, S, None) == -2
+    assert L.ternary_quantize(0, 0, 4, 128, 64, P, S, None) == -1
+    assert L.ternary_quantize(W, 0, 4, 128, 64, 0, S, None) == -1
+    assert L.ternary_quantize(W, 0, 4, 128, 64, P, 0, None) == -1
+    assert L.ternary_quantize(W + 8, 0, 4, 128, 64, P, S, None) == -5
+    assert L.ternary_quantize(W, 0, 4, 128, 64, P + 4, S, None) == -5
+    assert L.ternary_quantize(W, 0, 4, 128, 64, P, S + 1, None) == -5
+    assert L.ternary_quantize(W, 1, 4, 128, 64, W + 512, S, None) == -6   # packed inside w
+    assert L.ternary_quantize(W, 0, 4, 128, 64, P, W + 16, None) == -6    # scale inside w
+    assert L.ternary_quantize(W, 0, 4, 128, 64, P, P + 2, None) == -6     # scale inside packed
+    assert L.ternary_quantize(W, 0, 0, 128, 64, 0, 0, None) == 0          # N == 0: no-op
+
+
 @pytest.mark.parametrize("M,K,g,path", [
     (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "gemm"),
     (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
