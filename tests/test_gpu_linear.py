@@ -80,11 +80,11 @@ def test_linear_auto_small(tl, M, N, K, g, dtype):
     check_within(y, y_ref, bound, f"auto M={M} N={N} K={K} g={g} {dtype}")
 
 
-# Decode shapes at M <= 2 for the streaming kernel: K split over up to 16
-# waves, K parts longer than the load window (several window steps, the last
-# one partial), x staging of exactly 64 KB, a half slab at the end of K,
-# ragged N (a last block of 4 rows), tiny N, and workgroups whose last waves
-# hold no K part.
+# Decode shapes at M <= 2 for the streaming kernel: K split over up to 8
+# waves, parts of uneven length, parts longer than the one-shot length (run
+# with a window: several window steps, the last one partial), a half slab at
+# the end of K, ragged N (a last block of 4 rows), tiny N, and workgroups
+# whose last waves hold no block.
 STREAM = [
     (1, 40, 20480, 128), (1, 50, 18944, -1), (2, 45, 10240, -1), (2, 77, 6272, 128),
     (1, 4100, 4096, -1), (2, 19, 5248, 128), (1, 600, 3200, 128), (2, 1, 8192, -1),
@@ -380,9 +380,8 @@ def test_linear_gemm_few_tokens(tl, M, N, K, g):
     check_within(y, y_ref, bound, f"few-token gemm M={M} N={N} K={K} g={g}")
 
 
-# Shapes large enough that the streaming kernel keeps several channel blocks
-# per workgroup: the per-channel cases run the full ring of 20 slabs in every
-# wave, the group-scaled one needs more workgroups than CUs.  Raw random bytes
+# Shapes with many more workgroups than the device holds at once: 80 slabs
+# per block, 10 per wave, every wave on the windowed path.  Raw random bytes
 # (reserved code 11 included) stand in for packed codes.
 RING = [(1, 16384, 20480, 128), (1, 16384, 20480, -1), (2, 32768, 10240, -1)]
 
