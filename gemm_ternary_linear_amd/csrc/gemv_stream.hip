@@ -49,12 +49,12 @@ namespace {
 constexpr int kWaves = 8;            // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 // Parts of up to one_shot<M, GROUPED>() slabs issue every load at once (the x
-// area of a wave in LDS bounds it, 4 KB, and so do the registers of the
-// group-scaled kernels).
+// area of a wave in LDS bounds it, 4 KB for M tokens, and so do the registers
+// of the group-scaled kernels).
 template <int MT, bool GROUPED>
 constexpr int one_shot()
 {
-    return MT == 1 && !GROUPED ? 8 : 4;
+    return MT == 1 ? (GROUPED ? 4 : 8) : 8 / MT;
 }
 constexpr int kWindow = 4;           // longer parts: slabs in flight per wave
 constexpr int kSlabsPerPart = 4;     // target part length when K is short
@@ -69,9 +69,9 @@ struct StreamProblem {
     const uint8_t *packed;
     const uint16_t *scale;
     uint16_t *y;
-    int N, K;
-    int group;  // 0 (per channel) or the group size
-    int rb;     // 16-channel blocks per workgroup
+    int M, N, K;  // M <= the kernel's token count MT
+    int group;    // 0 (per channel) or the group size
+    int rb;       // 16-channel blocks per workgroup
     int kp;     // K parts (waves) per block, rb * kp <= kWaves
     int unit0;  // first workgroup of this problem
     // wave w -> (block rbi, part kpi) = 4-bit fields w of these maps (15 in
@@ -148,7 +148,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f3
 // What one wave needs to run its K part.
 struct WaveCtx {
     __amdgpu_buffer_rsrc_t xr, wr, sr;
-    int K, ngroups;
+    int M, K, ngroups;  // M: the problem's tokens (<= the kernel's MT)
     int gsh;       // GC = 2 with groups: column group (128 K) -> scale index shift
     int s_begin;   // first slab of the part
     int woff;      // this lane's byte offset of slab 0 in the block resource
@@ -284,25 +284,25 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
 #pragma unroll
     for (int j = 0; j < kSL; ++j)
         sv[j] = scale_load<GC>(c, 0, S, j);
-    constexpr int kXD = (S + 1) / 2;                 // x DMAs per token
+    // The x area is [MT][kTok]; DMA j fills its elements 512j .. 512j + 511
+    // (one token, or two when a token takes 256), DMAs that would only write
+    // slabs past the part are skipped, and lanes past the part, K or the
+    // problem's tokens write zeros.
     constexpr int kTok = one_shot<MT, GROUPED>() * 256;  // token stride of the x area
-    int xoff[MT * kXD];
+    constexpr int kXD = (MT * kTok + 511) / 512;          // DMAs that cover the area
+    int xoff[kXD];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int j = 0; j < kXD; ++j) {
-            // elements 512j + 8 lane of the part; past the part or K: zeros
-            const int e = 512 * j + 8 * c.lane;
-            const int k = c.s_begin * 256 + e;
-            xoff[t * kXD + j] = e < S * 256 && k < c.K ? (t * c.K + k) * 2 : kOOB;
-        }
+    for (int j = 0; j < kXD; ++j) {
+        const int a = 512 * j + 8 * c.lane;
+        const int t = a / kTok, e = a % kTok;
+        const int k = c.s_begin * 256 + e;
+        xoff[j] = e < S * 256 && k < c.K && t < c.M ? (t * c.K + k) * 2 : kOOB;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int j = 0; j < kXD; ++j)
-            dma16_to_lds(c.xr, c.xbuf + t * kTok + 512 * j, xoff[t * kXD + j]);
+    for (int j = 0; j < kXD; ++j)
+        if ((512 * j) % kTok < S * 256)  // folds: j, S and kTok are constants
+            dma16_to_lds(c.xr, c.xbuf + 512 * j, xoff[j]);
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t w[S];
 #pragma unroll
@@ -399,29 +399,54 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
     return acc;
 }
 
-// A part of n slabs: one-shot up to one_shot<MT, GROUPED>() slabs, rolling beyond.
+// A part of exactly n <= one_shot<MT, GROUPED>() slabs (S counts up to n).
 template <bool FP16, bool GROUPED, int GC, int MT, int S = 1>
-__device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t &chs)
+__device__ __forceinline__ f32x4_t run_short(const WaveCtx &c, int n, uint32_t &chs)
 {
-    if constexpr (S == 1) {
-        if (n == 0) {
-            chs = channel_scale_load<GROUPED>(c);
-            return f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    if (n == S)
+    if (n == S || S == one_shot<MT, GROUPED>())
         return run_part<FP16, GROUPED, GC, MT, S>(c, chs);
     if constexpr (S < one_shot<MT, GROUPED>())
-        return run_part_n<FP16, GROUPED, GC, MT, S + 1>(c, n, chs);
+        return run_short<FP16, GROUPED, GC, MT, S + 1>(c, n, chs);
     else
+        return f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// A part of n slabs: one-shot up to one_shot<MT, GROUPED>() slabs; beyond,
+// with a window (M <= 2) or as one-shot chunks in turn (M >= 4, whose x per
+// slab would take too many registers to stage).
+template <bool FP16, bool GROUPED, int GC, int MT>
+__device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t &chs)
+{
+    constexpr int L = one_shot<MT, GROUPED>();
+    if (n == 0) {
+        chs = channel_scale_load<GROUPED>(c);
+        return f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (n <= L)
+        return run_short<FP16, GROUPED, GC, MT>(c, n, chs);
+    if constexpr (MT <= 2) {
         return run_rolling<FP16, GROUPED, GC, MT>(c, n, chs);
+    } else {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        WaveCtx cc = c;
+        for (int done = 0; done < n; done += L) {
+            cc.s_begin = c.s_begin + done;
+            const f32x4_t part = run_short<FP16, GROUPED, GC, MT>(cc, min(L, n - done), chs);
+            acc[0] += part[0];
+            acc[1] += part[1];
+            acc[2] += part[2];
+            acc[3] += part[3];
+        }
+        return acc;
+    }
 }
 
 // GC: B columns per token (gemv_cols of the group size: 2 for per-channel
 // scales and groups of 128 K or more, 4 for 64, 8 for 32); column GC*t + p
 // holds token t restricted to group p of each slab (half p when GC = 2).
 template <bool FP16, bool GROUPED, int GC, int MT>
-__global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch batch)
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(GROUPED ? 1 : 8))) gemv_stream_kernel(const StreamBatch batch)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -431,8 +456,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
         if (i < batch.count && (int)blockIdx.x >= batch.unit0[i])
             pi = i;
     const StreamProblem &P = batch.p[pi];
-    constexpr int M = MT;
-    const int N = P.N, K = P.K, RB = P.rb, KP = P.kp;
+    const int M = P.M, N = P.N, K = P.K, RB = P.rb, KP = P.kp;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -457,6 +481,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
         return;
 
     WaveCtx c;
+    c.M = M;
     c.K = K;
     c.ngroups = ngroups;
     c.gsh = glog >= 7 ? glog - 7 : 0;
@@ -467,7 +492,7 @@ __global__ void __launch_bounds__(kThreads) gemv_stream_kernel(const StreamBatch
     c.par = col % GC;               // column group of the slab this column collects
     // Lane group g holds codes 64g .. 64g+63 of a slab, word d of them codes
     // 64g + 16d .. +15: in half g/2, in 64-group g, in 32-group 2g + d/2.
-    c.b_lane = c.tok < M && (GC == 2 ? (c.g >> 1) == c.par : (GC == 4 ? c.g == c.par : true));
+    c.b_lane = c.tok < MT && (GC == 2 ? (c.g >> 1) == c.par : (GC == 4 ? c.g == c.par : true));
     // Parts split the block's slabs evenly: part p = [p*n/KP, (p+1)*n/KP).
     c.s_begin = kpi * nslabs / KP;
     const int S = __builtin_amdgcn_readfirstlane((kpi + 1) * nslabs / KP - c.s_begin);
@@ -570,16 +595,30 @@ bool gemv_stream_takes(int64_t M, int64_t K, int group)
 }
 
 namespace {
+// Token count of the kernel instance that runs M tokens.
+int kernel_mt(int M) { return M <= 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+template <bool FP16, bool GROUPED, int GC, int MT>
+void launch_one(dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
+{
+    constexpr size_t lds = lds_bytes<GC, MT, GROUPED>();
+    hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, MT>), grid, block, lds, stream, b);
+}
+
+// MT * GC <= 16: the instances that exist.
 template <bool FP16, bool GROUPED, int GC>
 void launch_m(int mt, dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
 {
-    constexpr size_t lds1 = lds_bytes<GC, 1, GROUPED>(), lds2 = lds_bytes<GC, 2, GROUPED>();
     if (mt == 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 1>), grid, block, lds1, stream,
-                           b);
-    else
-        hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, 2>), grid, block, lds2, stream,
-                           b);
+        launch_one<FP16, GROUPED, GC, 1>(grid, block, stream, b);
+    else if (mt == 2)
+        launch_one<FP16, GROUPED, GC, 2>(grid, block, stream, b);
+    else if constexpr (GC <= 4) {
+        if (mt == 4)
+            launch_one<FP16, GROUPED, GC, 4>(grid, block, stream, b);
+        else if constexpr (GC == 2)
+            launch_one<FP16, GROUPED, GC, 8>(grid, block, stream, b);
+    }
 }
 
 template <bool FP16>
@@ -595,6 +634,12 @@ void launch_group(int group, int mt, dim3 grid, dim3 block, hipStream_t stream,
     else
         launch_m<FP16, true, 2>(mt, grid, block, stream, b);
 }
+
+// One-shot part length of the instance (one_shot<MT, GROUPED>() at run time).
+int one_shot_of(int mt, int group) { return mt == 1 ? (group ? 4 : 8) : 8 / mt; }
+static_assert(one_shot<1, false>() == 8 && one_shot<1, true>() == 4 && one_shot<2, true>() == 4 &&
+                  one_shot<4, false>() == 2 && one_shot<8, true>() == 1,
+              "one_shot_of mirrors one_shot");
 
 }  // namespace
 
@@ -619,11 +664,11 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
         p.packed = a.packed;
         p.scale = a.scale;
         p.y = a.y;
+        p.M = a.M;
         p.N = a.N;
         p.K = a.K;
         p.group = group;
-        split_k(a.K, a.M == 1 && group == 0 ? one_shot<1, false>() : one_shot<2, true>(), p.kp,
-                p.rb);
+        split_k(a.K, one_shot_of(kernel_mt(a.M), group), p.kp, p.rb);
         const int nblocks = (a.N + 15) / 16;
         p.rb = std::min(p.rb, nblocks);
         p.rbi_map = 0;
@@ -642,9 +687,9 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
         return hipSuccess;
     const dim3 grid(units), block(kThreads);
     if (fp16)
-        launch_group<true>(group, mt, grid, block, stream, b);
+        launch_group<true>(group, kernel_mt(mt), grid, block, stream, b);
     else
-        launch_group<false>(group, mt, grid, block, stream, b);
+        launch_group<false>(group, kernel_mt(mt), grid, block, stream, b);
     return hipGetLastError();
 }
 

@@ -108,7 +108,8 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(K=132, g=-1, path=2), -8),
     (dict(M=3, K=256, g=32, path=1), -8),     # g = 32 leaves 2 tokens per GEMV launch
     (dict(M=5, K=256, g=64, path=1), -8),     # g = 64 leaves 4
-    (dict(M=1, K=32768, g=32, path=1), -8),   # the GEMV stages at most 512 groups per row
+    # the GEMV takes K <= 65536
+    (dict(M=1, K=65664, g=-1, path=1, p=FAKE * 16, s=FAKE * 64, y=FAKE * 128), -8),
     (dict(K=160, g=32, path=2), -8),          # fast kernels need K % 128 == 0
 ])
 def test_linear_rejects(tl, kw, status):
@@ -159,13 +160,13 @@ def test_quantize_reject(tl):
 @pytest.mark.parametrize("M,K,g,path", [
     (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "gemm"),
     (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
-    # long K from M = 4: the GEMM is faster (measured crossover)
-    (8, 18944, -1, "gemm"), (4, 25600, 128, "gemm"), (3, 18944, -1, "gemv"),
-    (8, 16256, 128, "gemv"),
+    # long K up to 65536 stays on the GEMV at every M <= 8 (measured faster)
+    (8, 18944, -1, "gemv"), (4, 25600, 128, "gemv"), (3, 18944, -1, "gemv"),
+    (8, 16256, 128, "gemv"), (8, 65536, -1, "gemv"), (1, 65664, -1, "gemm"),
     (0, 128, 128, "gemv"),
     # other group sizes: the GEMV takes M * columns-per-token <= 16
     (2, 4096, 32, "gemv"), (3, 4096, 32, "gemm"), (4, 4096, 64, "gemv"), (5, 4096, 64, "gemm"),
-    (8, 4096, 256, "gemv"), (1, 16384, 32, "gemv"), (1, 32768, 32, "gemm"),
+    (8, 4096, 256, "gemv"), (1, 16384, 32, "gemv"), (1, 32768, 32, "gemv"),
     (64, 4096, 256, "gemm"), (1, 160, 32, "simple"),
 ])
 def test_select_path(tl, M, K, g, path):

@@ -80,7 +80,7 @@ def test_linear_auto_small(tl, M, N, K, g, dtype):
     check_within(y, y_ref, bound, f"auto M={M} N={N} K={K} g={g} {dtype}")
 
 
-# Decode shapes at M <= 2 for the streaming kernel: K split over up to 8
+# Decode shapes for the streaming kernel: K split over up to 8
 # waves, parts of uneven length, parts longer than the one-shot length (run
 # with a window: several window steps, the last one partial), a half slab at
 # the end of K, ragged N (a last block of 4 rows), tiny N, and workgroups
@@ -89,6 +89,10 @@ STREAM = [
     (1, 40, 20480, 128), (1, 50, 18944, -1), (2, 45, 10240, -1), (2, 77, 6272, 128),
     (1, 4100, 4096, -1), (2, 19, 5248, 128), (1, 600, 3200, 128), (2, 1, 8192, -1),
     (1, 48, 30720, 128), (1, 33, 32768, -1), (2, 20, 16384, 128), (1, 7, 31872, 128),
+    # 3..8 tokens (instances of 4 and 8 tokens; parts longer than the one-shot
+    # length run as one-shot chunks in turn)
+    (3, 100, 4096, -1), (4, 77, 18944, -1), (5, 50, 6272, 128), (8, 4100, 4096, -1),
+    (7, 33, 30720, 128), (8, 20, 1024, -1), (6, 40, 5120, -1), (8, 9, 65536, 128),
 ]
 
 
@@ -98,9 +102,8 @@ def test_linear_stream_decode(tl, M, N, K, g, dtype):
     say(f"linear stream decode M={M} N={N} K={K} g={g} {dtype}")
     rng = np.random.default_rng(zlib.crc32(repr(("stream", M, N, K, g, dtype)).encode()))
     codes, packed, scale, x = _case(rng, M, N, K, g, dtype)
-    assert tl.select_path(M, N, K, g) == "gemv"
     y_ref, bound = oracle.linear(x, packed, scale, g, dtype=dtype)
-    y = _run(tl, x, packed, scale, g, dtype, codes=codes)
+    y = _run(tl, x, packed, scale, g, dtype, path="gemv", codes=codes)
     check_within(y, y_ref, bound, f"stream M={M} N={N} K={K} g={g} {dtype}")
 
 
