@@ -142,13 +142,12 @@ int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t gro
  * each group's (or the row's) fp32 partial sum; y is rounded from fp32 to the
  * output dtype, round-to-nearest-even.  x and s must be finite (results for
  * non-finite inputs are unspecified) and |x| < 2^126.
- * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (except M >= 4
- * with K >= 16384, K % 256 == 0, which runs faster on the GEMM), larger M the
+ * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV, larger M the
  * MFMA GEMM; shapes neither fast kernel takes (K % 128 != 0) run the plain
  * kernel.  The GEMV gives each token 2 MFMA columns (per channel, groups of
  * 128 or 256), 4 (groups of 64) or 8 (groups of 32) of 16, so it takes M <= 4
- * for groups of 64 and M <= 2 for groups of 32, and at most 512 groups per
- * row; the GEMM runs the rest.  Results of different paths agree within the bound
+ * for groups of 64 and M <= 2 for groups of 32, and K <= 65536; the GEMM runs
+ * the rest.  Results of different paths agree within the bound
  * |y - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6, not bitwise.
  */
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
@@ -187,7 +186,7 @@ typedef struct {
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
  * any error nothing is launched.  Problems the automatic path sends to the
  * decode GEMV (see ternary_linear) run together in one launch per scale
- * mode (per channel, or each group size) and kernel class (M <= 2, larger M);
+ * mode (per channel, or each group size) and token count M;
  * the GEMM problems the pipelined kernel takes (K % 256 == 0; group sizes 64,
  * 128 or 256 with an even number of groups per row and 4-byte-aligned scales)
  * run together in one grouped GEMM launch per scale mode and tile shape
