@@ -54,7 +54,7 @@ __device__ __forceinline__ uint16_t round_out(float f)
 //   out[2j+1] = {weight 4j+2, weight 4j+3}
 // Each 16-bit weight is +2.0 (0x4000), -2.0 (0xC000), +0 or -0 (code 11).
 // These bit patterns mean +-2 in both bf16 and fp16, so callers fold the
-// factor 1/2 into the scale.  No branches, no table: 18 VALU ops per word.
+// factor 1/2 into the scale.  No branches, no table: 17 VALU ops per word.
 //
 // Step 1 rewrites every field (b1 b0) as (sign, magnitude) = (b1, b0 ^ b1):
 //   00 -> 00, 01 -> 01, 10 -> 11, 11 -> 10.
@@ -63,8 +63,10 @@ __device__ __forceinline__ uint16_t round_out(float f)
 // (v_perm_b32; selector 0x0c yields a zero byte).
 __device__ __forceinline__ void decode16(uint32_t w, uint32_t out[8])
 {
-    const uint32_t e = w ^ (w >> 1);                                   // bit 2i = b0 ^ b1
-    const uint32_t z = (e & 0x55555555u) | (w & 0xaaaaaaaau);          // (sign, magnitude)
+    // (sign, magnitude): even bits w ^ (w >> 1) = b0 ^ b1, odd bits w = b1, as
+    // one three-input bit operation (truth table 0x78 of (w, w >> 1, mask):
+    // mask ? w ^ (w >> 1) : w).
+    const uint32_t z = __builtin_amdgcn_bitop3_b32(w, w >> 1, 0x55555555u, 0x78);
     const uint32_t z3 = z & 0xc0c0c0c0u;                               // field 3 of each byte
     const uint32_t z2 = (z << 2) & 0xc0c0c0c0u;                        // field 2
     const uint32_t z1 = (z << 4) & 0xc0c0c0c0u;                        // field 1

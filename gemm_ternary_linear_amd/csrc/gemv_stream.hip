@@ -229,14 +229,14 @@ __device__ __forceinline__ uint32_t scale_load(const WaveCtx &c, int i0, int nsl
 // column GC*tok + par) added to `part`.
 template <bool FP16, int GC>
 __device__ __forceinline__ f32x4_t slab_mfma(const WaveCtx &c, const uint16_t *xs, int tstride,
-                                             u32x4_t w, f32x4_t part)
+                                             u32x4_t w, f32x4_t part, uint4 &b0, uint4 &b1)
 {
     const uint4 *xb = reinterpret_cast<const uint4 *>(xs + c.tok * tstride + c.g * 64);
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    // B operand pieces: lanes without real B entries keep zeros (GC = 8:
-    // every lane rewrites both, the 32-groups change with d).
+    // B operand pieces b0, b1 (zeroed once per part by the caller): lanes
+    // without real B entries keep the zeros (GC = 8: every lane rewrites
+    // both, the 32-groups change with d).
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
-    uint4 b0 = zero4, b1 = zero4;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         if constexpr (GC == 8) {
@@ -322,15 +322,16 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
     __builtin_amdgcn_wave_barrier();
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
 #pragma unroll
     for (int i = 0; i < S; ++i) {
         const uint16_t *xs = c.xbuf + i * 256;
         if constexpr (GROUPED) {
             const f32x4_t part =
-                slab_mfma<FP16, GC>(c, xs, kTok, w[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                slab_mfma<FP16, GC>(c, xs, kTok, w[i], f32x4_t{0.f, 0.f, 0.f, 0.f}, b0, b1);
             fold_scales<GC>(c, GC * i + c.par, part, acc);
         } else {
-            acc = slab_mfma<FP16, GC>(c, xs, kTok, w[i], acc);
+            acc = slab_mfma<FP16, GC>(c, xs, kTok, w[i], acc, b0, b1);
         }
     }
     return acc;
@@ -367,6 +368,7 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
     x_piece_store<MT>(c, 0, xv[0]);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
     for (int base = 0; base < S; base += W) {
 #pragma unroll
         for (int j = 0; j < W; ++j) {
@@ -385,11 +387,13 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
                     x_piece_store<MT>(c, (i + 1) & 1, xv[(j + 1) % W]);
                 __builtin_amdgcn_wave_barrier();
                 if constexpr (GROUPED) {
-                    const f32x4_t part = slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256,
-                                                             w[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    const f32x4_t part =
+                        slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j],
+                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, b0, b1);
                     fold_scales<GC>(c, (i & 1) * GC + c.par, part, acc);
                 } else {
-                    acc = slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j], acc);
+                    acc = slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j], acc,
+                                              b0, b1);
                 }
                 __builtin_amdgcn_wave_barrier();
             }
