@@ -395,6 +395,55 @@ def summarize_mfma(*dirs) -> None:
     print("\n".join(lines))
 
 
+VALU_FILE = ROOT / "profiles" / "gemv_stream_7b_decode_m1_valu.txt"
+VALU_PASS = ("VALUBusy", "MfmaUtil", "SQ_INSTS_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
+             "SQ_ACTIVE_INST_ANY", "SQ_BUSY_CYCLES")
+
+
+def summarize_valu(d: str) -> None:
+    """Digest one --pmc run of bench.py for the fused decode launch (the
+    largest-grid gemv_stream_kernel dispatch): how busy its vector ALUs and
+    matrix cores are, and how much of a wave's life goes to waiting."""
+    vals = {}
+    for r in read_counter_csv(Path(d)):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size", 0)), r["Dispatch_Id"])
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+        vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    keys = [k for k in vals if "gemv_stream_kernel" in k[0]]
+    if not keys:
+        raise SystemExit(f"no gemv_stream_kernel dispatch under {d}")
+    top = max(k[1] for k in keys)
+    keys = [k for k in keys if k[1] == top]
+    mean = {}
+    for c in {c for k in keys for c in vals[k]}:
+        v = [vals[k][c] for k in keys if c in vals[k]]
+        mean[c] = (sum(v) / len(v), len(v))
+    lines = [
+        "# Vector-ALU and matrix-core activity of the fused decode GEMV launch (all 7",
+        "# projections of the 7B layer at M=1, the largest gemv_stream_kernel dispatch), from",
+        "#   rocprofv3 --pmc " + " ".join(VALU_PASS) + " --output-format csv -d <D> -o bench -- \\",
+        "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
+        "--prefill-steps 1 --prefill-warmup 2",
+        "#   python3 bench.py --summarize-valu <D>",
+        "# VALUBusy and MfmaUtil are rocprofv3's derived percentages of the launch's GPU time;",
+        "# wait_share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of the waves' lifetime spent",
+        "# waiting on memory), issue_share = SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES.",
+        f"source_hash {kernel_source_hash()}",
+        f"grid_threads {top}",
+    ]
+    for c in sorted(mean):
+        lines.append(f"{c:<24} {mean[c][0]:>16.4f} (n={mean[c][1]})")
+
+    def get(c):
+        return mean[c][0] if c in mean else float("nan")
+
+    lines += [f"wait_share {get('SQ_WAIT_INST_ANY') / get('SQ_WAVE_CYCLES'):.4f}",
+              f"issue_share {get('SQ_ACTIVE_INST_ANY') / get('SQ_WAVE_CYCLES'):.4f}"]
+    VALU_FILE.parent.mkdir(exist_ok=True)
+    VALU_FILE.write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 TRACE_FILE = ROOT / "profiles" / "kernels_7b_decode_prefill_trace.txt"
 
 
@@ -752,6 +801,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "LDS_DIR"))
+    ap.add_argument("--summarize-valu", metavar="VALU_DIR")
     ap.add_argument("--detail", type=str, default=None, help="write per-shape results here")
     args = ap.parse_args()
 
@@ -763,6 +813,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_valu:
+        summarize_valu(args.summarize_valu)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -148,3 +148,31 @@ def test_summarize_mfma_relates_gemm_to_probe(tmp_path, monkeypatch):
     assert float(kv["gemm_mfma_flops"]) == pytest.approx(1.024e12)
     assert float(kv["gemm_lds_bank_conflict_per_active"]) == pytest.approx(0.025)
     assert bench.stored_mfma() == pytest.approx(0.75)
+
+
+def test_summarize_valu_takes_the_fused_launch(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "VALU_FILE", tmp_path / "valu.txt")
+    gemv = "ternary::gemv_stream_kernel<false, false, 2, 1>(StreamBatch)"
+    d = tmp_path / "V"
+    d.mkdir()
+    with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        for i, (grid, busy, wait, life) in enumerate([(884736, 40.0, 30.0, 60.0),
+                                                      (884736, 36.0, 26.0, 56.0),
+                                                      (65536, 5.0, 1.0, 100.0)]):
+            for name, v in (("VALUBusy", busy), ("SQ_WAIT_INST_ANY", wait),
+                            ("SQ_WAVE_CYCLES", life), ("SQ_ACTIVE_INST_ANY", life / 4)):
+                w.writerow({c: 0 for c in COLS} | {"Dispatch_Id": i + 1, "Kernel_Name": gemv,
+                                                   "Grid_Size": grid, "Counter_Name": name,
+                                                   "Counter_Value": v})
+    bench.summarize_valu(str(d))
+    kv = {}
+    for ln in (tmp_path / "valu.txt").read_text().splitlines():
+        if ln and not ln.startswith("#"):
+            k, v = ln.split(None, 1)
+            kv[k] = v.split()[0]
+    assert int(kv["grid_threads"]) == 884736           # the larger launch only
+    assert float(kv["VALUBusy"]) == pytest.approx(38.0)
+    assert float(kv["wait_share"]) == pytest.approx(28.0 / 58.0, rel=1e-3)
+    assert float(kv["issue_share"]) == pytest.approx(0.25, rel=1e-3)
