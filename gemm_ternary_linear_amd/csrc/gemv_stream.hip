@@ -1,7 +1,7 @@
-// Streaming decode GEMV (M <= 2) for the ternary linear layer on gfx950.
+// Streaming decode GEMV (M <= 8) for the ternary linear layer on gfx950.
 //
 // The layer ([xxqk] m.xxqk.cn/news/593501 §4.3: y = x @ (unpack(q) * s)^T)
-// at one or two tokens reads every packed weight byte once and does little
+// at a few tokens reads every packed weight byte once and does little
 // arithmetic per byte, so its speed is the HBM stream ([nxbn]
 // m.nxbn.cn/news/169761 §4.1/§4.4).  The kernel is shaped by how gfx950
 // serves such a stream (measured on MI355X with read-only probes of the same
@@ -11,11 +11,13 @@
 //    block's K range split into KP = 8 / RB parts, one per wave: parts of
 //    about 4 slabs at short K (K = 4096: 2 blocks x 4 parts), 8 parts at long
 //    K.  A slab is 256 codes = 64 bytes of each of the block's 16 rows, one
-//    16-byte buffer load per lane.  Parts of at most 8 slabs (4 at M = 2)
-//    issue every load at once, as the wave's first instructions: x by DMA
-//    straight into the wave's LDS, then the codes.  Longer parts keep kWindow
-//    slabs in flight and issue the next slab's loads as each slab is
-//    consumed.  Small workgroups of short-lived waves keep the memory system
+//    16-byte buffer load per lane.  Parts of at most one_shot<M>() slabs (8
+//    at M = 1, 8 / M beyond) issue every load at once, as the wave's first
+//    instructions: x by DMA straight into the wave's LDS, then the codes.
+//    Longer parts keep kWindow slabs in flight and issue the next slab's
+//    loads as each slab is consumed (M <= 2), or run as one-shot chunks in
+//    turn (M >= 4).  Instances of 1, 2, 4 and 8 tokens exist; a problem runs
+//    on the smallest one that holds its M (tokens past M read zeros).  Small workgroups of short-lived waves keep the memory system
 //    supplied: the dispatcher refills a CU as soon as a workgroup is done.
 //  * A block's K parts meet without a workgroup barrier: each wave stores its
 //    partial sums in LDS and bumps the block's LDS counter; the wave that
@@ -72,8 +74,8 @@ struct StreamProblem {
     int M, N, K;  // M <= the kernel's token count MT
     int group;    // 0 (per channel) or the group size
     int rb;       // 16-channel blocks per workgroup
-    int kp;     // K parts (waves) per block, rb * kp <= kWaves
-    int unit0;  // first workgroup of this problem
+    int kp;       // K parts (waves) per block, rb * kp <= kWaves
+    int unit0;    // first workgroup of this problem
     // wave w -> (block rbi, part kpi) = 4-bit fields w of these maps (15 in
     // both: the wave holds no part); precomputed so that the kernel's start
     // needs no division
@@ -90,9 +92,10 @@ struct StreamBatch {
 
 // LDS: per wave an x area of M*L*256 elements, L = one_shot<M, GROUPED>() (a
 // one-shot part's x, token t at t*L*256; a long part uses the first M*512
-// elements as two slab buffers; once the part is done, its first 1 KB holds the wave's
-// partial sums for the K-part reduction) and (group-scaled) the scales of GC
-// column groups x 16 channels for up to L slabs; then one counter per block.
+// elements as two slab buffers; once the part is done, its first 1 KB holds
+// the wave's partial sums for the K-part reduction) and (group-scaled) the
+// scales of GC column groups x 16 channels for up to L slabs; then one
+// counter per block.
 template <int MT, bool GROUPED>
 constexpr int x_area_elems()
 {
