@@ -11,14 +11,16 @@
 //    block's K range split into KP = 8 / RB parts, one per wave: parts of
 //    about 4 slabs at short K (K = 4096: 2 blocks x 4 parts), 8 parts at long
 //    K.  A slab is 256 codes = 64 bytes of each of the block's 16 rows, one
-//    16-byte buffer load per lane.  Parts of at most one_shot<M>() slabs (8
-//    at M = 1, 8 / M beyond) issue every load at once, as the wave's first
-//    instructions: x by DMA straight into the wave's LDS, then the codes.
-//    Longer parts keep kWindow slabs in flight and issue the next slab's
-//    loads as each slab is consumed (M <= 2), or run as one-shot chunks in
-//    turn (M >= 4).  Instances of 1, 2, 4 and 8 tokens exist; a problem runs
-//    on the smallest one that holds its M (tokens past M read zeros).  Small workgroups of short-lived waves keep the memory system
-//    supplied: the dispatcher refills a CU as soon as a workgroup is done.
+//    16-byte buffer load per lane.  Parts of at most one_shot() slabs (8 at
+//    M = 1, 4 at M = 1 with group scales, 8 / M beyond) issue every load at
+//    once, as the wave's first instructions: x by DMA straight into the
+//    wave's LDS, then the codes.  Longer per-channel parts of 1 or 2 tokens
+//    keep kWindow slabs in flight and issue the next slab's loads as each
+//    slab is consumed; other long parts run as one-shot chunks of near-equal
+//    length in turn.  Instances of 1, 2, 4 and 8 tokens exist; a problem runs
+//    on the smallest one that holds its M (tokens past M read zeros).  Small
+//    workgroups of short-lived waves keep the memory system supplied: the
+//    dispatcher refills a CU as soon as a workgroup is done.
 //  * A block's K parts meet without a workgroup barrier: each wave stores its
 //    partial sums in LDS and bumps the block's LDS counter; the wave that
 //    arrives last adds the parts in part order (so the result does not depend
@@ -340,25 +342,19 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
     return acc;
 }
 
-// Run a K part of S > one_shot<MT, GROUPED>() slabs with kWindow slabs in
-// flight: slab i's loads (its scales, x and codes) sit in ring slot
+// Run a per-channel K part of S > one_shot<MT, false>() slabs with kWindow
+// slabs in flight: slab i's loads (its x and codes) sit in ring slot
 // i % kWindow, and the loads of slab i + kWindow are issued as soon as slab i
-// is consumed.  Slots past
-// the part load as zeros without touching memory, so every pass issues the
-// same loads and the compiler's waits stay exact.
-template <bool FP16, bool GROUPED, int GC, int MT>
+// is consumed.  Slots past the part load as zeros without touching memory, so
+// every pass issues the same loads and the compiler's waits stay exact.
+template <bool FP16, int GC, int MT>
 __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t &chs)
 {
     constexpr int W = kWindow;
-    constexpr int kSL = GROUPED ? (GC + 3) / 4 : 0;  // scale loads per lane and slab
-    uint32_t sv[W][kSL > 0 ? kSL : 1];
     XPiece<MT> xv[W];
     u32x4_t w[W];
     auto issue = [&](int slot, int i) {
         const bool in = i < S;
-#pragma unroll
-        for (int j = 0; j < kSL; ++j)
-            sv[slot][j] = scale_load<GC>(c, in ? i : 0, in ? 1 : 0, j);
         xv[slot] = x_piece_load<MT>(c, in ? c.s_begin + i : (1 << 20));
         w[slot] = __builtin_amdgcn_raw_buffer_load_b128(
             c.wr, in ? c.woff + (c.s_begin + i) * 64 : kOOB, 0, 0);
@@ -367,7 +363,7 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
 #pragma unroll
     for (int j = 0; j < W; ++j)
         issue(j, j);
-    chs = channel_scale_load<GROUPED>(c);
+    chs = channel_scale_load<false>(c);
     x_piece_store<MT>(c, 0, xv[0]);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -377,27 +373,11 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
         for (int j = 0; j < W; ++j) {
             const int i = base + j;
             if (i < S) {
-                if constexpr (GROUPED) {
-#pragma unroll
-                    for (int t = 0; t < kSL; ++t) {
-                        const int lg = (c.lane >> 4) + 4 * t;
-                        if (lg < GC)
-                            c.sbuf[((i & 1) * GC + lg) * 16 + (c.lane & 15)] =
-                                (uint16_t)sv[j][t];
-                    }
-                }
                 if (i + 1 < S)
                     x_piece_store<MT>(c, (i + 1) & 1, xv[(j + 1) % W]);
                 __builtin_amdgcn_wave_barrier();
-                if constexpr (GROUPED) {
-                    const f32x4_t part =
-                        slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j],
-                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, b0, b1);
-                    fold_scales<GC>(c, (i & 1) * GC + c.par, part, acc);
-                } else {
-                    acc = slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j], acc,
-                                              b0, b1);
-                }
+                acc = slab_mfma<FP16, GC>(c, c.xbuf + (i & 1) * (MT * 256), 256, w[j], acc, b0,
+                                          b1);
                 __builtin_amdgcn_wave_barrier();
             }
             issue(j, i + W);
@@ -418,9 +398,11 @@ __device__ __forceinline__ f32x4_t run_short(const WaveCtx &c, int n, uint32_t &
         return f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// A part of n slabs: one-shot up to one_shot<MT, GROUPED>() slabs; beyond,
-// with a window (M <= 2) or as one-shot chunks in turn (M >= 4, whose x per
-// slab would take too many registers to stage).
+// A part of n slabs: one-shot up to L = one_shot<MT, GROUPED>() slabs;
+// beyond, per-channel parts of 1 or 2 tokens run with a window, and the rest
+// (grouped parts, whose scales take registers of their own, and 4 or 8 tokens,
+// whose x per slab would take too many) as ceil(n / L) one-shot chunks of
+// near-equal length in turn.
 template <bool FP16, bool GROUPED, int GC, int MT>
 __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t &chs)
 {
@@ -431,14 +413,15 @@ __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t 
     }
     if (n <= L)
         return run_short<FP16, GROUPED, GC, MT>(c, n, chs);
-    if constexpr (MT <= 2) {
-        return run_rolling<FP16, GROUPED, GC, MT>(c, n, chs);
+    if constexpr (MT <= 2 && !GROUPED) {
+        return run_rolling<FP16, GC, MT>(c, n, chs);
     } else {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         WaveCtx cc = c;
-        for (int done = 0; done < n; done += L) {
+        const int chunks = (n + L - 1) / L, len = (n + chunks - 1) / chunks;
+        for (int done = 0; done < n; done += len) {
             cc.s_begin = c.s_begin + done;
-            const f32x4_t part = run_short<FP16, GROUPED, GC, MT>(cc, min(L, n - done), chs);
+            const f32x4_t part = run_short<FP16, GROUPED, GC, MT>(cc, min(len, n - done), chs);
             acc[0] += part[0];
             acc[1] += part[1];
             acc[2] += part[2];
@@ -581,7 +564,7 @@ __global__ void __launch_bounds__(kThreads)
 // that RB = kWaves / KP blocks fill the workgroup.  KP is the largest power
 // of two with parts of at least kSlabsPerPart slabs, doubled while a part
 // would exceed the one-shot length `one` (up to kWaves parts; longer parts
-// run with a window).
+// run with a window or in chunks).
 void split_k(int K, int one, int &kp, int &rb)
 {
     const int nslabs = (K + 255) / 256;

@@ -79,7 +79,7 @@ def test_groups_stream_gemv(tl, M, N, K, g, dtype):
 
 # M <= 8 GEMV beyond the streaming kernel (groups of 64 up to M = 4, of 256 up
 # to M = 8), and the streaming kernel's longest parts (M <= 2, K up to 65536:
-# 20 and 32 slabs per wave, run with a window)
+# 20 and 32 slabs per wave, run as one-shot chunks)
 GEMV = [(3, 257, 4096, 64), (4, 100, 1536, 64), (4, 33, 8192, 64),
         (3, 100, 2048, 256), (5, 64, 4096, 256), (8, 48, 5120, 256), (7, 1030, 1280, 256),
         (1, 40, 40960, 256), (2, 9, 65536, 256)]

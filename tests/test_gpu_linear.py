@@ -82,7 +82,8 @@ def test_linear_auto_small(tl, M, N, K, g, dtype):
 
 # Decode shapes for the streaming kernel: K split over up to 8
 # waves, parts of uneven length, parts longer than the one-shot length (run
-# with a window: several window steps, the last one partial), a half slab at
+# with a window, per-channel: several window steps, the last one partial; in
+# one-shot chunks of near-equal length, grouped), a half slab at
 # the end of K, ragged N (a last block of 4 rows), tiny N, and workgroups
 # whose last waves hold no block.
 STREAM = [
@@ -384,7 +385,8 @@ def test_linear_gemm_few_tokens(tl, M, N, K, g):
 
 
 # Shapes with many more workgroups than the device holds at once: 80 slabs
-# per block, 10 per wave, every wave on the windowed path.  Raw random bytes
+# per block, 10 per wave, every wave on the windowed (per-channel) or chunked
+# (grouped) path.  Raw random bytes
 # (reserved code 11 included) stand in for packed codes.
 RING = [(1, 16384, 20480, 128), (1, 16384, 20480, -1), (2, 32768, 10240, -1)]
 
