@@ -18,14 +18,11 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 // ---------------------------------------------------------------- rounding
 
-// fp32 -> bf16 bit pattern, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 bit pattern: gfx950's conversion instruction (v_cvt_pk_bf16_f32),
+// round to nearest even under the default rounding mode; NaN stays a NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // fp32 -> IEEE binary16 bit pattern (hardware conversion, round to nearest even).

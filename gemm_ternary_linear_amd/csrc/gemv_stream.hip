@@ -150,6 +150,19 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t a[4], uint4 b, f3
                                                        0);
 }
 
+// Lane i of each quad of lanes takes v from lane (SEL >> 2i) & 3 of its quad
+// (a DPP quad permutation).
+template <int SEL>
+__device__ __forceinline__ int quad_perm(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, SEL, 0xf, 0xf, false);
+}
+template <int SEL>
+__device__ __forceinline__ float quad_perm(float v)
+{
+    return __builtin_bit_cast(float, quad_perm<SEL>(__builtin_bit_cast(int, v)));
+}
+
 // What one wave needs to run its K part.
 struct WaveCtx {
     __amdgpu_buffer_rsrc_t xr, wr, sr;
@@ -162,11 +175,12 @@ struct WaveCtx {
     uint16_t *xbuf;  // this wave's x area
     uint16_t *sbuf;  // this wave's group scales [GC*one_shot<M, GROUPED>()][16]
     int srow_off;    // grouped: scale offset (bytes) of this lane's row, group 0; < 0: none
-    int chs_off;     // per channel: scale offset (bytes) of this lane's channel, or kOOB
+    int chs_off;     // per channel: scale offset (bytes) of channel 4g + (lane & 3), or kOOB
 };
 
-// Per-channel scale of the block's channel `lane` (lanes 0..15), issued after
-// the part's own loads: whichever wave finishes the block applies it.
+// Per-channel scale of the block's channel 4g + (lane & 3), issued after the
+// part's own loads: whichever wave finishes the block applies it (each quad
+// of lanes holds the scales of the four channels its C rows cover).
 template <bool GROUPED>
 __device__ __forceinline__ uint32_t channel_scale_load(const WaveCtx &c)
 {
@@ -499,7 +513,8 @@ __global__ void __launch_bounds__(kThreads)
     c.xbuf = wlds;
     c.sbuf = wlds + x_area_elems<MT, GROUPED>();
 
-    c.chs_off = lane < 16 && rb * 16 + lane < N ? (rb * 16 + lane) * 2 : kOOB;
+    const int chs_ch = rb * 16 + 4 * c.g + (lane & 3);
+    c.chs_off = chs_ch < N ? chs_ch * 2 : kOOB;
 
     uint32_t chs = 0u;
     const f32x4_t acc = run_part_n<FP16, GROUPED, GC, MT>(c, S, chs);
@@ -529,18 +544,27 @@ __global__ void __launch_bounds__(kThreads)
     }
 
     // ---- epilogue: the token's GC columns, channel scale, rounding ----------
+    // channel 4g + r's scale: lane r of this lane's quad
+    float chsc[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (!GROUPED) {
+        chsc[0] = f16_bits_to_f32((uint16_t)quad_perm<0x00>((int)chs));
+        chsc[1] = f16_bits_to_f32((uint16_t)quad_perm<0x55>((int)chs));
+        chsc[2] = f16_bits_to_f32((uint16_t)quad_perm<0xaa>((int)chs));
+        chsc[3] = f16_bits_to_f32((uint16_t)quad_perm<0xff>((int)chs));
+    }
     uint16_t o16[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        // the GC columns of a token (adjacent lanes) hold disjoint K sets
-        float tot = sum[r] + __shfl_xor(sum[r], 1);
+        // the GC columns of a token (adjacent lanes) hold disjoint K sets:
+        // within a quad, swap lanes 1 apart, then 2 apart (DPP)
+        float tot = sum[r] + quad_perm<0xb1>(sum[r]);
         if constexpr (GC >= 4)
-            tot += __shfl_xor(tot, 2);
+            tot += quad_perm<0x4e>(tot);
         if constexpr (GC >= 8)
             tot += __shfl_xor(tot, 4);
         float o = 0.5f * tot;  // decoded weights are +-2
         if constexpr (!GROUPED)
-            o *= f16_bits_to_f32((uint16_t)__shfl((int)chs, 4 * c.g + r));
+            o *= chsc[r];
         o16[r] = round_out<FP16>(o);
     }
     // lane (g, token t, par 0) holds channels 4g..4g+3 of token t

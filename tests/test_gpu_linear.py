@@ -171,6 +171,47 @@ def test_closed_form_exact(tl, path):
     assert np.all(y3 == 0.0)
 
 
+# y = x0 + x1 exactly (two +1 codes, unit scales), with x1 putting y on a tie
+# of the output format, just above or below one, or on none; the expected
+# patterns follow from round-to-nearest, ties to even (u = 1 ULP at 1.0):
+#   1 + u/2 -> 1 (tie, even down)    1 + 3u/2 -> 1 + 2u (tie, even up)
+#   1 + 3u/4 -> 1 + u (above half)   1 + u/4 -> 1 (below half)
+#   the two ties negated             2 + u -> 2 (tie at the next binade)
+ROUNDING = {  # dtype: (fraction bits, expected output bit patterns)
+    "bf16": (7, [0x3F80, 0x3F82, 0x3F81, 0x3F80, 0xBF80, 0xBF82, 0x4000, 0x3F80]),
+    "fp16": (10, [0x3C00, 0x3C02, 0x3C01, 0x3C00, 0xBC00, 0xBC02, 0x4000, 0x3C00]),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("path", ["gemv", "gemm", "simple"])
+def test_output_rounding_ties_to_even(tl, path, dtype):
+    say(f"linear output rounding {path} {dtype}")
+    import torch
+    fb, expect = ROUNDING[dtype]
+    u = 2.0 ** -fb
+    pairs = [(1.0, u / 2), (1.0, 3 * u / 2), (1.0, 3 * u / 4), (1.0, u / 4), (-1.0, -u / 2),
+             (-1.0, -3 * u / 2), (2.0, u), (1.0, 0.0)]
+    reps = 1 if path == "gemv" else 8      # 8 tokens (GEMV) or 64 (GEMM tiles)
+    N, K = 20, 256
+    xv = np.zeros((8 * reps, K))
+    xv[:, 0] = [a for a, _ in pairs] * reps
+    xv[:, 1] = [b for _, b in pairs] * reps
+    to_bits = synth.f64_to_bf16_bits if dtype == "bf16" else synth.f64_to_f16_bits
+    x = to_bits(xv)
+    assert np.array_equal(widen(x, dtype), xv)  # every activation is exact
+    codes = np.zeros((N, K), np.int8)
+    codes[:, :2] = 1
+    packed, _ = oracle.pack(codes)
+    scale = synth.f64_to_f16_bits(np.ones(N))
+    y = tl.linear(to_dev(x, _tdt(dtype)), to_dev(packed, None), to_dev(scale, torch.float16),
+                  -1, path=path)
+    torch.cuda.synchronize()
+    got = bits_of(y)
+    want = np.repeat(np.array(expect * reps, np.uint16)[:, None], N, axis=1)
+    assert np.array_equal(got, want), [hex(v) for v in got[:8, 0]]
+
+
 def test_deterministic(tl):
     say("linear determinism")
     import torch
