@@ -646,11 +646,13 @@ hipError_t launch_gemm_t(const uint16_t *x, int M, int N, int K, const uint8_t *
 typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;  // per-channel, M > 64
 // Few tokens: the MFMAs are not the limit, the weight stream is, so the
 // tiles take fewer tokens and (M <= 32) the pipeline runs 8 stages deep to
-// keep more weight bytes in flight per CU.  Group-scaled problems, which keep
-// a second set of accumulators, use these at every M so that they still run
-// two workgroups per CU.
+// keep more weight bytes in flight per CU, in two-wave workgroups of 128
+// channels: twice the tiles of 256 channels, which spreads shapes of few
+// channel tiles over more CUs (a 25600 x 5120 problem at M = 16: 33 against
+// 40 us).  Group-scaled problems, which keep a second set of accumulators,
+// use these at every M so that they still run two workgroups per CU.
 typedef dma::Cfg<256, 64, 4, 1, 4, 2> MidCfg;   // 32 < M <= 64 (or K % 512 != 0)
-typedef dma::Cfg<256, 32, 4, 1, 8, 2> SmallCfg; // M <= 32, K % 512 == 0
+typedef dma::Cfg<128, 32, 2, 1, 8, 2> SmallCfg; // M <= 32, K % 512 == 0
 
 // Which configuration a problem runs with: 0 small, 1 mid, 2 large.
 int big_cfg_of(int M, int K, int group)
