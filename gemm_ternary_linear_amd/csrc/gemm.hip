@@ -649,18 +649,21 @@ typedef dma::Cfg<256, 128, 4, 1, 4, 2> BigCfg;  // per-channel, M > 64
 // keep more weight bytes in flight per CU, in two-wave workgroups of 128
 // channels: twice the tiles of 256 channels, which spreads shapes of few
 // channel tiles over more CUs (a 25600 x 5120 problem at M = 16: 33 against
-// 40 us).  Group-scaled problems, which keep a second set of accumulators,
-// use these at every M so that they still run two workgroups per CU.
+// 40 us); up to 16 tokens the tile takes 16 (30 us).  Group-scaled problems,
+// which keep a second set of accumulators, use these at every M so that they
+// still run two workgroups per CU.
 typedef dma::Cfg<256, 64, 4, 1, 4, 2> MidCfg;   // 32 < M <= 64 (or K % 512 != 0)
-typedef dma::Cfg<128, 32, 2, 1, 8, 2> SmallCfg; // M <= 32, K % 512 == 0
+typedef dma::Cfg<128, 32, 2, 1, 8, 2> SmallCfg; // 16 < M <= 32, K % 512 == 0
+typedef dma::Cfg<128, 16, 2, 1, 8, 2> TinyCfg;  // M <= 16, K % 512 == 0
 
-// Which configuration a problem runs with: 0 small, 1 mid, 2 large.
+// Which configuration a problem runs with: 0 tiny, 1 small, 2 mid, 3 large.
 int big_cfg_of(int M, int K, int group)
 {
+    static_assert(TinyCfg::NS == SmallCfg::NS, "one K condition for both");
     const bool grouped = group != 0;
     if (M <= 32 && K % (dma::TK * SmallCfg::NS) == 0)
-        return 0;
-    return M <= 64 || grouped ? 1 : 2;
+        return M <= 16 ? 0 : 1;
+    return M <= 64 || grouped ? 2 : 3;
 }
 
 // The pipelined kernel takes problems whose K is a whole number of 4-step
@@ -801,12 +804,14 @@ hipError_t launch_big_group(const GemvArgs *args, const int (*idx)[kGemvMaxBatch
 {
     hipError_t e = hipSuccess;
     if (n[0] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[0], n[0], stream);
+        e = launch_big_mode<FP16, GS, TinyCfg>(args, idx[0], n[0], stream);
     if (n[1] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[1], n[1], stream);
+        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[1], n[1], stream);
+    if (n[2] && e == hipSuccess)
+        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[2], n[2], stream);
     if constexpr (GS == 0)  // group-scaled problems never take the large configuration
-        if (n[2] && e == hipSuccess)
-            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[2], n[2], stream);
+        if (n[3] && e == hipSuccess)
+            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[3], n[3], stream);
     return e;
 }
 
@@ -814,7 +819,7 @@ template <bool FP16>
 hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
 {
     // one launch per (group size, configuration) present
-    int idx[4][3][kGemvMaxBatch], n[4][3] = {};
+    int idx[4][4][kGemvMaxBatch], n[4][4] = {};
     static_assert(kGemvMaxBatch <= 8, "batch table");
     for (int i = 0; i < count; ++i) {
         const int g = args[i].group;

@@ -408,11 +408,13 @@ def test_linear_gemm_grouped_pipelined(tl, M, N, K, dtype):
                  f"grouped (2-byte aligned scales) M={M} N={N} K={K} {dtype}")
 
 
-# Few-token prefill shapes on the pipelined kernel: 32-token tiles 8 stages
-# deep (M <= 32, K % 512 == 0) and 64-token tiles (32 < M <= 64, or K % 512
-# != 0), both scale modes, ragged tiles; the GEMM path forced at M = 1 and 8.
+# Few-token prefill shapes on the pipelined kernel: 16-token (M <= 16) and
+# 32-token (M <= 32) tiles of 128 channels 8 stages deep (K % 512 == 0), and
+# 64-token tiles (32 < M <= 64, or K % 512 != 0), both scale modes, ragged
+# tiles; the GEMM path forced at M = 1 and 8.
 SMALLM = [(9, 300, 2048, -1), (32, 1100, 1024, -1), (48, 520, 768, -1), (1, 700, 4096, -1),
-          (8, 700, 5120, 128), (33, 200, 1536, 128), (20, 260, 768, 128)]
+          (8, 700, 5120, 128), (33, 200, 1536, 128), (20, 260, 768, 128),
+          (13, 300, 1536, 128), (16, 1030, 2048, -1), (24, 129, 2048, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,g", SMALLM)
