@@ -712,7 +712,7 @@ def measure_ceilings(tl, layer_bytes, steps):
     - copy_512MiB: a 512 MiB -> 512 MiB copy (reads plus writes);
     - mfma_loop: four independent bf16 MFMA chains per wave on register
       operands, 1.1e12 flops per launch; cold (the first launches) and
-      sustained (after 10 untimed launches, like the prefill step)."""
+      sustained (after 10 untimed launches)."""
     import torch
 
     def ev_time(fn, reps):
@@ -793,7 +793,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--prefill-warmup", type=int, default=10,
+    ap.add_argument("--prefill-warmup", type=int, default=60,
                     help="untimed prefill steps first (clocks settle under sustained MFMA load)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true",
