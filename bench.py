@@ -152,6 +152,25 @@ class Layer:
         return 2 * self.M * s.N * s.K
 
 
+SETTLE_S = 0.05  # --settle-ms
+
+
+def settle(replay):
+    """Run `replay` untimed, synchronising after each call, until SETTLE_S
+    seconds have passed.  Under continuous load the device's clocks take some
+    tens of milliseconds to settle (the fused decode step measures about 20 us
+    over the first few milliseconds from idle and 17.6 us from about 40 ms on),
+    so every graph-timed figure is taken after this."""
+    import time
+    import torch
+    t_end = time.perf_counter() + SETTLE_S
+    while True:
+        replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            return
+
+
 def time_region(tl, layer, steps, warmup, separate=False):
     """Wall time of `steps` back-to-back eager steps (events around the region)."""
     import torch
@@ -173,7 +192,8 @@ def time_graph_region(tl, layer, steps, warmup, separate=False):
     """Wall time of exactly `steps` steps replayed from one captured HIP graph.
 
     The graph holds `steps` consecutive steps (weights rotating over the
-    copies); it is replayed once untimed, then once inside the timed region.
+    copies); it is replayed untimed for SETTLE_S seconds (settle()), then once
+    inside the timed region.
     """
     import torch
     step = layer.step_separate if separate else layer.step
@@ -184,8 +204,7 @@ def time_graph_region(tl, layer, steps, warmup, separate=False):
     with torch.cuda.graph(g):
         for i in range(steps):
             step(tl, warmup + i)
-    g.replay()
-    torch.cuda.synchronize()
+    settle(g.replay)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -199,7 +218,7 @@ def time_graph_region(tl, layer, steps, warmup, separate=False):
 def time_per_shape(tl, layer, launches=64, reps=3):
     """Mean duration (s) of one launch of each projection: a graph of
     `launches` back-to-back launches of that projection (rotating copies),
-    replayed `reps` times between events on the launch stream."""
+    replayed `reps` times between events on the launch stream, after settle()."""
     import torch
     out = []
     for j in range(len(layer.shapes)):
@@ -207,8 +226,7 @@ def time_per_shape(tl, layer, launches=64, reps=3):
         with torch.cuda.graph(g):
             for i in range(launches):
                 layer.launch(tl, j, i)
-        g.replay()
-        torch.cuda.synchronize()
+        settle(g.replay)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
@@ -287,7 +305,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
             f"# HBM traffic of {what}",
             "# from two rocprofv3 --pmc runs of bench.py:",
             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- \\",
-            "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2",
+            "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2 --settle-ms 0",
             "#   (the same with --pmc WRITE_SIZE into <W>), then",
             "#   python3 bench.py --summarize-pmc <F> <W>",
             "# Counters read KiB per dispatch (summed over instances); each is scaled by what",
@@ -355,7 +373,7 @@ def summarize_mfma(*dirs) -> None:
     for cs in MFMA_PASSES:
         lines.append(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <D> -o bench -- \\")
         lines.append("#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
-                     "--prefill-steps 1 --prefill-warmup 2")
+                     "--prefill-steps 1 --prefill-warmup 2 --settle-ms 0")
     lines += [
         "#   python3 bench.py --summarize-mfma <D1> <D2>",
         "# Values are per dispatch (summed over counter instances), mean over the dispatches",
@@ -423,7 +441,7 @@ def summarize_valu(d: str) -> None:
         "# projections of the 7B layer at M=1, the largest gemv_stream_kernel dispatch), from",
         "#   rocprofv3 --pmc " + " ".join(VALU_PASS) + " --output-format csv -d <D> -o bench -- \\",
         "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
-        "--prefill-steps 1 --prefill-warmup 2",
+        "--prefill-steps 1 --prefill-warmup 2 --settle-ms 0",
         "#   python3 bench.py --summarize-valu <D>",
         "# VALUBusy and MfmaUtil are rocprofv3's derived percentages of the launch's GPU time;",
         "# wait_share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of the waves' lifetime spent",
@@ -609,7 +627,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
     per M from the M's own generator) are copied R times into one allocation,
     R * weight bytes >= 1 GiB where R <= max_copies, and a HIP graph of R
     launches (one per copy), captured after a warm-up on its capture stream,
-    is replayed between events on the stream it replays on."""
+    is replayed between events on the stream it replays on, after settle()."""
     import torch
     import numpy as np
     import synth
@@ -625,8 +643,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
         with torch.cuda.graph(g, stream=cap):
             for r in range(R):
                 fn(r)
-        g.replay()
-        torch.cuda.synchronize()
+        settle(g.replay)
         best = None
         for _ in range(2):
             # the replay runs on the current stream: the events go there too
@@ -747,8 +764,7 @@ def measure_ceilings(tl, layer_bytes, steps):
         with torch.cuda.graph(g):
             for i in range(steps):
                 tl.probe_read(views[i % nchunk], sink, wg)
-        g.replay()
-        torch.cuda.synchronize()
+        settle(g.replay)
         t = ev_time(lambda r: g.replay(), 1) / steps
         del g
         best = max(best, (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
@@ -795,6 +811,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=60,
                     help="untimed prefill steps first (clocks settle under sustained MFMA load)")
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed graph replays before each graph-timed figure (clocks settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4)")
@@ -804,6 +822,8 @@ def main():
     ap.add_argument("--summarize-valu", metavar="VALU_DIR")
     ap.add_argument("--detail", type=str, default=None, help="write per-shape results here")
     args = ap.parse_args()
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle_ms) / 1e3
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -956,8 +976,10 @@ def main():
                                "M=1, per-channel fp16 scales, bf16 x",
                    "M": 1, "global_batch": 1, "rotated_copies": rotated, "parallelism": "none"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "timing": "one HIP-graph replay of the K steps (one fused launch each); eager "
-                  "launches and seven separate launches per step reported beside",
+        "timing": f"one HIP-graph replay of the K steps (one fused launch each), after "
+                  f"{args.warmup} eager steps and {args.settle_ms:g} ms of untimed replays "
+                  "(clocks settle); eager launches and seven separate launches per step "
+                  "reported beside",
         "eager_value": round(eager_value, 1),
         "separate_launches_value": round(sep_value, 1),
         "roofline": roofline,
