@@ -586,14 +586,14 @@ __global__ void __launch_bounds__(kThreads)
 
 // K split of one problem: KP parts per block, a power of two up to kWaves so
 // that RB = kWaves / KP blocks fill the workgroup.  KP is the largest power
-// of two with parts of at least kSlabsPerPart slabs, doubled while a part
-// would exceed the one-shot length `one` (up to kWaves parts; longer parts
-// run with a window or in chunks).
-void split_k(int K, int one, int &kp, int &rb)
+// of two with parts of at least `target` slabs, doubled while a part would
+// exceed the one-shot length `one` (up to kWaves parts; longer parts run with
+// a window or in chunks).
+void split_k(int K, int one, int target, int &kp, int &rb)
 {
     const int nslabs = (K + 255) / 256;
     kp = 1;
-    while (2 * kp <= kWaves && 2 * kp * kSlabsPerPart <= nslabs)
+    while (2 * kp <= kWaves && 2 * kp * target <= nslabs)
         kp *= 2;
     while (kp < kWaves && (nslabs + kp - 1) / kp > one)
         kp *= 2;
@@ -662,41 +662,55 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
 {
     // One workgroup per block of 16 channels (per RB blocks at short K), in
     // the caller's problem order (longest K first: those workgroups live
-    // longest and start first).
+    // longest and start first).  Parts of about `target` slabs.
     StreamBatch b;
-    b.count = 0;
     int units = 0, mt = 0;
-    for (int oi = 0; oi < count; ++oi) {
-        const GemvArgs &a = args[order[oi]];
-        if (a.M == 0 || a.N == 0)
-            continue;
-        if (a.group != group || (mt != 0 && a.M != mt) || !gemv_stream_takes(a.M, a.K, group))
-            return hipErrorInvalidValue;
-        mt = a.M;
-        StreamProblem &p = b.p[b.count];
-        p.x = a.x;
-        p.packed = a.packed;
-        p.scale = a.scale;
-        p.y = a.y;
-        p.M = a.M;
-        p.N = a.N;
-        p.K = a.K;
-        p.group = group;
-        split_k(a.K, one_shot_of(kernel_mt(a.M), group), p.kp, p.rb);
-        const int nblocks = (a.N + 15) / 16;
-        p.rb = std::min(p.rb, nblocks);
-        p.rbi_map = 0;
-        p.kpi_map = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            const bool act = w < p.rb * p.kp;
-            p.rbi_map |= (uint64_t)(act ? w % p.rb : 15) << (4 * w);
-            p.kpi_map |= (uint64_t)(act ? w / p.rb : 15) << (4 * w);
+    auto fill = [&](int target) -> hipError_t {
+        b.count = 0;
+        units = 0;
+        mt = 0;
+        for (int oi = 0; oi < count; ++oi) {
+            const GemvArgs &a = args[order[oi]];
+            if (a.M == 0 || a.N == 0)
+                continue;
+            if (a.group != group || (mt != 0 && a.M != mt) || !gemv_stream_takes(a.M, a.K, group))
+                return hipErrorInvalidValue;
+            mt = a.M;
+            StreamProblem &p = b.p[b.count];
+            p.x = a.x;
+            p.packed = a.packed;
+            p.scale = a.scale;
+            p.y = a.y;
+            p.M = a.M;
+            p.N = a.N;
+            p.K = a.K;
+            p.group = group;
+            split_k(a.K, one_shot_of(kernel_mt(a.M), group), target, p.kp, p.rb);
+            const int nblocks = (a.N + 15) / 16;
+            p.rb = std::min(p.rb, nblocks);
+            p.rbi_map = 0;
+            p.kpi_map = 0;
+            for (int w = 0; w < kWaves; ++w) {
+                const bool act = w < p.rb * p.kp;
+                p.rbi_map |= (uint64_t)(act ? w % p.rb : 15) << (4 * w);
+                p.kpi_map |= (uint64_t)(act ? w / p.rb : 15) << (4 * w);
+            }
+            p.unit0 = units;
+            b.unit0[b.count] = units;
+            units += (nblocks + p.rb - 1) / p.rb;
+            ++b.count;
         }
-        p.unit0 = units;
-        b.unit0[b.count] = units;
-        units += (nblocks + p.rb - 1) / p.rb;
-        ++b.count;
-    }
+        return hipSuccess;
+    };
+    // Parts of kSlabsPerPart slabs; a launch whose workgroups would not cover
+    // the compute units once takes parts of half that, twice the workgroups
+    // (such launches are latency-bound: a 512 x 4096 problem at M = 1 takes
+    // 3.5 against 4.3 us).
+    hipError_t e = fill(kSlabsPerPart);
+    if (e == hipSuccess && b.count > 0 && units < device_cus())
+        e = fill(kSlabsPerPart / 2);
+    if (e != hipSuccess)
+        return e;
     if (b.count == 0)
         return hipSuccess;
     const dim3 grid(units), block(kThreads);
