@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -195,10 +195,18 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     const int group = group_of(group_size);
     if (path == TERNARY_PATH_AUTO)
         path = select_path(M, K, group);
+    const bool fp16 = dtype == TERNARY_FP16;
+    ternary::GemvKernel gk = ternary::GemvKernel::AUTO;
     switch (path) {
+    case TERNARY_PATH_GEMV_F4:
+    case TERNARY_PATH_GEMV_B16:
     case TERNARY_PATH_GEMV:
-        if (!(M == 0 || N == 0 || ternary::gemv_takes(M, K, group)))
+        gk = path == TERNARY_PATH_GEMV_F4 ? ternary::GemvKernel::F4
+             : path == TERNARY_PATH_GEMV_B16 ? ternary::GemvKernel::B16
+                                             : ternary::GemvKernel::AUTO;
+        if (!(M == 0 || N == 0 || ternary::gemv_kernel_takes(gk, M, K, group, fp16)))
             return TERNARY_ERR_PATH;
+        path = TERNARY_PATH_GEMV;
         break;
     case TERNARY_PATH_GEMM:
         if (!(M == 0 || N == 0 || ternary::gemm_takes(M, K, group)))
@@ -209,13 +217,13 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     }
     if (M == 0 || N == 0)
         return TERNARY_OK;
-    const bool fp16 = dtype == TERNARY_FP16;
     const uint16_t *xv = static_cast<const uint16_t *>(x);
     uint16_t *yv = static_cast<uint16_t *>(y);
     hipError_t e;
     switch (path) {
     case TERNARY_PATH_GEMV:
-        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream);
+        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
+                                 gk);
         break;
     case TERNARY_PATH_GEMM:
         e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream);
@@ -266,7 +274,7 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
         const ternary::GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
                                      static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
                                      group_of(p.group_size)};
-        if (ternary::gemv_preferred(p.M, p.K, a.group)) {
+        if (ternary::gemv_kernel_takes(ternary::GemvKernel::AUTO, p.M, p.K, a.group, fp16)) {
             fused[nf++] = a;
         } else if (ternary::gemm_takes(p.M, p.K, a.group) &&
                    ternary::gemm_big_takes(a.M, a.N, a.K, a.group, a.scale)) {

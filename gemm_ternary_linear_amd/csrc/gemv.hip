@@ -3,12 +3,26 @@
 // the kernel instances allow ([trdm] trdm.cn
 // "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §2.2: the segments of a
 // fused QKV weight share one launch, which pays the fixed launch and
-// first-byte latency once).  The kernel itself is gemv_stream.hip.
+// first-byte latency once).  Two decode kernels exist: gemv_f4.hip (codes as
+// fp4, activations as exact fp8 pieces, on the scaled fp4 x fp8 matrix
+// instruction; the default wherever its LDS holds the activations) and
+// gemv_stream.hip (codes as 16-bit +-2 / 0 on the bf16/fp16 matrix
+// instruction; every other decode shape).
 #include "internal.h"
 
 namespace ternary {
 
-hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
+bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16)
+{
+    switch (k) {
+    case GemvKernel::F4: return gemv_f4_takes(M, K, group, fp16);
+    case GemvKernel::B16: return gemv_stream_takes(M, K, group);
+    default: return gemv_f4_takes(M, K, group, fp16) || gemv_stream_takes(M, K, group);
+    }
+}
+
+hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
+                             GemvKernel kernel)
 {
     if (count < 1 || count > kGemvMaxBatch)
         return hipErrorInvalidValue;
@@ -23,36 +37,46 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             order[j] = order[j - 1];
             order[j - 1] = t;
         }
-    // Each group value (per channel, 32, 64, 128, 256) and each M is a
-    // separate kernel instance: one launch per non-empty class.
+    // Each group value (per channel, 32, 64, 128, 256), each M and each kernel
+    // is a separate instance: one launch per non-empty class.
     static const int kGroups[] = {0, 32, 64, 128, 256};
     for (const int group : kGroups) {
-        int idx[kGemvStreamMaxM][kGemvMaxBatch];
-        int n[kGemvStreamMaxM] = {};
+        int f4[kGemvMaxM][kGemvMaxBatch], b16[kGemvMaxM][kGemvMaxBatch];
+        int nf[kGemvMaxM] = {}, nb[kGemvMaxM] = {};
         for (int oi = 0; oi < count; ++oi) {
             const GemvArgs &a = args[order[oi]];
             if (a.group != group || a.M == 0 || a.N == 0)
                 continue;
-            if (!gemv_stream_takes(a.M, a.K, group))
+            const bool use_f4 = kernel != GemvKernel::B16 && gemv_f4_takes(a.M, a.K, group, fp16);
+            if (use_f4)
+                f4[a.M - 1][nf[a.M - 1]++] = order[oi];
+            else if (kernel != GemvKernel::F4 && gemv_stream_takes(a.M, a.K, group))
+                b16[a.M - 1][nb[a.M - 1]++] = order[oi];
+            else
                 return hipErrorInvalidValue;
-            idx[a.M - 1][n[a.M - 1]++] = order[oi];
         }
-        for (int m = 0; m < kGemvStreamMaxM; ++m) {
-            if (n[m] == 0)
-                continue;
-            const hipError_t e = launch_gemv_stream(args, idx[m], n[m], fp16, group, stream);
-            if (e != hipSuccess)
-                return e;
+        for (int m = 0; m < kGemvMaxM; ++m) {
+            if (nf[m]) {
+                const hipError_t e = launch_gemv_f4(args, f4[m], nf[m], fp16, group, stream);
+                if (e != hipSuccess)
+                    return e;
+            }
+            if (nb[m]) {
+                const hipError_t e = launch_gemv_stream(args, b16[m], nb[m], fp16, group, stream);
+                if (e != hipSuccess)
+                    return e;
+            }
         }
     }
     return hipSuccess;
 }
 
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream)
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
+                       GemvKernel kernel)
 {
     const GemvArgs a = {x, packed, scale, y, M, N, K, group};
-    return launch_gemv_batch(&a, 1, fp16, stream);
+    return launch_gemv_batch(&a, 1, fp16, stream, kernel);
 }
 
 }  // namespace ternary

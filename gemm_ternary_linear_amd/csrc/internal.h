@@ -43,18 +43,37 @@ hipError_t launch_quantize(const uint16_t *w, bool fp16, int N, int K, int group
 
 // All linear launchers: x/y are 2-byte elements (bf16 or fp16 by `fp16`),
 // `group` as in GemvArgs, shapes already validated by the caller.
+// Which decode kernel runs a GEMV problem: AUTO prefers the fp4 x fp8 one
+// wherever it takes the shape; F4 and B16 force one (parity tests, tuning).
+enum class GemvKernel { AUTO, F4, B16 };
+bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16);
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
-// Up to kGemvMaxBatch decode problems in one launch (all gemv_takes()).
-hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream);
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
+                       GemvKernel kernel = GemvKernel::AUTO);
+// Up to kGemvMaxBatch decode problems (all taken by `kernel`), one launch per
+// (kernel, scale mode, M) class.
+hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
+                             GemvKernel kernel = GemvKernel::AUTO);
 // Largest M the streaming decode kernel takes (M * gemv_cols(group) <= 16).
 constexpr int kGemvStreamMaxM = 8;
-// Whether the streaming decode kernel takes a gemv_takes() shape.
+// Whether the 16-bit streaming decode kernel (gemv_stream.hip) takes a shape.
 bool gemv_stream_takes(int64_t M, int64_t K, int group);
 // The problems args[order[0..count)] (all gemv_stream_takes(), one group
 // value, one M) in one launch of the streaming decode kernel.
 hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count, bool fp16,
                               int group, hipStream_t stream);
+// Decode GEMV on the scaled fp4 x fp8 matrix instruction (gemv_f4.hip):
+// largest M, and the most dynamic LDS a workgroup may take (the activations of
+// a problem live in LDS as fp8 pieces, 2 or 3 bytes per element and token).
+constexpr int kGemvF4MaxM = 8;
+constexpr int kGemvF4MaxLds = 80 * 1024;
+// Whether the fp4 x fp8 decode kernel takes a shape (M <= 8, K % 128 == 0,
+// the activation pieces fit in LDS).
+bool gemv_f4_takes(int64_t M, int64_t K, int group, bool fp16);
+// The problems args[order[0..count)] (all gemv_f4_takes(), one group value,
+// one M) in one launch of the fp4 x fp8 decode kernel.
+hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, bool fp16,
+                          int group, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
@@ -77,22 +96,21 @@ hipError_t release_workspaces();
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                          const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 
-// Shape requirements of the fast kernels.  The decode GEMV takes K up to
-// 65536 (a multiple of 128); a token's B columns times M fit the 16 MFMA
-// columns.
+// Shape requirements of the fast kernels.  The decode kernels take K up to
+// 65536 (a multiple of 128).
 constexpr int64_t kGemvMaxK = 65536;
-inline bool gemv_takes(int64_t M, int64_t K, int group)
-{
-    return M >= 1 && M <= kGemvMaxM && M * gemv_cols(group) <= 16 && K % 128 == 0 &&
-           K <= kGemvMaxK && (group == 0 || K % group == 0);
-}
 inline bool gemm_takes(int64_t M, int64_t K, int group)
 {
     return M >= 1 && K % 128 == 0 && (group == 0 || K % group == 0);
 }
-// The automatic choice: the decode GEMV wherever it takes the shape (measured
-// on MI355X, 7B down 4096 x 18944 at M = 8: GEMV 12.8 us, pipelined GEMM with
-// split K 23.7 us).
-inline bool gemv_preferred(int64_t M, int64_t K, int group) { return gemv_takes(M, K, group); }
+// The automatic GEMV/GEMM choice, the same for both activation dtypes: the
+// decode GEMV wherever one of its kernels takes the shape (fp16 activations
+// need the most LDS in the fp4 x fp8 kernel).  Measured on MI355X, the decode
+// kernels beat the GEMM at every M <= 8 they take (7B down 4096 x 18944 at
+// M = 8: GEMV 12.8 us, pipelined GEMM with split K 23.7 us).
+inline bool gemv_preferred(int64_t M, int64_t K, int group)
+{
+    return gemv_kernel_takes(GemvKernel::AUTO, M, K, group, true);
+}
 
 }  // namespace ternary

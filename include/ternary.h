@@ -77,9 +77,15 @@ typedef enum { TERNARY_BF16 = 0, TERNARY_FP16 = 1 } ternary_dtype;
 /* Kernel path for ternary_linear_ex.  AUTO picks by M (see ternary_linear). */
 typedef enum {
     TERNARY_PATH_AUTO = 0,
-    TERNARY_PATH_GEMV = 1,   /* decode kernel, requires 1 <= M <= ternary_gemv_max_m() */
-    TERNARY_PATH_GEMM = 2,   /* prefill kernel (LDS expansion + bf16/fp16 MFMA)        */
-    TERNARY_PATH_SIMPLE = 3  /* plain one-output-per-thread kernel, any valid shape    */
+    TERNARY_PATH_GEMV = 1,     /* decode GEMV, requires 1 <= M <= ternary_gemv_max_m();
+                                  the fp4 x fp8 kernel where it takes the shape, else
+                                  the 16-bit one                                       */
+    TERNARY_PATH_GEMM = 2,     /* prefill kernel (bf16/fp16 MFMA)                       */
+    TERNARY_PATH_SIMPLE = 3,   /* plain one-output-per-thread kernel, any valid shape   */
+    TERNARY_PATH_GEMV_F4 = 4,  /* decode GEMV on the scaled fp4 x fp8 matrix
+                                  instruction (codes as fp4, x as exact fp8 pieces)     */
+    TERNARY_PATH_GEMV_B16 = 5  /* decode GEMV on the bf16/fp16 matrix instruction
+                                  (codes as 16-bit +-2 / 0)                            */
 } ternary_path;
 
 /*

@@ -63,7 +63,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 3
+    assert tl.abi_version() == 4
     assert tl.gemv_max_m() == 8
     for st in range(0, -9, -1):
         s = tl.status_string(st)
@@ -106,8 +106,16 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(M=9, path=1), -8),                  # GEMV takes M <= 8 only
     (dict(K=132, g=-1, path=1), -8),          # fast kernels need K % 128 == 0
     (dict(K=132, g=-1, path=2), -8),
-    (dict(M=3, K=256, g=32, path=1), -8),     # g = 32 leaves 2 tokens per GEMV launch
-    (dict(M=5, K=256, g=64, path=1), -8),     # g = 64 leaves 4
+    (dict(M=3, K=256, g=32, path=5), -8),     # 16-bit decode kernel: g = 32 leaves 2 tokens
+    (dict(M=5, K=256, g=64, path=5), -8),     # g = 64 leaves 4
+    (dict(M=9, path=4), -8),                  # fp4 x fp8 decode kernel: M <= 8
+    (dict(K=132, g=-1, path=4), -8),
+    (dict(M=9, path=5), -8),
+    (dict(path=6), -8),
+    # fp4 x fp8 kernel: 8 tokens of K = 65536 do not fit its LDS (x is 1 MB here)
+    (dict(M=8, N=16, K=65536, g=-1, path=4, p=FAKE * 64, s=FAKE * 128, y=FAKE * 256), -8),
+    # fp16 activations at g = 64 and M = 5 take 8 matrix passes there (at most 4)
+    (dict(M=5, K=256, g=64, dtype=1, path=4), -8),
     # the GEMV takes K <= 65536
     (dict(M=1, K=65664, g=-1, path=1, p=FAKE * 16, s=FAKE * 64, y=FAKE * 128), -8),
     (dict(K=160, g=32, path=2), -8),          # fast kernels need K % 128 == 0

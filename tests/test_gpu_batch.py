@@ -67,9 +67,10 @@ def _run_and_check(tl, probs, dtype="bf16", samples=None):
 
 @pytest.mark.parametrize("M", [1, 8])
 def test_batch_7b_decode_layer(tl, M):
+    # every output of the fused decode launch against the oracle
     say(f"batch of the 7 decode projections, M={M}")
     specs = [(M, s.N, s.K, -1) for s in synth.CONFIGS[2].shapes]
-    _run_and_check(tl, _problems(np.random.default_rng(40 + M), specs), samples=800)
+    _run_and_check(tl, _problems(np.random.default_rng(40 + M), specs))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
