@@ -23,7 +23,12 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? TERNARY_OK : TERNARY_ERR_HIP; }
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return TERNARY_OK;
+    return e == ternary::kErrCaptureWorkspace ? TERNARY_ERR_WORKSPACE : TERNARY_ERR_HIP;
+}
 
 // Largest M, N or K accepted: kernels index channels, tokens and K with
 // 32-bit ints (element offsets are 64-bit) and grids stay far inside the
@@ -88,6 +93,75 @@ int select_path(int64_t M, int64_t K, int group)
 
 }  // namespace
 
+namespace ternary {
+
+int linear_batch(const ternary_problem *problems, int count, int dtype, hipStream_t stream)
+{
+    if (count < 1 || count > TERNARY_MAX_BATCH)
+        return TERNARY_ERR_SHAPE;
+    if (!problems)
+        return TERNARY_ERR_NULL;
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &p = problems[i];
+        const int st = check_linear(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y);
+        if (st != TERNARY_OK)
+            return st;
+    }
+    // No output may overlap another problem's inputs or output.
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &a = problems[i];
+        const int64_t ya = 2 * a.M * a.N;
+        for (int j = 0; j < count; ++j) {
+            if (i == j)
+                continue;
+            const ternary_problem &b = problems[j];
+            const int64_t sb = 2 * scale_elems(b.N, b.K, b.group_size);
+            if (overlap(a.y, ya, b.x, 2 * b.M * b.K) ||
+                overlap(a.y, ya, b.packed, b.N * (b.K / 4)) || overlap(a.y, ya, b.scale, sb) ||
+                overlap(a.y, ya, b.y, 2 * b.M * b.N))
+                return TERNARY_ERR_ALIAS;
+        }
+    }
+    // Plan every launch before the first one: decode problems fused, the
+    // pipelined GEMM's problems grouped, the rest one call each.
+    const bool fp16 = dtype == TERNARY_FP16;
+    GemvArgs fused[TERNARY_MAX_BATCH], grouped_gemm[TERNARY_MAX_BATCH];
+    int others[TERNARY_MAX_BATCH];
+    int nf = 0, ng = 0, no = 0;
+    for (int i = 0; i < count; ++i) {
+        const ternary_problem &p = problems[i];
+        if (p.M == 0 || p.N == 0)
+            continue;
+        const GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
+                            static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
+                            group_of(p.group_size)};
+        if (gemv_kernel_takes(GemvKernel::AUTO, p.M, p.K, a.group, fp16))
+            fused[nf++] = a;
+        else if (gemm_takes(p.M, p.K, a.group) && gemm_big_takes(a.M, a.N, a.K, a.group, a.scale))
+            grouped_gemm[ng++] = a;
+        else
+            others[no++] = i;
+    }
+    for (int oi = 0; oi < no; ++oi) {
+        // (the 128 x 128 GEMM and the plain kernel use no scratch)
+        const ternary_problem &p = problems[others[oi]];
+        const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,
+                                         p.group_size, p.y, TERNARY_PATH_AUTO, stream);
+        if (st != TERNARY_OK)
+            return st;
+    }
+    if (ng) {
+        const int st = hip_status(launch_gemm_batch(grouped_gemm, ng, fp16, stream));
+        if (st != TERNARY_OK)
+            return st;
+    }
+    if (nf)
+        return hip_status(launch_gemv_batch(fused, nf, fp16, stream));
+    return TERNARY_OK;
+}
+
+}  // namespace ternary
+
 extern "C" {
 
 int ternary_abi_version(void) { return kAbiVersion; }
@@ -111,6 +185,10 @@ const char *ternary_status_string(int status)
     case TERNARY_ERR_ALIAS: return "output overlaps an input";
     case TERNARY_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case TERNARY_ERR_PATH: return "forced kernel path cannot take this shape";
+    case TERNARY_ERR_WORKSPACE:
+        return "the stream is being captured and its split-K workspace is too small: run the same "
+               "call once outside capture first";
+
     default: return "unknown status";
     }
 }
@@ -239,61 +317,7 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
 int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
                          hipStream_t stream)
 {
-    if (count < 1 || count > TERNARY_MAX_BATCH)
-        return TERNARY_ERR_SHAPE;
-    if (!problems)
-        return TERNARY_ERR_NULL;
-    for (int i = 0; i < count; ++i) {
-        const ternary_problem &p = problems[i];
-        const int st = check_linear(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y);
-        if (st != TERNARY_OK)
-            return st;
-    }
-    // No output may overlap another problem's inputs or output.
-    for (int i = 0; i < count; ++i) {
-        const ternary_problem &a = problems[i];
-        const int64_t ya = 2 * a.M * a.N;
-        for (int j = 0; j < count; ++j) {
-            if (i == j)
-                continue;
-            const ternary_problem &b = problems[j];
-            const int64_t sb = 2 * scale_elems(b.N, b.K, b.group_size);
-            if (overlap(a.y, ya, b.x, 2 * b.M * b.K) ||
-                overlap(a.y, ya, b.packed, b.N * (b.K / 4)) || overlap(a.y, ya, b.scale, sb) ||
-                overlap(a.y, ya, b.y, 2 * b.M * b.N))
-                return TERNARY_ERR_ALIAS;
-        }
-    }
-    const bool fp16 = dtype == TERNARY_FP16;
-    ternary::GemvArgs fused[TERNARY_MAX_BATCH], grouped_gemm[TERNARY_MAX_BATCH];
-    int nf = 0, ng = 0;
-    for (int i = 0; i < count; ++i) {
-        const ternary_problem &p = problems[i];
-        if (p.M == 0 || p.N == 0)
-            continue;
-        const ternary::GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
-                                     static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
-                                     group_of(p.group_size)};
-        if (ternary::gemv_kernel_takes(ternary::GemvKernel::AUTO, p.M, p.K, a.group, fp16)) {
-            fused[nf++] = a;
-        } else if (ternary::gemm_takes(p.M, p.K, a.group) &&
-                   ternary::gemm_big_takes(a.M, a.N, a.K, a.group, a.scale)) {
-            grouped_gemm[ng++] = a;
-        } else {
-            const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,
-                                             p.group_size, p.y, TERNARY_PATH_AUTO, stream);
-            if (st != TERNARY_OK)
-                return st;
-        }
-    }
-    if (ng) {
-        const int st = hip_status(ternary::launch_gemm_batch(grouped_gemm, ng, fp16, stream));
-        if (st != TERNARY_OK)
-            return st;
-    }
-    if (nf)
-        return hip_status(ternary::launch_gemv_batch(fused, nf, fp16, stream));
-    return TERNARY_OK;
+    return ternary::linear_batch(problems, count, dtype, stream);
 }
 
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,

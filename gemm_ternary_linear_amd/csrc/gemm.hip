@@ -715,16 +715,15 @@ int big_ksplit(int tiles, int K, int ns, int tile_elems)
     return std::max(ks, 1);
 }
 
-// Launches the problems args[idx[0..count)) (all gemm_big_takes(), one scale
-// mode) as one grouped launch of the pipelined kernel, problems with the
-// longest K first so that the longest tiles start first.  When all their
-// tiles together do not cover the compute units, each problem's K range is
-// split as big_ksplit() says and per-problem reduce kernels follow.
-template <bool FP16, int GS, class C>
-hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipStream_t stream)
+// The plan of one grouped launch: problem order (longest K first, so that the
+// longest tiles start first), tiles and K slices per problem, and the bytes
+// of fp32 partial tiles the split problems need.  When all the tiles together
+// do not cover the compute units, each problem's K range is split as
+// big_ksplit() says.
+template <class C>
+size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order, int *tiles,
+                     int *ks)
 {
-    int order[kGemvMaxBatch];
-    int tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
     int64_t total = 0;
     for (int i = 0; i < count; ++i) {
         order[i] = i;
@@ -746,16 +745,33 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
         if (ks[i] > 1)
             ws_bytes += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
     }
+    return ws_bytes;
+}
+
+// Launches the problems args[idx[0..count)) (all gemm_big_takes(), one scale
+// mode) as one grouped launch of the pipelined kernel, plus one reduce launch
+// per problem whose K range is split.  The fp32 partials of split problems go
+// to `fixed` when given (the caller checked its size), else to the stream's
+// workspace.
+template <bool FP16, int GS, class C>
+hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipStream_t stream,
+                           const FixedScratch *fixed)
+{
+    int order[kGemvMaxBatch], tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
+    const size_t ws_bytes = plan_big_mode<C>(args, idx, count, order, tiles, ks);
     char *ws = nullptr;
     if (ws_bytes) {
-        void *w = nullptr;
-        const hipError_t e = stream_workspace(stream, ws_bytes, &w);
-        if (e != hipSuccess)
-            return e;
-        ws = static_cast<char *>(w);
-        if (!ws)  // under capture without a workspace: the unsplit kernel
-            for (int i = 0; i < count; ++i)
-                ks[i] = 1;
+        if (fixed) {
+            if (ws_bytes > fixed->bytes)
+                return hipErrorInvalidValue;
+            ws = static_cast<char *>(fixed->ptr);
+        } else {
+            void *w = nullptr;
+            const hipError_t e = stream_workspace(stream, ws_bytes, &w);
+            if (e != hipSuccess)
+                return e;
+            ws = static_cast<char *>(w);
+        }
     }
     dma::BigBatch b = {};
     b.count = count;
@@ -800,47 +816,78 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
 
 template <bool FP16, int GS>
 hipError_t launch_big_group(const GemvArgs *args, const int (*idx)[kGemvMaxBatch], const int *n,
-                            hipStream_t stream)
+                            hipStream_t stream, const FixedScratch *fixed)
 {
     hipError_t e = hipSuccess;
     if (n[0] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, TinyCfg>(args, idx[0], n[0], stream);
+        e = launch_big_mode<FP16, GS, TinyCfg>(args, idx[0], n[0], stream, fixed);
     if (n[1] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[1], n[1], stream);
+        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[1], n[1], stream, fixed);
     if (n[2] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[2], n[2], stream);
+        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[2], n[2], stream, fixed);
     if constexpr (GS == 0)  // group-scaled problems never take the large configuration
         if (n[3] && e == hipSuccess)
-            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[3], n[3], stream);
+            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[3], n[3], stream, fixed);
     return e;
 }
+
+// The batch's problems by (scale mode, configuration): one grouped launch each.
+struct BigClasses {
+    int idx[4][4][kGemvMaxBatch];
+    int n[4][4] = {};
+    BigClasses(const GemvArgs *args, int count)
+    {
+        static_assert(kGemvMaxBatch <= 8, "batch table");
+        for (int i = 0; i < count; ++i) {
+            const int g = args[i].group;
+            const int mode = g == 0 ? 0 : (g == 64 ? 1 : (g == 128 ? 2 : 3));
+            const int c = big_cfg_of(args[i].M, args[i].K, g);
+            idx[mode][c][n[mode][c]++] = i;
+        }
+    }
+};
 
 template <bool FP16>
-hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream)
+hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream,
+                                 const FixedScratch *fixed)
 {
-    // one launch per (group size, configuration) present
-    int idx[4][4][kGemvMaxBatch], n[4][4] = {};
-    static_assert(kGemvMaxBatch <= 8, "batch table");
-    for (int i = 0; i < count; ++i) {
-        const int g = args[i].group;
-        const int mode = g == 0 ? 0 : (g == 64 ? 1 : (g == 128 ? 2 : 3));
-        const int c = big_cfg_of(args[i].M, args[i].K, g);
-        idx[mode][c][n[mode][c]++] = i;
-    }
-    hipError_t e = launch_big_group<FP16, 0>(args, idx[0], n[0], stream);
+    const BigClasses cl(args, count);
+    hipError_t e = launch_big_group<FP16, 0>(args, cl.idx[0], cl.n[0], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 64>(args, idx[1], n[1], stream);
+        e = launch_big_group<FP16, 64>(args, cl.idx[1], cl.n[1], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 128>(args, idx[2], n[2], stream);
+        e = launch_big_group<FP16, 128>(args, cl.idx[2], cl.n[2], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 256>(args, idx[3], n[3], stream);
+        e = launch_big_group<FP16, 256>(args, cl.idx[3], cl.n[3], stream, fixed);
     return e;
 }
 
-hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream)
+size_t gemm_batch_scratch_need(const GemvArgs *args, int count)
 {
-    return fp16 ? launch_gemm_big_batch<true>(args, count, stream)
-                : launch_gemm_big_batch<false>(args, count, stream);
+    // the launches of one call run in stream order and reuse the buffer from
+    // its start: the need is the largest single launch's
+    const BigClasses cl(args, count);
+    int order[kGemvMaxBatch], tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
+    size_t need = 0;
+    for (int mode = 0; mode < 4; ++mode) {
+        const int *n = cl.n[mode];
+        if (n[0])
+            need = std::max(need, plan_big_mode<TinyCfg>(args, cl.idx[mode][0], n[0], order, tiles, ks));
+        if (n[1])
+            need = std::max(need, plan_big_mode<SmallCfg>(args, cl.idx[mode][1], n[1], order, tiles, ks));
+        if (n[2])
+            need = std::max(need, plan_big_mode<MidCfg>(args, cl.idx[mode][2], n[2], order, tiles, ks));
+        if (n[3] && mode == 0)
+            need = std::max(need, plan_big_mode<BigCfg>(args, cl.idx[mode][3], n[3], order, tiles, ks));
+    }
+    return need;
+}
+
+hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
+                             const FixedScratch *fixed)
+{
+    return fp16 ? launch_gemm_big_batch<true>(args, count, stream, fixed)
+                : launch_gemm_big_batch<false>(args, count, stream, fixed);
 }
 
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,

@@ -80,17 +80,32 @@ hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const 
                        const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 // Whether the pipelined (grouped) prefill kernel takes a problem.
 bool gemm_big_takes(int M, int N, int K, int group, const void *scale);
+// A caller-provided scratch buffer for split-K partial tiles (device memory
+// of `bytes` bytes), used instead of the per-stream workspace.
+struct FixedScratch {
+    void *ptr;
+    size_t bytes;
+};
 // Up to kGemvMaxBatch prefill problems (all gemm_big_takes()) in one grouped
 // launch per scale mode (plus one reduce launch per problem whose K range is
-// split).
-hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream);
+// split).  Split-K partials go to `fixed` if given (it must hold
+// gemm_batch_scratch_need() bytes), else to the stream's workspace.
+hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
+                             const FixedScratch *fixed = nullptr);
+// Scratch bytes launch_gemm_batch needs for these problems (0: no K split).
+size_t gemm_batch_scratch_need(const GemvArgs *args, int count);
 
 // Library-owned scratch of at least `bytes` for work on `stream` of the
-// current device.  While `stream` is being captured nothing is allocated:
-// *out is set to nullptr (with hipSuccess) when the stream has no workspace
-// that large yet.
+// current device.  While `stream` is being captured nothing is allocated: a
+// stream without a workspace that large returns kErrCaptureWorkspace.  A
+// workspace replaced by a larger one stays allocated until
+// release_workspaces() (a graph captured earlier may still use it).
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void **out);
-// Frees every workspace (after the work queued on its stream has finished).
+// The error stream_workspace() returns under capture when the stream's
+// workspace is too small (reported as TERNARY_ERR_WORKSPACE).
+constexpr hipError_t kErrCaptureWorkspace = hipErrorStreamCaptureUnsupported;
+// Frees every workspace, retired ones included, after waiting for the
+// devices that hold them.
 hipError_t release_workspaces();
 
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,

@@ -3,10 +3,13 @@
 // The split-K GEMM keeps its fp32 partial tiles here between its two
 // kernels.  A workspace belongs to one stream, so work on other streams never
 // shares it; calls on one stream run in order, so consecutive calls may reuse
-// it.
+// it.  A HIP graph captured on a stream keeps the workspace address it was
+// captured with, so a workspace replaced by a larger one is retired, not
+// freed: retired buffers live until ternary_shutdown().
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "internal.h"
 
@@ -21,6 +24,7 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_pool;
+std::vector<std::pair<int, void *>> g_retired;  // (device, buffer) replaced by larger ones
 
 }  // namespace
 
@@ -34,31 +38,23 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void **out)
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace &w = g_pool[{dev, stream}];
     if (w.bytes < bytes) {
-        // no allocation (nor free) while the stream is being captured
+        // nothing is allocated while the stream is being captured: the
+        // caller runs the same call once outside capture first
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         e = hipStreamIsCapturing(stream, &cap);
         if (e != hipSuccess)
             return e;
         if (cap != hipStreamCaptureStatusNone)
-            return hipSuccess;
-        if (w.ptr) {
-            // earlier work on this stream may still read the old buffer
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess)
-                return e;
-            e = hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess)
-                return e;
-        }
+            return kErrCaptureWorkspace;
         // round up to 16 MiB so that slowly growing shapes do not reallocate
         const size_t want = (bytes + (size_t(16) << 20) - 1) & ~((size_t(16) << 20) - 1);
-        e = hipMalloc(&w.ptr, want);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
+        void *p = nullptr;
+        e = hipMalloc(&p, want);
+        if (e != hipSuccess)
             return e;
-        }
+        if (w.ptr)
+            g_retired.push_back({dev, w.ptr});  // work queued or captured earlier may use it
+        w.ptr = p;
         w.bytes = want;
     }
     *out = w.ptr;
@@ -72,18 +68,29 @@ hipError_t release_workspaces()
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess)
         cur = -1;
-    for (auto &kv : g_pool) {
-        if (!kv.second.ptr)
-            continue;
-        hipError_t e = hipSetDevice(kv.first.first);
+    std::vector<std::pair<int, void *>> all = g_retired;
+    for (auto &kv : g_pool)
+        if (kv.second.ptr)
+            all.push_back({kv.first.first, kv.second.ptr});
+    // wait for every device that holds a buffer (its streams may still use
+    // them), then free them all
+    std::vector<int> synced;
+    for (auto &dp : all) {
+        hipError_t e = hipSetDevice(dp.first);
+        bool seen = false;
+        for (int d : synced)
+            seen = seen || d == dp.first;
+        if (e == hipSuccess && !seen) {
+            e = hipDeviceSynchronize();
+            synced.push_back(dp.first);
+        }
         if (e == hipSuccess)
-            e = hipStreamSynchronize(kv.first.second);
-        if (e == hipSuccess)
-            e = hipFree(kv.second.ptr);
+            e = hipFree(dp.second);
         if (e != hipSuccess && first == hipSuccess)
             first = e;
     }
     g_pool.clear();
+    g_retired.clear();
     if (cur >= 0)
         (void)hipSetDevice(cur);
     return first;

@@ -35,12 +35,13 @@
  *     caller memory.
  *   - The library owns one device workspace per (device, stream) for GEMM
  *     shapes whose K range it splits over several workgroups (fp32 partial
- *     tiles, added in a fixed order by a second kernel).  The first call on a stream that needs
- *     a larger one allocates it (hipMalloc).  Under stream capture nothing is
- *     allocated: a stream without a large enough workspace then runs the
- *     unsplit kernel, so warm a stream up (one call per shape) before
- *     capturing on it to capture the split kernel.  ternary_shutdown() frees
- *     them all.
+ *     tiles, added in a fixed order by a second kernel).  The first call on a
+ *     stream that needs a larger one allocates it (hipMalloc); the one it
+ *     replaces stays allocated (a graph captured earlier may use it) until
+ *     ternary_shutdown(), which frees them all.  Under stream capture nothing
+ *     is allocated: a call that would need a larger workspace returns
+ *     TERNARY_ERR_WORKSPACE, so warm a stream up (one call per shape) before
+ *     capturing on it.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
  *     Arguments are validated on the host before anything is launched; on any
  *     error a negative ternary_status is returned and nothing is enqueued.
@@ -68,7 +69,9 @@ typedef enum {
     TERNARY_ERR_ALIGN = -5,  /* a pointer is not aligned as documented           */
     TERNARY_ERR_ALIAS = -6,  /* the output overlaps an input                     */
     TERNARY_ERR_HIP = -7,    /* a HIP runtime call or kernel launch failed       */
-    TERNARY_ERR_PATH = -8    /* a forced kernel path cannot take this shape      */
+    TERNARY_ERR_PATH = -8,   /* a forced kernel path cannot take this shape      */
+    TERNARY_ERR_WORKSPACE = -9  /* stream under capture, its split-K workspace too
+                                   small: run the same call once outside capture */
 } ternary_status;
 
 /* Activation / output element type (2 bytes per element). */
@@ -219,12 +222,15 @@ const char *ternary_status_string(int status);
 int ternary_abi_version(void);
 
 /*
- * ternary_shutdown - free the library's workspaces.  Waits for the work queued
- * on each workspace's stream, then frees it; later calls allocate again as
- * needed.  Returns TERNARY_ERR_HIP if a synchronisation or free failed (the
- * remaining workspaces are still released).
+ * ternary_shutdown - free the library's workspaces, those replaced by larger
+ * ones included.  Waits for every device that holds one, then frees them;
+ * later calls allocate again as needed.  A HIP graph captured before with a
+ * split-K GEMM launch in it must not be replayed afterwards.  Returns
+ * TERNARY_ERR_HIP if a synchronisation or free failed (the remaining
+ * workspaces are still released).
  */
 int ternary_shutdown(void);
+
 
 #ifdef __cplusplus
 }
