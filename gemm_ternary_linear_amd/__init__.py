@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
     "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH", "probe_read", "probe_copy",
-    "probe_mfma", "probe_mfma_flops", "quantize",
+    "probe_mfma", "probe_mfma_flops", "quantize", "linear_batch_noalloc",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
@@ -39,6 +39,7 @@ EXPORTS = (
     "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
     "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
     "ternary_status_string", "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
+    "ternary_linear_batch_noalloc",
 )
 # Every symbol include/ternary_probe.h declares (measurement probes).
 PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_copy", "ternary_probe_mfma")
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.ternary_linear.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, p]
     L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
     L.ternary_linear_batch.argtypes = [p, i32, i32, p]
+    L.ternary_linear_batch_noalloc.argtypes = [p, i32, i32, p]
     L.ternary_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p]
     L.ternary_select_path.argtypes = [i64, i64, i64, i64]
     L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
                "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
-               *PROBE_EXPORTS):
+               "ternary_linear_batch_noalloc", *PROBE_EXPORTS):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -248,10 +250,13 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
     return out
 
 
-def linear_batch(problems) -> list:
+def linear_batch(problems, noalloc: bool = False) -> list:
     """Several projections in as few launches as possible (one for all decode
     shapes).  ``problems`` is a sequence of (x, packed, scale, group_size, out)
-    tuples (group_size and out may be None); returns the outputs."""
+    tuples (group_size and out may be None); returns the outputs.  With
+    ``noalloc`` the call goes to ternary_linear_batch_noalloc (split-K scratch
+    in the library's static array; no device memory is allocated by the
+    library; the outputs are allocated here unless given)."""
     n = len(problems)
     if not 1 <= n <= MAX_BATCH:
         raise ValueError(f"1..{MAX_BATCH} problems per batch")
@@ -266,10 +271,16 @@ def linear_batch(problems) -> list:
         outs.append(out)
     if len(dts) != 1:
         raise ValueError("all problems of a batch share one activation dtype")
-    st = lib().ternary_linear_batch(arr, n, dts.pop(), _stream(problems[0][0]))
+    fn = lib().ternary_linear_batch_noalloc if noalloc else lib().ternary_linear_batch
+    st = fn(arr, n, dts.pop(), _stream(problems[0][0]))
     if st:
-        raise TernaryError(st, "ternary_linear_batch")
+        raise TernaryError(st, "ternary_linear_batch_noalloc" if noalloc else "ternary_linear_batch")
     return outs
+
+
+def linear_batch_noalloc(problems) -> list:
+    """linear_batch through ternary_linear_batch_noalloc."""
+    return linear_batch(problems, noalloc=True)
 
 
 # ---------------------------------------------------------------- probes

@@ -95,7 +95,8 @@ int select_path(int64_t M, int64_t K, int group)
 
 namespace ternary {
 
-int linear_batch(const ternary_problem *problems, int count, int dtype, hipStream_t stream)
+int linear_batch(const ternary_problem *problems, int count, int dtype, hipStream_t stream,
+                 bool noalloc)
 {
     if (count < 1 || count > TERNARY_MAX_BATCH)
         return TERNARY_ERR_SHAPE;
@@ -142,6 +143,18 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
         else
             others[no++] = i;
     }
+    FixedScratch fs = {nullptr, 0};
+    if (noalloc) {
+        // split-K partials go to the library's static scratch: check its size
+        // before anything is enqueued
+        const size_t need = ng ? gemm_batch_scratch_need(grouped_gemm, ng) : 0;
+        if (need > noalloc_scratch_bytes())
+            return TERNARY_ERR_SCRATCH;
+        const int st = hip_status(noalloc_scratch(&fs.ptr));
+        if (st != TERNARY_OK)
+            return st;
+        fs.bytes = noalloc_scratch_bytes();
+    }
     for (int oi = 0; oi < no; ++oi) {
         // (the 128 x 128 GEMM and the plain kernel use no scratch)
         const ternary_problem &p = problems[others[oi]];
@@ -151,7 +164,8 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
             return st;
     }
     if (ng) {
-        const int st = hip_status(launch_gemm_batch(grouped_gemm, ng, fp16, stream));
+        const int st = hip_status(launch_gemm_batch(grouped_gemm, ng, fp16, stream,
+                                                    noalloc ? &fs : nullptr));
         if (st != TERNARY_OK)
             return st;
     }
@@ -188,7 +202,8 @@ const char *ternary_status_string(int status)
     case TERNARY_ERR_WORKSPACE:
         return "the stream is being captured and its split-K workspace is too small: run the same "
                "call once outside capture first";
-
+    case TERNARY_ERR_SCRATCH:
+        return "the call needs more split-K scratch than the library's static buffer holds";
     default: return "unknown status";
     }
 }
@@ -317,7 +332,7 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
 int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
                          hipStream_t stream)
 {
-    return ternary::linear_batch(problems, count, dtype, stream);
+    return ternary::linear_batch(problems, count, dtype, stream, false);
 }
 
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,

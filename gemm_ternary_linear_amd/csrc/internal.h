@@ -108,6 +108,12 @@ constexpr hipError_t kErrCaptureWorkspace = hipErrorStreamCaptureUnsupported;
 // devices that hold them.
 hipError_t release_workspaces();
 
+// The allocation-free variant's scratch (noalloc.hip): the device address of
+// this device's copy of the library's static scratch array (looked up once per
+// device), and its size.
+hipError_t noalloc_scratch(void **out);
+size_t noalloc_scratch_bytes();
+
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                          const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
 

@@ -41,7 +41,7 @@
  *     ternary_shutdown(), which frees them all.  Under stream capture nothing
  *     is allocated: a call that would need a larger workspace returns
  *     TERNARY_ERR_WORKSPACE, so warm a stream up (one call per shape) before
- *     capturing on it.
+ *     capturing on it.  ternary_linear_batch_noalloc allocates nothing.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
  *     Arguments are validated on the host before anything is launched; on any
  *     error a negative ternary_status is returned and nothing is enqueued.
@@ -70,8 +70,10 @@ typedef enum {
     TERNARY_ERR_ALIAS = -6,  /* the output overlaps an input                     */
     TERNARY_ERR_HIP = -7,    /* a HIP runtime call or kernel launch failed       */
     TERNARY_ERR_PATH = -8,   /* a forced kernel path cannot take this shape      */
-    TERNARY_ERR_WORKSPACE = -9  /* stream under capture, its split-K workspace too
+    TERNARY_ERR_WORKSPACE = -9, /* stream under capture, its split-K workspace too
                                    small: run the same call once outside capture */
+    TERNARY_ERR_SCRATCH = -10   /* ternary_linear_batch_noalloc: the call needs more
+                                   split-K scratch than TERNARY_NOALLOC_SCRATCH_BYTES */
 } ternary_status;
 
 /* Activation / output element type (2 bytes per element). */
@@ -231,6 +233,24 @@ int ternary_abi_version(void);
  */
 int ternary_shutdown(void);
 
+/* Bytes of the static scratch array of ternary_linear_batch_noalloc. */
+#define TERNARY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * ternary_linear_batch_noalloc - ternary_linear_batch for callers that cannot
+ * allocate device memory: code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, validation, results (the
+ * same bits) and launches as ternary_linear_batch, but the fp32 partial tiles
+ * of a split-K GEMM go to a static device array of the library
+ * (TERNARY_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead
+ * of the per-stream workspace: the call never allocates or frees.  A batch
+ * whose split-K partials need more returns TERNARY_ERR_SCRATCH and enqueues
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on a GPU (other streams, other host threads) race, and a graph captured with
+ * it must not be replayed while another such call runs on the GPU.
+ */
+int ternary_linear_batch_noalloc(const ternary_problem *problems, int count, int dtype,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -65,7 +65,7 @@ def test_no_oracle_linkage(tl):
 def test_versions_and_strings(tl):
     assert tl.abi_version() == 4
     assert tl.gemv_max_m() == 8
-    for st in range(0, -10, -1):
+    for st in range(0, -11, -1):
         s = tl.status_string(st)
         assert s and s != "unknown status"
     assert tl.status_string(-99) == "unknown status"
