@@ -548,6 +548,18 @@ def stored_mfma():
 
 # ---------------------------------------------------------------- CPU baseline
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        for ln in Path("/proc/cpuinfo").read_text().splitlines():
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline_decode(layer):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
@@ -564,6 +576,7 @@ def cpu_baseline_decode(layer):
     t = sorted(times)[1]
     total = sum(layer.bytes_per_launch(j) for j in range(len(layer.shapes)))
     return {"value": round(total / t / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "full 7B decode layer (7 projections, M=1, per-channel), fp64 oracle, "
                       "median of 3 runs",
             "seconds_per_layer": round(t, 4)}
@@ -581,7 +594,7 @@ def cpu_baseline_prefill(layer, tokens=8):
         t += time.perf_counter() - t0
         flops += 2 * tokens * c.shape.N * c.shape.K
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": used,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"first {tokens} of the 2048 tokens through all 7 projections, fp64 oracle"}
 
 

@@ -161,14 +161,18 @@ def pack(q: torch.Tensor, invalid_count: torch.Tensor | None = None) -> torch.Te
 
 
 def unpack(packed: torch.Tensor, K: int | None = None) -> torch.Tensor:
-    """uint8 (or int8 reinterpreted) [N, K/4] -> int8 [N, K]."""
-    _dev(packed, "packed")
+    """uint8 (or int8 reinterpreted) [N, K/4] -> int8 [N, K].  ``K``, if given,
+    must be the row length the packed bytes hold (4 codes per byte)."""
     if packed.dtype == torch.int8:
         packed = packed.view(torch.uint8)
     if packed.dtype != torch.uint8 or packed.dim() != 2:
         raise ValueError("packed must be a 2-D uint8/int8 tensor")
     N = packed.shape[0]
-    K = packed.shape[1] * 4 if K is None else K
+    if K is not None and K != packed.shape[1] * 4:
+        raise ValueError(f"K={K} does not match the packed rows ({packed.shape[1]} bytes hold "
+                         f"K={packed.shape[1] * 4})")
+    K = packed.shape[1] * 4
+    _dev(packed, "packed")
     out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
     _check(lib().ternary_unpack(packed.data_ptr(), N, K, out.data_ptr(), _stream(packed)),
            "ternary_unpack")

@@ -290,9 +290,10 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     const int ch0 = rb * 16 + 4 * g;
     uint32_t chs = 0;
     if constexpr (!GROUPED) {
-        const __amdgpu_buffer_rsrc_t sr = make_rsrc(P.scale, (uint32_t)N * 2u);
-        const int ch = ch0 + (lane & 3);
-        chs = __builtin_amdgcn_raw_buffer_load_b16(sr, ch < N ? ch * 2 : kOOB, 0, 0);
+        const __amdgpu_buffer_rsrc_t sr =
+            make_rsrc(nrows > 0 ? P.scale + (int64_t)rb * 16 : P.scale, (uint32_t)nrows * 2u);
+        const int r = 4 * g + (lane & 3);
+        chs = __builtin_amdgcn_raw_buffer_load_b16(sr, r < nrows ? r * 2 : kOOB, 0, 0);
     }
     int *const cnt = reinterpret_cast<int *>(smem + L.cnt_base);
     if (KP > 1 && tid < kWaves)
@@ -336,7 +337,11 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     // group scales: this wave's staging area and this lane's row offset
     uint16_t *const gsb = reinterpret_cast<uint16_t *>(smem + L.gs_base) + wave * (kSP * G::GPS * 16);
     const int ngroups = GROUPED ? (K >> G::GLOG) : 1;
-    const __amdgpu_buffer_rsrc_t gsr = make_rsrc(P.scale, GROUPED ? (uint32_t)N * (uint32_t)ngroups * 2u : 0u);
+    // group scales: the resource starts at the block's first row (64-bit
+    // pointer arithmetic), so offsets stay below 16 rows of scales
+    const __amdgpu_buffer_rsrc_t gsr =
+        make_rsrc(GROUPED && nrows > 0 ? P.scale + (int64_t)rb * 16 * ngroups : P.scale,
+                  GROUPED ? (uint32_t)(nrows * ngroups * 2) : 0u);
 
     f32x4_t acc[NPASS];
 #pragma unroll
@@ -361,7 +366,7 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
             for (int i = 0; i < NG / 4; ++i) {
                 const int lg = (lane >> 4) + 4 * i, row = lane & 15;
                 const int gi = g_first + lg;
-                const int off = row < nrows && gi < ngroups ? ((rb * 16 + row) * ngroups + gi) * 2 : kOOB;
+                const int off = row < nrows && gi < ngroups ? (row * ngroups + gi) * 2 : kOOB;
                 gsb[lg * 16 + row] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(gsr, off, 0, 0);
             }
             __builtin_amdgcn_wave_barrier();

@@ -448,9 +448,12 @@ __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t 
 // GC: B columns per token (gemv_cols of the group size: 2 for per-channel
 // scales and groups of 128 K or more, 4 for 64, 8 for 32); column GC*t + p
 // holds token t restricted to group p of each slab (half p when GC = 2).
+// (per-channel instances of 2 or more tokens are held to 64 VGPRs, 8 waves per
+// SIMD; the 1-token per-channel instance, whose one-shot parts hold 8 slabs of
+// codes, and the group-scaled ones keep the registers they need: no scratch)
 template <bool FP16, bool GROUPED, int GC, int MT>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(GROUPED ? 1 : 8))) gemv_stream_kernel(const StreamBatch batch)
+    __attribute__((amdgpu_waves_per_eu(GROUPED || MT == 1 ? 1 : 8))) gemv_stream_kernel(const StreamBatch batch)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -507,14 +510,18 @@ __global__ void __launch_bounds__(kThreads)
     c.wr = make_rsrc(wbase, (uint32_t)(nrows * rowbytes));
     c.woff = col * rowbytes + c.g * 16;
     c.xr = make_rsrc(P.x, (uint32_t)M * (uint32_t)K * 2u);
-    c.sr = make_rsrc(P.scale, (uint32_t)N * (uint32_t)(GROUPED ? ngroups : 1) * 2u);
-    c.srow_off = (lane & 15) < nrows ? (rb * 16 + (lane & 15)) * ngroups * 2 : -1;
+    // the scale resource starts at the block's first row (64-bit pointer
+    // arithmetic), so its 32-bit offsets stay below 16 rows of scales
+    const int spr = GROUPED ? ngroups : 1;  // scales per row
+    const uint16_t *sbase = nrows > 0 ? P.scale + (int64_t)rb * 16 * spr : P.scale;
+    c.sr = make_rsrc(sbase, (uint32_t)(nrows * spr * 2));
+    c.srow_off = (lane & 15) < nrows ? (lane & 15) * spr * 2 : -1;
     uint16_t *wlds = reinterpret_cast<uint16_t *>(smem) + wave * wave_lds_elems<GC, MT, GROUPED>();
     c.xbuf = wlds;
     c.sbuf = wlds + x_area_elems<MT, GROUPED>();
 
-    const int chs_ch = rb * 16 + 4 * c.g + (lane & 3);
-    c.chs_off = chs_ch < N ? chs_ch * 2 : kOOB;
+    const int chs_r = 4 * c.g + (lane & 3);
+    c.chs_off = chs_r < nrows ? chs_r * 2 : kOOB;
 
     uint32_t chs = 0u;
     const f32x4_t acc = run_part_n<FP16, GROUPED, GC, MT>(c, S, chs);

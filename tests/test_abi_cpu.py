@@ -243,3 +243,13 @@ def test_probe_rejects(tl):
     assert L.ternary_probe_mfma(64, (1 << 20) + 1, A, None) == SHAPE
     assert L.ternary_probe_mfma(64, 4, None, None) == NULL
     assert L.ternary_probe_mfma(64, 4, A + 2, None) == ALIGN
+
+
+def test_binding_unpack_rejects_wrong_K(tl):
+    # K must be the row length the packed bytes hold; a larger K would read
+    # past the buffer, a smaller one would return a wrong flat prefix
+    import torch
+    p = torch.zeros((3, 16), dtype=torch.uint8)
+    for K in (60, 68, 128, 4):
+        with pytest.raises(ValueError, match="does not match the packed rows"):
+            tl.unpack(p, K)

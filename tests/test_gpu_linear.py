@@ -470,3 +470,51 @@ def test_stream_full_ring(tl, M, N, K, g, kernel):
     yv = _run(tl, x, packed, scale, g, "bf16", path=kernel)
     y_ref, bound = oracle.linear(x, packed, scale, g)
     check_within(yv, y_ref, bound, f"ring {kernel} M={M} N={N} K={K} g={g}")
+
+
+def test_ternary_linear_entry_point_through_ctypes(tl):
+    # the C entry point ternary_linear itself (the binding calls ternary_linear_ex)
+    import ctypes
+    import torch
+    say("ternary_linear through ctypes")
+    rng = np.random.default_rng(12)
+    for M, N, K, g in ((1, 300, 4096, -1), (3, 200, 2048, 128), (100, 130, 1024, -1)):
+        codes, packed, scale, x = _case(rng, M, N, K, g, "bf16")
+        xd, pd, sd = to_dev(x, torch.bfloat16), to_dev(packed, None), to_dev(scale, torch.float16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        st = tl.lib().ternary_linear(xd.data_ptr(), 0, M, N, K, pd.data_ptr(), sd.data_ptr(), g,
+                                     y.data_ptr(),
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert st == 0
+        y_ref, bound = oracle.linear(x, packed, scale, g)
+        check_within(widen(bits_of(y), "bf16"), y_ref, bound, f"ternary_linear M={M}")
+
+
+@pytest.mark.parametrize("kernel,K", [("gemv_b16", 65536), ("gemv_f4", 16384)])
+def test_scale_offsets_past_2GiB(tl, kernel, K):
+    # groups of 32: 2 GiB of scales, so the last rows' scale offsets pass 2^31
+    # bytes; those rows hold +1 / -1 codes with power-of-two scales and x = 1,
+    # every other row zero codes and zero scales, so y is exact
+    import torch
+    say(f"scale offsets past 2 GiB {kernel} K={K}")
+    g, ngroups = 32, K // 32
+    N = (1 << 31) // (ngroups * 2) + 48
+    packed = torch.zeros((N, K // 4), dtype=torch.uint8, device="cuda:0")
+    scale = torch.zeros((N, ngroups), dtype=torch.float16, device="cuda:0")
+    packed[N - 1] = 0x55                  # codes +1
+    packed[N - 2] = 0xAA                  # codes -1
+    packed[N - 40] = 0x55
+    scale[N - 1] = 2.0 ** -4
+    scale[N - 2] = 2.0 ** -3
+    scale[N - 40] = 2.0 ** -5
+    x = torch.ones((1, K), dtype=torch.bfloat16, device="cuda:0")
+    y = tl.linear(x, packed, scale, g, path=kernel)
+    torch.cuda.synchronize()
+    yv = y.float().cpu().numpy()[0]
+    assert yv[N - 1] == K * 2.0 ** -4 and yv[N - 2] == -K * 2.0 ** -3 and yv[N - 40] == K * 2.0 ** -5
+    mask = np.ones(N, bool)
+    mask[[N - 1, N - 2, N - 40]] = False
+    assert np.all(yv[mask] == 0.0)
+    del packed, scale
+    torch.cuda.empty_cache()
