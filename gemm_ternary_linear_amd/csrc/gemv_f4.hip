@@ -344,9 +344,22 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
                   GROUPED ? (uint32_t)(nrows * ngroups * 2) : 0u);
 
     f32x4_t acc[NPASS];
+    // B operands of every pass.  With one pass they are kept across slabs:
+    // lanes whose column holds no piece, and the half of a grouped column's K
+    // blocks that is not its group's, stay zero, and only the rest is reloaded
+    // from LDS every slab.  With more passes, keeping them would take more
+    // than 128 registers (half the occupancy) in some instances, so they are
+    // cleared and reloaded every slab.
+    constexpr bool KEEPB = NPASS == 1;
+    i32x8_t bo[NPASS][2];
+    uint32_t bsw[NPASS];
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps)
+    for (int ps = 0; ps < NPASS; ++ps) {
         acc[ps] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        bo[ps][0] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        bo[ps][1] = bo[ps][0];
+        bsw[ps] = 0;
+    }
 
     for (int c0 = 0; c0 < S; c0 += kSP) {
         if (c0 > 0) {
@@ -386,36 +399,45 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
             const i32x8_t A1 = {(int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3], 0, 0, 0, 0};
 #pragma unroll
             for (int ps = 0; ps < NPASS; ++ps) {
-                u32x4_t p0 = {0, 0, 0, 0}, p1 = p0, p2 = p0, p3 = p0;
-                uint32_t sw = 0;
+                if constexpr (!KEEPB) {
+                    bo[ps][0] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    bo[ps][1] = bo[ps][0];
+                    bsw[ps] = 0;
+                }
                 if (bvalid[ps]) {
                     const unsigned char *src = smem + bbase[ps] + s * 256;
                     if (keep_lo) {
-                        p0 = *reinterpret_cast<const u32x4_t *>(src);
-                        p2 = *reinterpret_cast<const u32x4_t *>(src + 128);
+                        const u32x4_t p0 = *reinterpret_cast<const u32x4_t *>(src);
+                        const u32x4_t p2 = *reinterpret_cast<const u32x4_t *>(src + 128);
+                        bo[ps][0][0] = (int)p0.x; bo[ps][0][1] = (int)p0.y;
+                        bo[ps][0][2] = (int)p0.z; bo[ps][0][3] = (int)p0.w;
+                        bo[ps][1][0] = (int)p2.x; bo[ps][1][1] = (int)p2.y;
+                        bo[ps][1][2] = (int)p2.z; bo[ps][1][3] = (int)p2.w;
                     }
                     if (keep_hi) {
-                        p1 = *reinterpret_cast<const u32x4_t *>(src + 64);
-                        p3 = *reinterpret_cast<const u32x4_t *>(src + 192);
+                        const u32x4_t p1 = *reinterpret_cast<const u32x4_t *>(src + 64);
+                        const u32x4_t p3 = *reinterpret_cast<const u32x4_t *>(src + 192);
+                        bo[ps][0][4] = (int)p1.x; bo[ps][0][5] = (int)p1.y;
+                        bo[ps][0][6] = (int)p1.z; bo[ps][0][7] = (int)p1.w;
+                        bo[ps][1][4] = (int)p3.x; bo[ps][1][5] = (int)p3.y;
+                        bo[ps][1][6] = (int)p3.z; bo[ps][1][7] = (int)p3.w;
                     }
-                    sw = *reinterpret_cast<const uint16_t *>(smem + sbase[ps] + 8 * s);
+                    bsw[ps] = *reinterpret_cast<const uint16_t *>(smem + sbase[ps] + 8 * s);
                 }
-                const i32x8_t B0 = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
-                                    (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-                const i32x8_t B1 = {(int)p2.x, (int)p2.y, (int)p2.z, (int)p2.w,
-                                    (int)p3.x, (int)p3.y, (int)p3.z, (int)p3.w};
                 if constexpr (!GROUPED) {
                     acc[ps] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        A0, B0, acc[ps], 4, 0, 0, 127, 0, (int)sw);
+                        A0, bo[ps][0], acc[ps], 4, 0, 0, 127, 0, (int)bsw[ps]);
                     acc[ps] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        A1, B1, acc[ps], 4, 0, 0, 127, 1, (int)sw);
+                        A1, bo[ps][1], acc[ps], 4, 0, 0, 127, 1, (int)bsw[ps]);
                 } else {
                     // this lane's column holds one group of the slab (per
                     // MFMA for groups of 32): fold its partial with the scale
                     // of rows 4g .. 4g+3
                     const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-                    f32x4_t d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B0, z4, 4, 0, 0, 127, 0, (int)sw);
-                    f32x4_t d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B1, GMODE == 4 ? z4 : d0, 4, 0, 0, 127, 1, (int)sw);
+                    f32x4_t d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A0, bo[ps][0], z4, 4, 0, 0, 127, 0, (int)bsw[ps]);
+                    f32x4_t d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A1, bo[ps][1], GMODE == 4 ? z4 : d0, 4, 0, 0, 127, 1, (int)bsw[ps]);
                     auto fold = [&](int lgrp, f32x4_t d) {
                         const uint2 s4 = *reinterpret_cast<const uint2 *>(gsb + lgrp * 16 + 4 * g);
                         acc[ps][0] += f16_bits_to_f32((uint16_t)s4.x) * d[0];
