@@ -26,20 +26,23 @@ import torch
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
     "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH", "probe_read", "probe_copy",
-    "probe_mfma", "probe_mfma_flops", "quantize", "linear_batch_noalloc",
+    "probe_mfma", "probe_mfma_flops", "quantize", "linear_batch_noalloc", "tile", "untile",
+    "tiled_bytes", "LAYOUTS",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
 
 BF16, FP16 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3, "gemv_f4": 4, "gemv_b16": 5}
+LAYOUTS = {"rows": 0, "tiled": 1}
 
 # Every symbol include/ternary.h declares.
 EXPORTS = (
     "ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
     "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
     "ternary_status_string", "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
-    "ternary_linear_batch_noalloc",
+    "ternary_linear_batch_noalloc", "ternary_tile", "ternary_untile", "ternary_tiled_bytes",
+    "ternary_linear_tiled",
 )
 # Every symbol include/ternary_probe.h declares (measurement probes).
 PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_copy", "ternary_probe_mfma")
@@ -51,7 +54,8 @@ class Problem(ctypes.Structure):
     """ternary_problem of include/ternary.h."""
     _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
-                ("K", ctypes.c_int64), ("group_size", ctypes.c_int64)]
+                ("K", ctypes.c_int64), ("group_size", ctypes.c_int64),
+                ("layout", ctypes.c_int64)]
 
 _lib = None
 
@@ -77,6 +81,11 @@ def lib() -> ctypes.CDLL:
     L.ternary_unpack.argtypes = [p, i64, i64, p, p]
     L.ternary_linear.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, p]
     L.ternary_linear_ex.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
+    L.ternary_linear_tiled.argtypes = [p, i32, i64, i64, i64, p, p, i64, p, i32, p]
+    L.ternary_tile.argtypes = [p, i64, i64, p, p]
+    L.ternary_untile.argtypes = [p, i64, i64, p, p]
+    L.ternary_tiled_bytes.argtypes = [i64, i64]
+    L.ternary_tiled_bytes.restype = i64
     L.ternary_linear_batch.argtypes = [p, i32, i32, p]
     L.ternary_linear_batch_noalloc.argtypes = [p, i32, i32, p]
     L.ternary_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p]
@@ -89,7 +98,8 @@ def lib() -> ctypes.CDLL:
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
                "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
-               "ternary_linear_batch_noalloc", *PROBE_EXPORTS):
+               "ternary_linear_batch_noalloc", "ternary_linear_tiled", "ternary_tile",
+               "ternary_untile", *PROBE_EXPORTS):
         getattr(L, nm).restype = i32
     _lib = L
     return L
@@ -182,6 +192,43 @@ def unpack(packed: torch.Tensor, K: int | None = None) -> torch.Tensor:
 _ACT = {torch.bfloat16: BF16, torch.float16: FP16}
 
 
+def tiled_bytes(N: int, K: int) -> int:
+    """Bytes of the tiled layout of an [N, K] code matrix (ternary_tiled_bytes)."""
+    r = int(lib().ternary_tiled_bytes(N, K))
+    if r < 0:
+        raise TernaryError(r, "ternary_tiled_bytes")
+    return r
+
+
+def tile(packed: torch.Tensor) -> torch.Tensor:
+    """Row-major codes uint8 [N, K/4] -> the library's tiled layout, a uint8
+    tensor [ceil(N/16), ceil(K/256), 1024] (one kilobyte per block of 16 rows x
+    256 codes; include/ternary.h gives the byte order)."""
+    if packed.dtype == torch.int8:
+        packed = packed.view(torch.uint8)
+    if packed.dtype != torch.uint8 or packed.dim() != 2:
+        raise ValueError("packed must be a 2-D uint8/int8 tensor")
+    _dev(packed, "packed")
+    N, K = packed.shape[0], packed.shape[1] * 4
+    out = torch.empty(((N + 15) // 16, (K + 255) // 256, 1024), dtype=torch.uint8,
+                      device=packed.device)
+    assert out.numel() == tiled_bytes(N, K)
+    _check(lib().ternary_tile(packed.data_ptr(), N, K, out.data_ptr(), _stream(packed)),
+           "ternary_tile")
+    return out
+
+
+def untile(tiled: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    """The inverse of tile(): tiled codes of an [N, K] matrix -> uint8 [N, K/4]."""
+    _dev(tiled, "tiled")
+    if tiled.dtype != torch.uint8 or tiled.numel() != tiled_bytes(N, K):
+        raise ValueError(f"tiled must be uint8 with {tiled_bytes(N, K)} bytes for N={N}, K={K}")
+    out = torch.empty((N, K // 4), dtype=torch.uint8, device=tiled.device)
+    _check(lib().ternary_untile(tiled.data_ptr(), N, K, out.data_ptr(), _stream(tiled)),
+           "ternary_untile")
+    return out
+
+
 def quantize(w: torch.Tensor, group_size: int = 128):
     """bf16/fp16 weights [N, K] -> (packed uint8 [N, K/4], fp16 scales [N] or
     [N, K/group_size]) by ternary_quantize: per group s = max|w| (fp16),
@@ -199,8 +246,12 @@ def quantize(w: torch.Tensor, group_size: int = 128):
     return packed, scale
 
 
-def _check_problem(x, packed, scale, group_size, out):
-    """Shapes/dtypes of one problem checked against each other -> (dt, M, N, K, g, packed, out)."""
+def _check_problem(x, packed, scale, group_size, out, layout="rows"):
+    """Shapes/dtypes of one problem checked against each other -> (dt, M, N, K, g, packed, out).
+    Row-major codes are [N, K/4]; tiled ones any uint8 tensor of tiled_bytes(N, K)
+    bytes, N then being taken from the scale's first dimension."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {tuple(LAYOUTS)}")
     dt = _ACT.get(x.dtype)
     if dt is None:
         raise ValueError("x must be bfloat16 or float16")
@@ -209,14 +260,22 @@ def _check_problem(x, packed, scale, group_size, out):
     xs, ps, ss = x.shape, packed.shape, scale.shape
     if len(xs) != 2:
         raise ValueError("x must be 2-D [M, K] (flatten leading dimensions first)")
-    if packed.dtype != torch.uint8 or len(ps) != 2:
-        raise ValueError("packed must be a 2-D uint8/int8 tensor")
     if scale.dtype != torch.float16:
         raise ValueError("scale must be float16")
     M, K = xs
-    N = ps[0]
-    if ps[1] * 4 != K:
-        raise ValueError(f"packed has {ps[1]} bytes per row, K={K} needs {K // 4}")
+    if layout == "tiled":
+        if packed.dtype != torch.uint8 or not len(ss):
+            raise ValueError("tiled codes must be a uint8 tensor; scale gives N")
+        N = ss[0]
+        if packed.numel() != tiled_bytes(N, K):
+            raise ValueError(f"tiled codes hold {packed.numel()} bytes, N={N}, K={K} needs "
+                             f"{tiled_bytes(N, K)}")
+    else:
+        if packed.dtype != torch.uint8 or len(ps) != 2:
+            raise ValueError("packed must be a 2-D uint8/int8 tensor")
+        N = ps[0]
+        if ps[1] * 4 != K:
+            raise ValueError(f"packed has {ps[1]} bytes per row, K={K} needs {K // 4}")
     if group_size is None:
         group_size = -1 if len(ss) == 1 else (K // ss[1] if ss[1] else 0)
     if group_size == -1:
@@ -238,26 +297,31 @@ def _check_problem(x, packed, scale, group_size, out):
 
 def linear(x: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
            group_size: int | None = None, path: str = "auto",
-           out: torch.Tensor | None = None) -> torch.Tensor:
+           out: torch.Tensor | None = None, layout: str = "rows") -> torch.Tensor:
     """y [M, N] = x [M, K] @ (q * s)^T in x's dtype (bf16 or fp16).
 
     ``scale`` is fp16 [N] (per channel) or [N, K/group_size]; ``group_size`` is
     inferred from its shape when not given.  ``path`` forces a kernel
-    ("gemv", "gemm", "simple"); "auto" picks by M.  Shapes are checked here
-    against each other, so the sizes passed to the C ABI match the tensors.
+    ("gemv", "gemm", "simple", "gemv_f4", "gemv_b16"); "auto" picks by M.
+    ``layout`` is "rows" (packed [N, K/4]) or "tiled" (packed from tile()).
+    Shapes are checked here against each other, so the sizes passed to the C
+    ABI match the tensors.
     """
-    dt, M, N, K, group_size, packed, out = _check_problem(x, packed, scale, group_size, out)
-    st = lib().ternary_linear_ex(x.data_ptr(), dt, M, N, K, packed.data_ptr(), scale.data_ptr(),
-                                 group_size, out.data_ptr(), PATHS[path], _stream(x))
+    dt, M, N, K, group_size, packed, out = _check_problem(x, packed, scale, group_size, out,
+                                                          layout)
+    fn = lib().ternary_linear_tiled if layout == "tiled" else lib().ternary_linear_ex
+    st = fn(x.data_ptr(), dt, M, N, K, packed.data_ptr(), scale.data_ptr(), group_size,
+            out.data_ptr(), PATHS[path], _stream(x))
     if st:
-        raise TernaryError(st, "ternary_linear")
+        raise TernaryError(st, "ternary_linear_tiled" if layout == "tiled" else "ternary_linear")
     return out
 
 
 def linear_batch(problems, noalloc: bool = False) -> list:
     """Several projections in as few launches as possible (one for all decode
     shapes).  ``problems`` is a sequence of (x, packed, scale, group_size, out)
-    tuples (group_size and out may be None); returns the outputs.  With
+    tuples, optionally with a sixth element, the layout ("rows" or "tiled");
+    group_size and out may be None; returns the outputs.  With
     ``noalloc`` the call goes to ternary_linear_batch_noalloc (split-K scratch
     in the library's static array; no device memory is allocated by the
     library; the outputs are allocated here unless given)."""
@@ -267,11 +331,13 @@ def linear_batch(problems, noalloc: bool = False) -> list:
     arr = (Problem * n)()
     outs = []
     dts = set()
-    for i, (x, packed, scale, g, out) in enumerate(problems):
-        dt, M, N, K, g, packed, out = _check_problem(x, packed, scale, g, out)
+    for i, prob in enumerate(problems):
+        x, packed, scale, g, out = prob[:5]
+        layout = prob[5] if len(prob) > 5 else "rows"
+        dt, M, N, K, g, packed, out = _check_problem(x, packed, scale, g, out, layout)
         dts.add(dt)
         arr[i] = Problem(x.data_ptr(), packed.data_ptr(), scale.data_ptr(), out.data_ptr(),
-                         M, N, K, g)
+                         M, N, K, g, LAYOUTS[layout])
         outs.append(out)
     if len(dts) != 1:
         raise ValueError("all problems of a batch share one activation dtype")

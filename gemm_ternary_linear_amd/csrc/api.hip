@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -60,8 +60,14 @@ int check_shape(int64_t M, int64_t N, int64_t K, int64_t group_size)
     return TERNARY_OK;
 }
 
+// Bytes of a problem's codes in its layout.
+int64_t code_bytes(int64_t N, int64_t K, bool tiled)
+{
+    return tiled ? ternary::tiled_bytes(N, K) : N * (K / 4);
+}
+
 int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                 const uint16_t *scale, int64_t group_size, const void *y)
+                 const uint16_t *scale, int64_t group_size, const void *y, bool tiled = false)
 {
     if (dtype != TERNARY_BF16 && dtype != TERNARY_FP16)
         return TERNARY_ERR_DTYPE;
@@ -76,7 +82,7 @@ int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, cons
         return TERNARY_ERR_ALIGN;
     const int64_t ybytes = 2 * M * N;
     const int64_t sbytes = 2 * scale_elems(N, K, group_size);
-    if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, packed, N * (K / 4)) ||
+    if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, packed, code_bytes(N, K, tiled)) ||
         overlap(y, ybytes, scale, sbytes))
         return TERNARY_ERR_ALIAS;
     return TERNARY_OK;
@@ -89,6 +95,81 @@ int select_path(int64_t M, int64_t K, int group)
     if (ternary::gemm_takes(M, K, group))
         return TERNARY_PATH_GEMM;
     return TERNARY_PATH_SIMPLE;
+}
+
+// The automatic choice for tiled codes: the decode GEMV as for row-major
+// codes, else the pipelined GEMM (the 128 x 128 kernel reads row-major codes
+// only), else the plain kernel.
+int select_path_tiled(int64_t M, int64_t N, int64_t K, int group, const void *scale)
+{
+    if (ternary::gemv_preferred(M, K, group))
+        return TERNARY_PATH_GEMV;
+    if (ternary::gemm_big_takes((int)M, (int)N, (int)K, group, scale, true))
+        return TERNARY_PATH_GEMM;
+    return TERNARY_PATH_SIMPLE;
+}
+
+// One linear problem after validation: path choice (AUTO or forced) and launch.
+int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+               const uint16_t *scale, int64_t group_size, void *y, int path, bool tiled,
+               hipStream_t stream)
+{
+    const int group = group_of(group_size);
+    const bool fp16 = dtype == TERNARY_FP16;
+    if (path == TERNARY_PATH_AUTO)
+        path = tiled ? select_path_tiled(M, N, K, group, scale) : select_path(M, K, group);
+    ternary::GemvKernel gk = ternary::GemvKernel::AUTO;
+    switch (path) {
+    case TERNARY_PATH_GEMV_F4:
+    case TERNARY_PATH_GEMV_B16:
+    case TERNARY_PATH_GEMV:
+        gk = path == TERNARY_PATH_GEMV_F4 ? ternary::GemvKernel::F4
+             : path == TERNARY_PATH_GEMV_B16 ? ternary::GemvKernel::B16
+                                             : ternary::GemvKernel::AUTO;
+        if (!(M == 0 || N == 0 || ternary::gemv_kernel_takes(gk, M, K, group, fp16, tiled)))
+            return TERNARY_ERR_PATH;
+        path = TERNARY_PATH_GEMV;
+        break;
+    case TERNARY_PATH_GEMM:
+        if (!(M == 0 || N == 0 ||
+              (tiled ? ternary::gemm_big_takes((int)M, (int)N, (int)K, group, scale, true)
+                     : ternary::gemm_takes(M, K, group))))
+            return TERNARY_ERR_PATH;
+        break;
+    case TERNARY_PATH_SIMPLE: break;
+    default: return TERNARY_ERR_PATH;
+    }
+    if (M == 0 || N == 0)
+        return TERNARY_OK;
+    const uint16_t *xv = static_cast<const uint16_t *>(x);
+    uint16_t *yv = static_cast<uint16_t *>(y);
+    hipError_t e;
+    switch (path) {
+    case TERNARY_PATH_GEMV:
+        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
+                                 gk, tiled);
+        break;
+    case TERNARY_PATH_GEMM:
+        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
+                                 tiled);
+        break;
+    default:
+        e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv,
+                                   stream, tiled);
+        break;
+    }
+    return hip_status(e);
+}
+
+// Shape checks of ternary_tile / ternary_untile (and the size they imply).
+int check_tile_shape(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || K % 4 != 0 || N > kMaxDim || K > kMaxDim)
+        return TERNARY_ERR_SHAPE;
+    // one thread per 16 bytes, grids below 2^32 workgroups
+    if (ternary::tiled_bytes(N, K) > ((int64_t)1 << 40))
+        return TERNARY_ERR_SHAPE;
+    return TERNARY_OK;
 }
 
 }  // namespace
@@ -104,7 +185,10 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
         return TERNARY_ERR_NULL;
     for (int i = 0; i < count; ++i) {
         const ternary_problem &p = problems[i];
-        const int st = check_linear(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y);
+        if (p.layout != TERNARY_LAYOUT_ROWS && p.layout != TERNARY_LAYOUT_TILED)
+            return TERNARY_ERR_SHAPE;
+        const int st = check_linear(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y,
+                                    p.layout == TERNARY_LAYOUT_TILED);
         if (st != TERNARY_OK)
             return st;
     }
@@ -118,7 +202,8 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
             const ternary_problem &b = problems[j];
             const int64_t sb = 2 * scale_elems(b.N, b.K, b.group_size);
             if (overlap(a.y, ya, b.x, 2 * b.M * b.K) ||
-                overlap(a.y, ya, b.packed, b.N * (b.K / 4)) || overlap(a.y, ya, b.scale, sb) ||
+                overlap(a.y, ya, b.packed, code_bytes(b.N, b.K, b.layout == TERNARY_LAYOUT_TILED)) ||
+                overlap(a.y, ya, b.scale, sb) ||
                 overlap(a.y, ya, b.y, 2 * b.M * b.N))
                 return TERNARY_ERR_ALIAS;
         }
@@ -133,12 +218,14 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
         const ternary_problem &p = problems[i];
         if (p.M == 0 || p.N == 0)
             continue;
+        const bool tiled = p.layout == TERNARY_LAYOUT_TILED;
         const GemvArgs a = {static_cast<const uint16_t *>(p.x), p.packed, p.scale,
                             static_cast<uint16_t *>(p.y), (int)p.M, (int)p.N, (int)p.K,
-                            group_of(p.group_size)};
-        if (gemv_kernel_takes(GemvKernel::AUTO, p.M, p.K, a.group, fp16))
+                            group_of(p.group_size), tiled ? 1 : 0};
+        if (gemv_kernel_takes(GemvKernel::AUTO, p.M, p.K, a.group, fp16, tiled))
             fused[nf++] = a;
-        else if (gemm_takes(p.M, p.K, a.group) && gemm_big_takes(a.M, a.N, a.K, a.group, a.scale))
+        else if (gemm_takes(p.M, p.K, a.group) &&
+                 gemm_big_takes(a.M, a.N, a.K, a.group, a.scale, tiled))
             grouped_gemm[ng++] = a;
         else
             others[no++] = i;
@@ -158,8 +245,8 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
     for (int oi = 0; oi < no; ++oi) {
         // (the 128 x 128 GEMM and the plain kernel use no scratch)
         const ternary_problem &p = problems[others[oi]];
-        const int st = ternary_linear_ex(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale,
-                                         p.group_size, p.y, TERNARY_PATH_AUTO, stream);
+        const int st = linear_one(p.x, dtype, p.M, p.N, p.K, p.packed, p.scale, p.group_size, p.y,
+                                  TERNARY_PATH_AUTO, p.layout == TERNARY_LAYOUT_TILED, stream);
         if (st != TERNARY_OK)
             return st;
     }
@@ -285,48 +372,55 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
     const int st = check_linear(x, dtype, M, N, K, packed, scale, group_size, y);
     if (st != TERNARY_OK)
         return st;
-    const int group = group_of(group_size);
-    if (path == TERNARY_PATH_AUTO)
-        path = select_path(M, K, group);
-    const bool fp16 = dtype == TERNARY_FP16;
-    ternary::GemvKernel gk = ternary::GemvKernel::AUTO;
-    switch (path) {
-    case TERNARY_PATH_GEMV_F4:
-    case TERNARY_PATH_GEMV_B16:
-    case TERNARY_PATH_GEMV:
-        gk = path == TERNARY_PATH_GEMV_F4 ? ternary::GemvKernel::F4
-             : path == TERNARY_PATH_GEMV_B16 ? ternary::GemvKernel::B16
-                                             : ternary::GemvKernel::AUTO;
-        if (!(M == 0 || N == 0 || ternary::gemv_kernel_takes(gk, M, K, group, fp16)))
-            return TERNARY_ERR_PATH;
-        path = TERNARY_PATH_GEMV;
-        break;
-    case TERNARY_PATH_GEMM:
-        if (!(M == 0 || N == 0 || ternary::gemm_takes(M, K, group)))
-            return TERNARY_ERR_PATH;
-        break;
-    case TERNARY_PATH_SIMPLE: break;
-    default: return TERNARY_ERR_PATH;
-    }
-    if (M == 0 || N == 0)
+    return linear_one(x, dtype, M, N, K, packed, scale, group_size, y, path, false, stream);
+}
+
+int ternary_linear_tiled(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                         const uint8_t *tiled, const uint16_t *scale, int64_t group_size, void *y,
+                         int path, hipStream_t stream)
+{
+    const int st = check_linear(x, dtype, M, N, K, tiled, scale, group_size, y, true);
+    if (st != TERNARY_OK)
+        return st;
+    return linear_one(x, dtype, M, N, K, tiled, scale, group_size, y, path, true, stream);
+}
+
+int64_t ternary_tiled_bytes(int64_t N, int64_t K)
+{
+    const int st = check_tile_shape(N, K);
+    return st != TERNARY_OK ? st : ternary::tiled_bytes(N, K);
+}
+
+int ternary_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, hipStream_t stream)
+{
+    const int st = check_tile_shape(N, K);
+    if (st != TERNARY_OK)
+        return st;
+    if (N == 0 || K == 0)
         return TERNARY_OK;
-    const uint16_t *xv = static_cast<const uint16_t *>(x);
-    uint16_t *yv = static_cast<uint16_t *>(y);
-    hipError_t e;
-    switch (path) {
-    case TERNARY_PATH_GEMV:
-        e = ternary::launch_gemv(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
-                                 gk);
-        break;
-    case TERNARY_PATH_GEMM:
-        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream);
-        break;
-    default:
-        e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv,
-                                   stream);
-        break;
-    }
-    return hip_status(e);
+    if (!packed || !tiled)
+        return TERNARY_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(tiled, 16))
+        return TERNARY_ERR_ALIGN;
+    if (overlap(tiled, ternary::tiled_bytes(N, K), packed, N * (K / 4)))
+        return TERNARY_ERR_ALIAS;
+    return hip_status(ternary::launch_tile(packed, N, K, tiled, stream));
+}
+
+int ternary_untile(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *packed, hipStream_t stream)
+{
+    const int st = check_tile_shape(N, K);
+    if (st != TERNARY_OK)
+        return st;
+    if (N == 0 || K == 0)
+        return TERNARY_OK;
+    if (!packed || !tiled)
+        return TERNARY_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(tiled, 16))
+        return TERNARY_ERR_ALIGN;
+    if (overlap(tiled, ternary::tiled_bytes(N, K), packed, N * (K / 4)))
+        return TERNARY_ERR_ALIAS;
+    return hip_status(ternary::launch_untile(tiled, N, K, packed, stream));
 }
 
 int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,

@@ -290,6 +290,7 @@ struct BigProblem {
     uint16_t *y;
     float4 *partial;
     int M, N, K, ksplit;
+    int tiled;  // codes in the tiled layout (else row-major [N, K/4])
 };
 
 // The problems of one launch; workgroups wg0[i] .. wg0[i+1]-1 belong to
@@ -397,9 +398,18 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     // + tid of the stage (lanes of a wave write consecutive chunks).
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(x), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
+    // Codes: a K step is 16 bytes of each row.  Row-major, row n's 16 bytes of
+    // step kc sit at n * K/4 + 16 kc; tiled (K % 256 == 0 here), the 16 rows
+    // of a block have their 16 bytes of step kc together, 256 contiguous
+    // bytes at block * (K/256) KB + 256 kc (row n % 16 at 16 (n % 16)).
+    const bool tiled = P.tiled != 0;
+    const int nblk = (N + 15) >> 4;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(packed), (short)0, (int)((uint32_t)N * (uint32_t)(K >> 2)),
+        const_cast<uint8_t *>(packed), (short)0,
+        tiled ? (int)((uint32_t)nblk * 16u * (uint32_t)(K >> 2))
+              : (int)((uint32_t)N * (uint32_t)(K >> 2)),
         0x00020000);
+    const int wstep = tiled ? 256 : TK / 4;  // bytes between K steps of one row
     int xoff[C::XI], woff[C::WI];
 #pragma unroll
     for (int i = 0; i < C::XI; ++i) {
@@ -410,8 +420,10 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
     for (int i = 0; i < C::WI; ++i) {
         const int d = i * THREADS + tid;
-        const int row = d >> 2;
-        woff[i] = n0 + row < N ? (n0 + row) * (K >> 2) + 4 * (d & 3) : kOOB;
+        const int row = d >> 2, n = n0 + row;
+        woff[i] = n >= N ? kOOB
+                  : tiled ? (n >> 4) * (K >> 8) * 1024 + (n & 15) * 16 + 4 * (d & 3)
+                          : n * (K >> 2) + 4 * (d & 3);
     }
     // Scales: thread t loads channel n0 + t's pair of groups.
     const int ngroups = K / (GROUPED ? GS : 1);
@@ -433,7 +445,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
             dma_to_lds<16>(xr, (void *)(lx[s] + i * THREADS + wave_chunk), xoff[i], kc * (TK * 2));
 #pragma unroll
         for (int i = 0; i < C::WI; ++i)
-            dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * (TK / 4));
+            dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * wstep);
         if constexpr (GROUPED)  // the dword holding group kc / SPG
             dma_to_lds<4>(sr, (void *)(lsc[s] + wave_chunk), soff, ((kc >> GSH) >> 1) * 4);
     };
@@ -671,10 +683,10 @@ int big_cfg_of(int M, int K, int group)
 // (group scales) groups of 64, 128 or 256 K whose scale array is 4-byte
 // aligned with an even number of groups per row: it loads a channel's scales
 // of two consecutive groups as one dword.
-bool gemm_big_takes(int M, int N, int K, int group, const void *scale)
+bool gemm_big_takes(int M, int N, int K, int group, const void *scale, bool tiled)
 {
     if (M < 1 || N < 1 || K % (dma::TK * BigCfg::NS) != 0 || (int64_t)M * K * 2 >= dma::kOOB ||
-        (int64_t)N * (K / 4) >= dma::kOOB)
+        (tiled ? tiled_bytes(N, K) : (int64_t)N * (K / 4)) >= dma::kOOB)
         return false;
     if (group == 0)
         return true;
@@ -794,6 +806,7 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
         p.N = a.N;
         p.K = a.K;
         p.ksplit = ks[i];
+        p.tiled = a.tiled;
         b.wg0[r] = wg;
         wg += tiles[i] * ks[i];
     }
@@ -891,12 +904,15 @@ hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStre
 }
 
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream)
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
+                       bool tiled)
 {
-    if (gemm_big_takes(M, N, K, group, scale)) {
-        const GemvArgs a = {x, packed, scale, y, M, N, K, group};
+    if (gemm_big_takes(M, N, K, group, scale, tiled)) {
+        const GemvArgs a = {x, packed, scale, y, M, N, K, group, tiled ? 1 : 0};
         return launch_gemm_batch(&a, 1, fp16, stream);
     }
+    if (tiled)  // the 128 x 128 kernel reads row-major codes only
+        return hipErrorInvalidValue;
     const int glog = group ? group_log2(group) : 0;
     if (fp16)
         return group ? launch_gemm_t<true, true>(x, M, N, K, packed, scale, glog, y, stream)

@@ -7,12 +7,12 @@
 // fp4, activations as exact fp8 pieces, on the scaled fp4 x fp8 matrix
 // instruction; the default wherever its LDS holds the activations) and
 // gemv_stream.hip (codes as 16-bit +-2 / 0 on the bf16/fp16 matrix
-// instruction; every other decode shape).
+// instruction; every other decode shape).  Both read row-major and tiled codes.
 #include "internal.h"
 
 namespace ternary {
 
-bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16)
+bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16, bool tiled)
 {
     switch (k) {
     case GemvKernel::F4: return gemv_f4_takes(M, K, group, fp16);
@@ -73,9 +73,9 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
 
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
-                       GemvKernel kernel)
+                       GemvKernel kernel, bool tiled)
 {
-    const GemvArgs a = {x, packed, scale, y, M, N, K, group};
+    const GemvArgs a = {x, packed, scale, y, M, N, K, group, tiled ? 1 : 0};
     return launch_gemv_batch(&a, 1, fp16, stream, kernel);
 }
 

@@ -30,10 +30,15 @@
 //    K parts (RB * KP = 8).  It converts its problem's whole x into LDS once
 //    (all 512 lanes, 8 elements each), while every wave's first code loads
 //    are already in flight; then each wave runs its part in one-shot chunks
-//    of up to 8 slabs (a slab is 256 codes = 64 bytes of each of the block's
-//    16 rows, one 16-byte buffer load per lane).  K parts meet in LDS: the
-//    last wave of a block adds them in part order (deterministic) and writes
-//    y.
+//    of 4 slabs (8 for instances with several MFMA passes; a slab is 256
+//    codes = 64 bytes of each of the block's 16 rows, one 16-byte buffer load
+//    per lane).  K parts meet in LDS: the last wave of a block adds them in
+//    part order (deterministic) and writes y.
+//  * Code layouts.  Row-major codes ([trdm] §3.1) give each load instruction
+//    16 rows x 64 bytes; the library's tiled layout stores every slab of a
+//    block as one kilobyte in the A operand's lane order, so the same load
+//    reads one contiguous kilobyte (measured 14.2 against 15.3 us for the 7B
+//    decode layer at M = 1).  Only the address arithmetic differs.
 //  * Scales.  Per-channel scales ([nxbn] §3.2) multiply the final sum.  Group
 //    scales ([trdm] §3.1/§4.2: 128; [xxqk] §4.2: 64; yangyitao.com vLLM book,
 //    chapter 13, §13.3.3: 32, 256) multiply each group's fp32 partial: a
@@ -52,11 +57,13 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kSP = 8;        // slabs per one-shot chunk
 constexpr int kOOB = 0x40000000;
 constexpr int kPad = 64;      // bytes between two pieces in LDS (B reads of
                               // neighbouring columns fall on other banks)
-constexpr int kPreLoads = 2;  // x loads per lane issued before the codes
+// x loads per lane issued before the codes: all of a single token's x up to
+// K = 24576, fewer with more tokens (registers)
+template <int MT>
+constexpr int pre_loads() { return MT == 1 ? 6 : 2; }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -72,6 +79,9 @@ struct Geo {
     static constexpr int CPT = NP * GC <= 2 ? 2 : (NP * GC <= 4 ? 4 : (NP * GC <= 8 ? 8 : 16));
     static constexpr int TP = 16 / CPT;                           // tokens per MFMA pass
     static constexpr int NPASS = (MT + TP - 1) / TP;
+    // slabs per one-shot chunk of code loads: 4 with one MFMA pass (measured
+    // faster than 8 on the 7B decode layer), 8 with more (4 costs registers)
+    static constexpr int SP = NPASS == 1 ? 4 : 8;
     static constexpr int GPS = GMODE == 0 ? 0 : (GMODE == 1 ? 1 : (GMODE == 2 ? 2 : (GMODE == 3 ? 4 : 8)));  // groups per slab
     static constexpr int GLOG = GMODE == 1 ? 8 : (GMODE == 2 ? 7 : (GMODE == 3 ? 6 : 5));
 };
@@ -81,7 +91,7 @@ struct Geo {
 //                                       (K block kb of MFMA j at s*256 + j*128
 //                                       + 32 kb, in the fp4 operand's order)
 //   scales  [MT][NP][Kp / 32] bytes     E8M0 of 32-element block 8 s + 2 kb + j
-//   gscale  [kWaves][kSP * GPS][16]     fp16 group scales of a wave's chunk
+//   gscale  [kWaves][SP * GPS][16]      fp16 group scales of a wave's chunk
 //   red     [kWaves][NPASS][64] f32x4   K-part partial sums
 //   cnt     [kWaves] int
 struct Lds {
@@ -97,7 +107,7 @@ __host__ __device__ inline Lds lds_layout(int K)
     L.sc_base = MT * G::NP * L.piece_stride;
     L.sc_stride = Kp >> 5;
     L.gs_base = (L.sc_base + MT * G::NP * L.sc_stride + 15) & ~15;
-    L.red_base = L.gs_base + (G::GPS ? kWaves * kSP * G::GPS * 16 * 2 : 0);
+    L.red_base = L.gs_base + (G::GPS ? kWaves * G::SP * G::GPS * 16 * 2 : 0);
     L.cnt_base = L.red_base + kWaves * G::NPASS * 64 * 16;
     L.bytes = L.cnt_base + kWaves * 4;
     return L;
@@ -111,6 +121,7 @@ struct F4Problem {
     int M, N, K;
     int rb, kp;   // 16-channel blocks per workgroup, K parts per block (rb * kp = kWaves)
     int unit0;    // first workgroup of the problem
+    int tiled;    // codes in the tiled layout (else row-major [N, K/4])
 };
 struct F4Batch {
     int count;
@@ -259,6 +270,7 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
         const int tok = t / tasks_per_tok, e = (t - tok * tasks_per_tok) * 8;
         return (t < ntask && e < K) ? (tok * K + e) * 2 : kOOB;
     };
+    constexpr int kPreLoads = pre_loads<MT>();
     u32x4_t xv[kPreLoads];
 #pragma unroll
     for (int p = 0; p < kPreLoads; ++p) {
@@ -273,16 +285,28 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     const int s_begin = active ? kpi * nslabs / KP : 0;
     const int S = __builtin_amdgcn_readfirstlane(active ? (kpi + 1) * nslabs / KP - s_begin : 0);
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - rb * 16)));
-    const uint8_t *wbase = nrows > 0 ? P.packed + (int64_t)rb * 16 * rowbytes : P.packed;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)(nrows * rowbytes));
-    const int woff = col * rowbytes + g * 16;
-    // codes at or past K within a row read as whatever follows; their x pieces are zero
+    // Row-major codes: lane (g, col) reads bytes 16g .. 16g+15 of slab s of
+    // row col, 64 bytes a slab.  Tiled codes: slab s of the block is 1 KB,
+    // [4 quarters g][16 rows][16 bytes], so the lane reads bytes 16 * lane of
+    // it: one contiguous kilobyte per wave instruction.
+    const bool tiled = P.tiled != 0;
+    const uint8_t *wbase = nrows == 0 ? P.packed
+                           : tiled    ? P.packed + (int64_t)rb * nslabs * kTileBytes
+                                      : P.packed + (int64_t)rb * 16 * rowbytes;
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(wbase, nrows == 0 ? 0u : tiled ? (uint32_t)nslabs * kTileBytes
+                                                 : (uint32_t)(nrows * rowbytes));
+    const int woff = tiled ? lane * 16 : col * rowbytes + g * 16;
+    const int sstride = tiled ? kTileBytes : 64;
+    // row-major codes at or past K within a row read as whatever follows
+    // (tiled ones as the zero padding); their x pieces are zero
+    constexpr int kSP = G::SP;
     u32x4_t w[kSP];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kSP; ++j) {
-        w[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, j < S ? woff + (s_begin + j) * 64 : kOOB,
-                                                     0, 0);
+        w[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, j < S ? woff + (s_begin + j) * sstride : kOOB, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     // channel scale of row 4g + (lane & 3): each quad of lanes holds the four
@@ -367,7 +391,7 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
 #pragma unroll
             for (int j = 0; j < kSP; ++j) {
                 w[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    wr, c0 + j < S ? woff + (s_begin + c0 + j) * 64 : kOOB, 0, 0);
+                    wr, c0 + j < S ? woff + (s_begin + c0 + j) * sstride : kOOB, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -650,6 +674,7 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
             p.M = a.M;
             p.N = a.N;
             p.K = a.K;
+            p.tiled = a.tiled;
             const int nslabs = (a.K + 255) / 256;
             const int target = std::max(1, (a.K > 8192 ? 20 : 8) >> shrink);
             p.kp = parts_for(nslabs, target);

@@ -75,6 +75,7 @@ struct StreamProblem {
     uint16_t *y;
     int M, N, K;  // M <= the kernel's token count MT
     int group;    // 0 (per channel) or the group size
+    int tiled;    // codes in the tiled layout (else row-major [N, K/4])
     int rb;       // 16-channel blocks per workgroup
     int kp;       // K parts (waves) per block, rb * kp <= kWaves
     int unit0;    // first workgroup of this problem
@@ -170,6 +171,7 @@ struct WaveCtx {
     int gsh;       // GC = 2 with groups: column group (128 K) -> scale index shift
     int s_begin;   // first slab of the part
     int woff;      // this lane's byte offset of slab 0 in the block resource
+    int sstride;   // bytes from one slab to the next in the block resource
     int lane, g, tok, par;
     bool b_lane;
     uint16_t *xbuf;  // this wave's x area
@@ -326,7 +328,8 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
     u32x4_t w[S];
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-        w[i] = __builtin_amdgcn_raw_buffer_load_b128(c.wr, c.woff + (c.s_begin + i) * 64, 0, 0);
+        w[i] = __builtin_amdgcn_raw_buffer_load_b128(c.wr, c.woff + (c.s_begin + i) * c.sstride,
+                                                     0, 0);
         __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
     }
     chs = channel_scale_load<GROUPED>(c);
@@ -371,7 +374,7 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
         const bool in = i < S;
         xv[slot] = x_piece_load<MT>(c, in ? c.s_begin + i : (1 << 20));
         w[slot] = __builtin_amdgcn_raw_buffer_load_b128(
-            c.wr, in ? c.woff + (c.s_begin + i) * 64 : kOOB, 0, 0);
+            c.wr, in ? c.woff + (c.s_begin + i) * c.sstride : kOOB, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
@@ -506,9 +509,18 @@ __global__ void __launch_bounds__(kThreads)
     // (readfirstlane: the clamp lowers to a vector op, and a descriptor in
     // vector registers would put every load in a waterfall loop)
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - rb * 16)));
-    const uint8_t *wbase = nrows > 0 ? P.packed + (int64_t)rb * 16 * rowbytes : P.packed;
-    c.wr = make_rsrc(wbase, (uint32_t)(nrows * rowbytes));
-    c.woff = col * rowbytes + c.g * 16;
+    // Row-major codes: lane (g, col) reads bytes 16g .. 16g+15 of slab s of row
+    // col (64 bytes a slab).  Tiled codes: a slab of the block is 1 KB in the
+    // lane order [g][col][16 bytes], so the lane reads 16 contiguous bytes at
+    // 16 * (16g + col) and the wave one kilobyte.
+    const bool tiled = P.tiled != 0;
+    const uint8_t *wbase = nrows == 0 ? P.packed
+                           : tiled    ? P.packed + (int64_t)rb * nslabs * kTileBytes
+                                      : P.packed + (int64_t)rb * 16 * rowbytes;
+    c.wr = make_rsrc(wbase, nrows == 0 ? 0u : tiled ? (uint32_t)nslabs * kTileBytes
+                                                    : (uint32_t)(nrows * rowbytes));
+    c.woff = tiled ? (c.g * 16 + col) * 16 : col * rowbytes + c.g * 16;
+    c.sstride = tiled ? kTileBytes : 64;
     c.xr = make_rsrc(P.x, (uint32_t)M * (uint32_t)K * 2u);
     // the scale resource starts at the block's first row (64-bit pointer
     // arithmetic), so its 32-bit offsets stay below 16 rows of scales
@@ -692,6 +704,7 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
             p.N = a.N;
             p.K = a.K;
             p.group = group;
+            p.tiled = a.tiled;
             split_k(a.K, one_shot_of(kernel_mt(a.M), group), target, p.kp, p.rb);
             const int nblocks = (a.N + 15) / 16;
             p.rb = std::min(p.rb, nblocks);

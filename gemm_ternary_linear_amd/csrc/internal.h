@@ -32,7 +32,22 @@ struct GemvArgs {
     uint16_t *y;
     int M, N, K;
     int group;  // 0 (per channel) or the group size
+    int tiled;  // codes in the tiled layout (else row-major [N, K/4])
 };
+
+// The tiled layout of an [N, K] code matrix (include/ternary.h): blocks of 16
+// rows x 256 codes, 1 KB each, blocks of one row band consecutive.
+constexpr int kTileRows = 16, kTileK = 256, kTileBytes = 1024;
+inline int64_t tiled_slabs(int64_t K) { return (K + kTileK - 1) / kTileK; }
+inline int64_t tiled_bytes(int64_t N, int64_t K)
+{
+    return (N + kTileRows - 1) / kTileRows * tiled_slabs(K) * kTileBytes;
+}
+// Row-major <-> tiled, one thread per 16 tiled bytes (pack.hip).
+hipError_t launch_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled,
+                       hipStream_t stream);
+hipError_t launch_untile(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *packed,
+                         hipStream_t stream);
 
 hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,
                        hipStream_t stream);
@@ -45,11 +60,13 @@ hipError_t launch_quantize(const uint16_t *w, bool fp16, int N, int K, int group
 // `group` as in GemvArgs, shapes already validated by the caller.
 // Which decode kernel runs a GEMV problem: AUTO prefers the fp4 x fp8 one
 // wherever it takes the shape; F4 and B16 force one (parity tests, tuning).
+// Both read row-major and tiled codes.
 enum class GemvKernel { AUTO, F4, B16 };
-bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16);
+bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16,
+                       bool tiled = false);
 hipError_t launch_gemv(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
-                       GemvKernel kernel = GemvKernel::AUTO);
+                       GemvKernel kernel = GemvKernel::AUTO, bool tiled = false);
 // Up to kGemvMaxBatch decode problems (all taken by `kernel`), one launch per
 // (kernel, scale mode, M) class.
 hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
@@ -76,10 +93,13 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
                           int group, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
+// Tiled codes need the pipelined kernel (gemm_big_takes with tiled).
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
-// Whether the pipelined (grouped) prefill kernel takes a problem.
-bool gemm_big_takes(int M, int N, int K, int group, const void *scale);
+                       const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
+                       bool tiled = false);
+// Whether the pipelined (grouped) prefill kernel takes a problem (it reads
+// row-major and tiled codes; the 128 x 128 kernel only row-major ones).
+bool gemm_big_takes(int M, int N, int K, int group, const void *scale, bool tiled = false);
 // A caller-provided scratch buffer for split-K partial tiles (device memory
 // of `bytes` bytes), used instead of the per-stream workspace.
 struct FixedScratch {
@@ -115,7 +135,8 @@ hipError_t noalloc_scratch(void **out);
 size_t noalloc_scratch_bytes();
 
 hipError_t launch_simple(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
-                         const uint16_t *scale, int group, uint16_t *y, hipStream_t stream);
+                         const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
+                         bool tiled = false);
 
 // Shape requirements of the fast kernels.  The decode kernels take K up to
 // 65536 (a multiple of 128).

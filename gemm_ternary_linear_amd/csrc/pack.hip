@@ -1,4 +1,5 @@
-// Pack / unpack of 2-bit ternary codes on gfx950.
+// Pack / unpack of 2-bit ternary codes on gfx950, and the conversion between
+// the row-major packing and the library's tiled layout.
 //
 // Format from [trdm] trdm.cn "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战"
 // §3.1 and [nxbn] m.nxbn.cn/news/169761 §2.2: value +1 -> code 01, -1 -> 10,
@@ -109,6 +110,90 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint8_t *__restrict__
                 q[4 * b + i] = (int8_t)(v >> (8 * i));
         }
     }
+}
+
+// Tiled layout (the library's): 16-row x 256-code blocks of 1 KB, stored
+// [4 quarters][16 rows][16 bytes] (quarter g = bytes 16g .. 16g+15 of the
+// block's 64 bytes of each row), blocks of a row band consecutive.  Thread t
+// owns tiled bytes 16t .. 16t+15: quarter g of row r of block (band, slab),
+// i.e. row-major bytes j0 .. j0+15 of row n with
+//   t = ((band * ks + slab) * 4 + g) * 16 + r,  n = 16 band + r,  j0 = 64 slab + 16 g.
+// Bytes past N rows or K/4 columns are the zero padding.
+struct TileUnit {
+    int64_t n, j0;  // row and first row-major byte of the unit
+};
+__device__ __forceinline__ TileUnit tile_unit(int64_t t, int64_t ks)
+{
+    const int64_t r = t & 15, g = (t >> 4) & 3, blk = t >> 6;
+    return {(blk / ks) * 16 + r, (blk % ks) * 64 + 16 * g};
+}
+
+__global__ void __launch_bounds__(256) tile_kernel(const uint8_t *__restrict__ packed, int64_t N,
+                                                   int64_t K, uint8_t *__restrict__ tiled,
+                                                   int64_t units)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= units)
+        return;
+    const int64_t rb = K >> 2, ks = (K + 255) >> 8;
+    const TileUnit u = tile_unit(t, ks);
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (u.n < N) {
+        const uint8_t *src = packed + u.n * rb + u.j0;
+        if ((rb & 15) == 0 && u.j0 + 16 <= rb) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            w[0] = v.x;
+            w[1] = v.y;
+            w[2] = v.z;
+            w[3] = v.w;
+        } else {
+            for (int b = 0; b < 16; ++b)
+                if (u.j0 + b < rb)
+                    w[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+        }
+    }
+    *reinterpret_cast<uint4 *>(tiled + 16 * t) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(256) untile_kernel(const uint8_t *__restrict__ tiled, int64_t N,
+                                                     int64_t K, uint8_t *__restrict__ packed,
+                                                     int64_t units)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= units)
+        return;
+    const int64_t rb = K >> 2, ks = (K + 255) >> 8;
+    const TileUnit u = tile_unit(t, ks);
+    if (u.n >= N || u.j0 >= rb)
+        return;
+    const uint4 v = *reinterpret_cast<const uint4 *>(tiled + 16 * t);
+    uint8_t *dst = packed + u.n * rb + u.j0;
+    if ((rb & 15) == 0 && u.j0 + 16 <= rb) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int b = 0; b < 16; ++b)
+            if (u.j0 + b < rb)
+                dst[b] = (uint8_t)(w[b >> 2] >> (8 * (b & 3)));
+    }
+}
+
+hipError_t launch_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled,
+                       hipStream_t stream)
+{
+    const int64_t units = tiled_bytes(N, K) / 16;
+    hipLaunchKernelGGL(tile_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
+                       packed, N, K, tiled, units);
+    return hipGetLastError();
+}
+
+hipError_t launch_untile(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *packed,
+                         hipStream_t stream)
+{
+    const int64_t units = tiled_bytes(N, K) / 16;
+    hipLaunchKernelGGL(untile_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
+                       tiled, N, K, packed, units);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack(const int8_t *q, int64_t nbytes, uint8_t *packed, int32_t *invalid_count,

@@ -29,6 +29,17 @@
  *     (g consecutive K weights of a row share one: g = 128 in [trdm §3.1], 64
  *     in [xxqk §4.2], 32 and 256 in [ch13 §13.3.3]).
  *
+ * Tiled layout (this library's, not the pages'; TERNARY_LAYOUT_TILED): the same
+ * bytes as the row-major packing, permuted so that the matrix-core kernels read
+ * one contiguous kilobyte per wave instruction.  Rows are padded to a multiple
+ * of 16 and K to a multiple of 256 with code 00; with Ks = ceil(K / 256), byte
+ * j of row n of the row-major packing (j < K/4) sits at
+ *     ((n / 16) * Ks + j / 64) * 1024 + ((j % 64) / 16) * 256 + (n % 16) * 16 + j % 16
+ * i.e. block (n/16, j/64) of 16 rows x 64 bytes is 1 KB, stored as four
+ * [16 rows][16 bytes] quarters in K order.  ternary_tiled_bytes() gives the
+ * size, ternary_tile()/ternary_untile() convert; every linear entry point that
+ * takes a layout reads either.
+ *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers, owned by the caller.  The library
  *     keeps no reference after a call returns and never allocates or frees
@@ -76,6 +87,9 @@ typedef enum {
                                    split-K scratch than TERNARY_NOALLOC_SCRATCH_BYTES */
 } ternary_status;
 
+/* Weight layout of a linear call (see "Tiled layout" above). */
+typedef enum { TERNARY_LAYOUT_ROWS = 0, TERNARY_LAYOUT_TILED = 1 } ternary_layout;
+
 /* Activation / output element type (2 bytes per element). */
 typedef enum { TERNARY_BF16 = 0, TERNARY_FP16 = 1 } ternary_dtype;
 
@@ -114,6 +128,28 @@ int ternary_pack(const int8_t *q, int64_t N, int64_t K, uint8_t *packed,
  *   q       int8 [N, K] output, 16-byte aligned, must not overlap packed.
  */
 int ternary_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q, hipStream_t stream);
+
+/*
+ * ternary_tiled_bytes - size in bytes of the tiled layout of an [N, K] code
+ * matrix: ceil(N/16) * 16 * ceil(K/256) * 64.  Returns TERNARY_ERR_SHAPE for
+ * N < 0, K < 0, K % 4 != 0, N or K above 2^24, or more than 2^40 bytes (the
+ * limits of ternary_tile / ternary_untile as well).
+ */
+int64_t ternary_tiled_bytes(int64_t N, int64_t K);
+
+/*
+ * ternary_tile - row-major packed codes -> tiled layout (a byte permutation;
+ * padding bytes are written as 0).
+ *   packed  uint8 [N, K/4], 16-byte aligned.
+ *   tiled   uint8 [ternary_tiled_bytes(N, K)] output, 16-byte aligned, must not
+ *           overlap packed.
+ * N == 0 or K == 0 is a successful no-op.  ternary_untile is the inverse
+ * (same arguments, tiled -> packed; padding bytes are not read).
+ */
+int ternary_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled,
+                 hipStream_t stream);
+int ternary_untile(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *packed,
+                   hipStream_t stream);
 
 /*
  * ternary_quantize - codes and scales of 16-bit weights (the step before the
@@ -172,6 +208,23 @@ int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
                       const uint8_t *packed, const uint16_t *scale, int64_t group_size,
                       void *y, int path, hipStream_t stream);
 
+/*
+ * ternary_linear_tiled - ternary_linear_ex with the codes in the tiled layout:
+ *   tiled  uint8 [ternary_tiled_bytes(N, K)], 16-byte aligned; every other
+ *          argument as for ternary_linear_ex.
+ * The same products, sums and rounding as the row-major call.  Paths: both
+ * decode GEMVs, the pipelined GEMM and the plain kernel read the tiled
+ * layout; the GEMM shapes only the 128 x 128 kernel takes (K % 256 != 0, group
+ * size 32, an odd number of groups per row, scales not 4-byte aligned) run the
+ * plain kernel under TERNARY_PATH_AUTO and return TERNARY_ERR_PATH when
+ * TERNARY_PATH_GEMM is forced.  A forced path runs the same kernel, with the
+ * same launch shape, on tiled as on row-major codes: the results are the
+ * same bits.
+ */
+int ternary_linear_tiled(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
+                         const uint8_t *tiled, const uint16_t *scale, int64_t group_size,
+                         void *y, int path, hipStream_t stream);
+
 /* Most problems one ternary_linear_batch call takes. */
 #define TERNARY_MAX_BATCH 8
 
@@ -183,6 +236,9 @@ typedef struct {
     void *y;                /* [M, N] output, 16-byte aligned                       */
     int64_t M, N, K;        /* as for ternary_linear                                */
     int64_t group_size;     /* -1, 32, 64, 128 or 256                               */
+    int64_t layout;         /* TERNARY_LAYOUT_ROWS ([N, K/4] as above) or
+                               TERNARY_LAYOUT_TILED (packed holds
+                               ternary_tiled_bytes(N, K) bytes)                    */
 } ternary_problem;
 
 /*
@@ -193,7 +249,8 @@ typedef struct {
  *   problems  host array of `count` problems (1 <= count <= TERNARY_MAX_BATCH),
  *             read during the call only.
  *   dtype     activation/output dtype shared by all problems.
- * Every problem is validated as by ternary_linear; in addition no output may
+ * Every problem is validated as by ternary_linear (or ternary_linear_tiled);
+ * an unknown layout returns TERNARY_ERR_SHAPE; in addition no output may
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
  * any error nothing is launched.  Problems the automatic path sends to the
  * decode GEMV (see ternary_linear) run together in one launch per scale

@@ -63,7 +63,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 4
+    assert tl.abi_version() == 5
     assert tl.gemv_max_m() == 8
     for st in range(0, -11, -1):
         s = tl.status_string(st)
@@ -253,3 +253,73 @@ def test_binding_unpack_rejects_wrong_K(tl):
     for K in (60, 68, 128, 4):
         with pytest.raises(ValueError, match="does not match the packed rows"):
             tl.unpack(p, K)
+
+
+def _lint(tl, x=FAKE, dtype=0, M=1, N=16, K=256, p=FAKE * 2, s=FAKE * 3, g=-1, y=FAKE * 4, path=0):
+    return tl.lib().ternary_linear_tiled(x, dtype, M, N, K, p, s, g, y, path, None)
+
+
+def test_tiled_bytes(tl):
+    L = tl.lib()
+    assert L.ternary_tiled_bytes(17, 260) == 4096
+    assert L.ternary_tiled_bytes(16, 256) == 1024
+    assert L.ternary_tiled_bytes(1, 4) == 1024
+    assert L.ternary_tiled_bytes(0, 256) == 0
+    assert L.ternary_tiled_bytes(18944, 4096) == 18944 * 1024
+    assert L.ternary_tiled_bytes(3, 6) == -2
+    assert L.ternary_tiled_bytes(-1, 4) == -2
+    assert L.ternary_tiled_bytes(1 << 25, 4) == -2
+    assert L.ternary_tiled_bytes(1 << 24, 1 << 24) == -2     # above 2^40 bytes
+
+
+def test_tile_untile_reject(tl):
+    L = tl.lib()
+    for fn in (L.ternary_tile, L.ternary_untile):
+        assert fn(FAKE, 4, 6, FAKE * 4, None) == -2
+        assert fn(FAKE, -1, 8, FAKE * 4, None) == -2
+        assert fn(0, 4, 8, FAKE * 4, None) == -1
+        assert fn(FAKE, 4, 8, 0, None) == -1
+        assert fn(FAKE + 4, 4, 8, FAKE * 4, None) == -5
+        assert fn(FAKE, 4, 8, FAKE * 4 + 8, None) == -5
+        assert fn(FAKE, 0, 8, 0, None) == 0
+    # the tiled buffer (1 KB here) overlaps the row-major one (8 bytes)
+    assert L.ternary_tile(FAKE, 4, 8, FAKE - 512, None) == -6        # (packed, ..., tiled)
+    assert L.ternary_tile(FAKE + 1008, 4, 8, FAKE, None) == -6
+    assert L.ternary_untile(FAKE - 512, 4, 8, FAKE, None) == -6      # (tiled, ..., packed)
+    assert L.ternary_untile(FAKE, 4, 8, FAKE + 1008, None) == -6
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), -4),
+    (dict(g=16), -3),
+    (dict(K=130), -2),
+    (dict(x=0), -1),
+    (dict(p=0), -1),
+    (dict(p=FAKE * 2 + 4), -5),
+    # y overlaps the tiled codes beyond the row-major size (16 x 256 -> 1 KB
+    # either way; 17 rows -> 2 KB tiled against 1088 bytes row-major)
+    (dict(N=17, y=FAKE * 2 + 1536), -6),
+    (dict(M=64, K=384, path=2), -8),           # tiled GEMM needs K % 256 == 0
+    (dict(M=64, K=512, g=32, path=2), -8),     # and group sizes 64, 128, 256
+    (dict(M=9, path=4), -8),
+    (dict(path=6), -8),
+])
+def test_linear_tiled_rejects(tl, kw, status):
+    assert _lint(tl, **kw) == status
+
+
+def test_linear_tiled_empty_is_noop(tl):
+    assert _lint(tl, M=0) == 0
+    assert _lint(tl, N=0, p=0, s=0) == 0
+
+
+def test_batch_rejects_unknown_layout(tl):
+    L = tl.lib()
+    P = tl.Problem
+    ok = P(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 16, 128, 128, 0)
+    bad = P(FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, 1, 16, 128, 128, 2)
+    assert L.ternary_linear_batch((P * 2)(ok, bad), 2, 0, None) == -2
+    # a tiled member's codes count with their tiled size in the overlap checks
+    t = P(FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, 1, 17, 256, -1, 1)
+    clash = P(FAKE, FAKE * 2, FAKE * 3, FAKE * 6 + 1536, 1, 16, 128, 128, 0)
+    assert L.ternary_linear_batch((P * 2)(t, clash), 2, 0, None) == -6
