@@ -6,9 +6,13 @@
 One step is one decode pass of a 7B-shaped layer: the seven ternary
 projections q, k, v, o (4096/512 x 4096), gate, up (18944 x 4096) and down
 (4096 x 18944) at M = 1 token, per-channel fp16 scales, bf16 activations,
-in one ternary_linear_batch call (one fused decode-GEMV launch).  Weights rotate over
-enough copies (>= 1 GiB) that no step finds them in the 256 MB Infinity
-Cache; inputs are resident in HBM before timing starts.
+in one ternary_linear_batch call (one fused decode-GEMV launch).  The codes are
+stored in the library's tiled layout (ternary_tile: blocks of 16 rows x 256
+codes, one contiguous kilobyte each), the layout a deployment converts its
+weights to once at load; the same figures with row-major codes (the pages'
+[N, K/4] packing) are reported beside (rows_codes, prefill.rows_value).
+Weights rotate over enough copies (>= 1 GiB) that no step finds them in the
+256 MB Infinity Cache; inputs are resident in HBM before timing starts.
 
 Printed (one JSON line on stdout):
   value        decode throughput: algorithmic bytes of all timed launches /
@@ -34,7 +38,7 @@ Algorithmic bytes per launch: N*K/4 (codes) + scales (2N, or N*K/64 grouped)
 
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
 digests two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE)
-into profiles/gemv_stream_7b_decode_m1_counters.txt (the fused decode launch)
+into profiles/gemv_f4_7b_decode_m1_counters.txt (the fused decode launch)
 and profiles/gemm_dma_7b_prefill_m2048_counters.txt (the grouped prefill
 launch).
 """
@@ -60,11 +64,12 @@ ROTATE_BYTES = 1 << 30          # weight bytes cycled per rotation (> 256 MB MAL
 COPY_PROBE_BYTES = 512 << 20    # known-size copy kernel used to calibrate counters
 COUNTERS = {
     # kernel family -> (file, kernel-name substring, what the launch is)
-    "decode": (ROOT / "profiles" / "gemv_stream_7b_decode_m1_counters.txt", "gemv",
-               "the fused decode GEMV launch (all 7 projections of the 7B layer at M=1)"),
+    "decode": (ROOT / "profiles" / "gemv_f4_7b_decode_m1_counters.txt", "gemv_f4_kernel",
+               "the fused decode GEMV launch (all 7 projections of the 7B layer at M=1, "
+               "tiled codes)"),
     "prefill": (ROOT / "profiles" / "gemm_dma_7b_prefill_m2048_counters.txt", "gemm_dma_kernel",
                 "the grouped prefill GEMM launch (all 7 projections of the 7B layer at "
-                "M=2048)"),
+                "M=2048, tiled codes)"),
 }
 DECODE_CFG, PREFILL_CFG = 2, 3
 PROBE_ITERS = {512: 8192, 1024: 4096, 2048: 2048}   # MFMA loop probe: workgroups -> iters
@@ -98,13 +103,15 @@ def to_dev(a, dtype=None):
 
 
 class Layer:
-    """Seven projections of one config, packed on the GPU, with rotated copies."""
+    """The projections of one config, packed on the GPU (row-major codes, or
+    the library's tiled layout), with rotated copies."""
 
-    def __init__(self, tl, cfg_index, M, copies=None):
+    def __init__(self, tl, cfg_index, M, copies=None, layout="rows"):
         import torch
         import synth
         self.cfg = synth.CONFIGS[cfg_index]
         self.M = M
+        self.layout = layout
         self.g = self.cfg.group_size
         self.shapes = list(self.cfg.shapes)
         self.cases = []
@@ -114,6 +121,8 @@ class Layer:
             q = to_dev(case.codes)
             p = tl.pack(q)
             del q
+            if layout == "tiled":
+                p = tl.tile(p)
             self.cases.append(case)
             self.packed.append([p])
             self.scale.append([to_dev(case.scale, torch.float16)])
@@ -130,13 +139,13 @@ class Layer:
 
     def launch(self, tl, j, r):
         tl.linear(self.x[j], self.packed[j][r % self.copies], self.scale[j][r % self.copies],
-                  self.g, out=self.y[j])
+                  self.g, out=self.y[j], layout=self.layout)
 
     def step(self, tl, r):
         """All projections of the layer in one ternary_linear_batch call."""
         c = r % self.copies
-        tl.linear_batch([(self.x[j], self.packed[j][c], self.scale[j][c], self.g, self.y[j])
-                         for j in range(len(self.shapes))])
+        tl.linear_batch([(self.x[j], self.packed[j][c], self.scale[j][c], self.g, self.y[j],
+                          self.layout) for j in range(len(self.shapes))])
 
     def step_separate(self, tl, r):
         """The same projections as one ternary_linear call each."""
@@ -188,6 +197,20 @@ def time_region(tl, layer, steps, warmup, separate=False):
     return t0.elapsed_time(t1) * 1e-3
 
 
+_CAPTURE_STREAM = None
+
+
+def capture_stream():
+    """One side stream for every graph capture here: the library keeps a
+    split-K workspace per stream and allocates nothing under capture, so each
+    capture is preceded by eager calls on this same stream."""
+    global _CAPTURE_STREAM
+    import torch
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    return _CAPTURE_STREAM
+
+
 def time_graph_region(tl, layer, steps, warmup, separate=False):
     """Wall time of exactly `steps` steps replayed from one captured HIP graph.
 
@@ -197,11 +220,13 @@ def time_graph_region(tl, layer, steps, warmup, separate=False):
     """
     import torch
     step = layer.step_separate if separate else layer.step
-    for w in range(warmup):
-        step(tl, w)
+    side = capture_stream()
+    with torch.cuda.stream(side):  # warm-up on the capture stream (split-K workspaces)
+        for w in range(warmup):
+            step(tl, w)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=side):
         for i in range(steps):
             step(tl, warmup + i)
     settle(g.replay)
@@ -221,9 +246,13 @@ def time_per_shape(tl, layer, launches=64, reps=3):
     replayed `reps` times between events on the launch stream, after settle()."""
     import torch
     out = []
+    side = capture_stream()
     for j in range(len(layer.shapes)):
+        with torch.cuda.stream(side):  # a split-K shape's workspace exists before capture
+            layer.launch(tl, j, 0)
+        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=side):
             for i in range(launches):
                 layer.launch(tl, j, i)
         settle(g.replay)
@@ -305,7 +334,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
             f"# HBM traffic of {what}",
             "# from two rocprofv3 --pmc runs of bench.py:",
             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- \\",
-            "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2 --settle-ms 0",
+            "#       python3 bench.py --no-cpu --no-sweep --no-rows --steps 10 --warmup 2 --prefill-steps 1 --prefill-warmup 2 --settle-ms 0",
             "#   (the same with --pmc WRITE_SIZE into <W>), then",
             "#   python3 bench.py --summarize-pmc <F> <W>",
             "# Counters read KiB per dispatch (summed over instances); each is scaled by what",
@@ -372,7 +401,7 @@ def summarize_mfma(*dirs) -> None:
     ]
     for cs in MFMA_PASSES:
         lines.append(f"#   rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <D> -o bench -- \\")
-        lines.append("#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
+        lines.append("#       python3 bench.py --no-cpu --no-sweep --no-rows --steps 10 --warmup 2 "
                      "--prefill-steps 1 --prefill-warmup 2 --settle-ms 0")
     lines += [
         "#   python3 bench.py --summarize-mfma <D1> <D2>",
@@ -413,23 +442,23 @@ def summarize_mfma(*dirs) -> None:
     print("\n".join(lines))
 
 
-VALU_FILE = ROOT / "profiles" / "gemv_stream_7b_decode_m1_valu.txt"
+VALU_FILE = ROOT / "profiles" / "gemv_f4_7b_decode_m1_valu.txt"
 VALU_PASS = ("VALUBusy", "MfmaUtil", "SQ_INSTS_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
              "SQ_ACTIVE_INST_ANY", "SQ_BUSY_CYCLES")
 
 
 def summarize_valu(d: str) -> None:
     """Digest one --pmc run of bench.py for the fused decode launch (the
-    largest-grid gemv_stream_kernel dispatch): how busy its vector ALUs and
+    largest-grid gemv_f4_kernel dispatch): how busy its vector ALUs and
     matrix cores are, and how much of a wave's life goes to waiting."""
     vals = {}
     for r in read_counter_csv(Path(d)):
         key = (r["Kernel_Name"], int(r.get("Grid_Size", 0)), r["Dispatch_Id"])
         vals.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
         vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
-    keys = [k for k in vals if "gemv_stream_kernel" in k[0]]
+    keys = [k for k in vals if "gemv_f4_kernel" in k[0]]
     if not keys:
-        raise SystemExit(f"no gemv_stream_kernel dispatch under {d}")
+        raise SystemExit(f"no gemv_f4_kernel dispatch under {d}")
     top = max(k[1] for k in keys)
     keys = [k for k in keys if k[1] == top]
     mean = {}
@@ -438,9 +467,9 @@ def summarize_valu(d: str) -> None:
         mean[c] = (sum(v) / len(v), len(v))
     lines = [
         "# Vector-ALU and matrix-core activity of the fused decode GEMV launch (all 7",
-        "# projections of the 7B layer at M=1, the largest gemv_stream_kernel dispatch), from",
+        "# projections of the 7B layer at M=1, tiled codes, the largest gemv_f4_kernel dispatch), from",
         "#   rocprofv3 --pmc " + " ".join(VALU_PASS) + " --output-format csv -d <D> -o bench -- \\",
-        "#       python3 bench.py --no-cpu --no-sweep --steps 10 --warmup 2 "
+        "#       python3 bench.py --no-cpu --no-sweep --no-rows --steps 10 --warmup 2 "
         "--prefill-steps 1 --prefill-warmup 2 --settle-ms 0",
         "#   python3 bench.py --summarize-valu <D>",
         "# VALUBusy and MfmaUtil are rocprofv3's derived percentages of the launch's GPU time;",
@@ -479,11 +508,11 @@ def summarize_trace(d: str) -> None:
     if not stats or not trace:
         raise SystemExit(f"no kernel_stats/kernel_trace csv under {d}")
     lines = [
-        "# rocprofv3 kernel trace of `python3 bench.py --no-cpu --no-sweep` (7B decode layer",
+        "# rocprofv3 kernel trace of `python3 bench.py --no-cpu --no-sweep --no-rows` (7B decode layer",
         "# at M=1 as one fused ternary_linear_batch launch per step, per-projection launches,",
         "# the 7B prefill layer at M=2048, and the probe kernels), made by:",
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d <D> -o bench -- \\",
-        "#       python3 bench.py --no-cpu --no-sweep",
+        "#       python3 bench.py --no-cpu --no-sweep --no-rows",
         "#   python3 bench.py --summarize-trace <D>",
         f"source_hash {kernel_source_hash()}",
         "",
@@ -631,7 +660,7 @@ def bench_pack(tl):
 
 def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
     """Every (config, shape, M) of the five workloads that the headline lines do
-    not already time: per-launch time on the automatic path, as GB/s and
+    not already time (codes in the tiled layout): per-launch time on the automatic path, as GB/s and
     TFLOP/s with both roofline fractions; for every case the GEMV takes, and
     for config 4 at each M, also the forced GEMV and GEMM paths, to place the
     GEMV -> GEMM crossover.
@@ -680,7 +709,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
                 continue
             case = synth.make_case(ci, si, cfg.Ms[0])
             q = to_dev(case.codes)
-            p1 = tl.pack(q)
+            p1 = tl.tile(tl.pack(q))
             del q
             s1 = to_dev(case.scale, torch.float16)
             wbytes = p1.numel() + 2 * s1.numel()
@@ -697,7 +726,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
 
                 def run(path):
                     return graph_us(lambda r: tl.linear(x, P[r], S[r], cfg.group_size,
-                                                        path=path, out=y), R)
+                                                        path=path, out=y, layout="tiled"), R)
 
                 t = run("auto")
                 res[str(M)] = {"path": tl.select_path(M, shp.N, shp.K, cfg.group_size),
@@ -829,6 +858,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4)")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the row-major-codes figures reported beside the tiled ones "
+                         "(profiled runs: only tiled launches then)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "LDS_DIR"))
@@ -862,8 +894,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     tl.lib()
 
-    log("[bench] building the decode layer (config 2, M=1)")
-    dec = Layer(tl, DECODE_CFG, 1)
+    log("[bench] building the decode layer (config 2, M=1, tiled codes)")
+    dec = Layer(tl, DECODE_CFG, 1, layout="tiled")
     paths = {s.name: tl.select_path(1, s.N, s.K, dec.g) for s in dec.shapes}
     log(f"[bench] decode paths {paths}, {dec.copies} rotated copies")
     copy_probe()
@@ -894,17 +926,32 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if traffic is None else round(traffic, 1),
-                "kernel": "gemv_stream_kernel<bf16, per-channel, M=1>: one fused launch of the "
-                          "7 projections",
+                "kernel": "gemv_f4_kernel<bf16, per-channel, M=1>: one fused launch of the "
+                          "7 projections, tiled codes",
                 "alg_bytes_per_launch": step_bytes,
                 "mean_launch_us": round(mean_dur * 1e6, 3)}
     log(f"[bench] decode per-launch {shapes_out}")
     rotated = dec.copies
     del dec
     torch.cuda.empty_cache()
+    rows_dec = None
+    if not args.no_rows:
+        # the same layer with row-major codes (the pages' [N, K/4] packing)
+        dr = Layer(tl, DECODE_CFG, 1, layout="rows")
+        t_rows = time_graph_region(tl, dr, args.steps, args.warmup)
+        dur_r = time_per_shape(tl, dr)
+        rows_dec = {"value": round(step_bytes * args.steps / t_rows / 1e9, 1),
+                    "frac_of_hbm_peak": round(step_bytes * args.steps / t_rows / 1e9
+                                              / HBM_PEAK_GBPS, 4),
+                    "mean_launch_us": round(t_rows / args.steps * 1e6, 3),
+                    "shapes_us": {s.name: round(dur_r[j] * 1e6, 3)
+                                  for j, s in enumerate(dr.shapes)}}
+        log(f"[bench] decode with row-major codes {rows_dec}")
+        del dr
+        torch.cuda.empty_cache()
 
-    log("[bench] building the prefill layer (config 3, M=2048)")
-    pre = Layer(tl, PREFILL_CFG, 2048, copies=2)
+    log("[bench] building the prefill layer (config 3, M=2048, tiled codes)")
+    pre = Layer(tl, PREFILL_CFG, 2048, copies=2, layout="tiled")
     pre_flops = sum(pre.flops_per_launch(j) for j in range(len(pre.shapes)))
     # One step = one ternary_linear_batch call = one grouped GEMM launch (the
     # layer has enough tiles that no K range is split): events on the launch
@@ -940,7 +987,7 @@ def main():
                      "traffic": None if traffic_p is None else round(traffic_p, 1),
                      "mfma_busy_vs_probe": stored_mfma(),
                      "kernel": "gemm_dma_kernel<bf16, per-channel>: one grouped launch of the "
-                               "7 projections",
+                               "7 projections, tiled codes",
                      "alg_flops_per_launch": pre_flops,
                      "alg_bytes_per_launch": sum(pre.bytes_per_launch(j)
                                                  for j in range(len(pre.shapes))),
@@ -949,6 +996,13 @@ def main():
     }
     log(f"[bench] prefill {pre_value:.1f} TFLOP/s (separate calls {pre_sep_value:.1f}) "
         f"{pre_shapes}")
+    if not args.no_rows:
+        pr = Layer(tl, PREFILL_CFG, 2048, copies=2, layout="rows")
+        t_pr = time_region(tl, pr, args.prefill_steps, args.prefill_warmup)
+        prefill["rows_value"] = round(pre_flops * args.prefill_steps / t_pr / 1e12, 1)
+        log(f"[bench] prefill with row-major codes {prefill['rows_value']} TFLOP/s")
+        del pr
+        torch.cuda.empty_cache()
     pack = bench_pack(tl)
     log(f"[bench] pack {pack}")
     ceilings = measure_ceilings(tl, step_bytes, min(args.steps, 200))
@@ -987,7 +1041,9 @@ def main():
         "config": {"workload": "7B-shaped decode layer: 7 ternary projections "
                                "(q,k,v,o 4096|512x4096; gate,up 18944x4096; down 4096x18944), "
                                "M=1, per-channel fp16 scales, bf16 x",
-                   "M": 1, "global_batch": 1, "rotated_copies": rotated, "parallelism": "none"},
+                   "M": 1, "global_batch": 1, "rotated_copies": rotated, "parallelism": "none",
+                   "layout": "tiled codes (ternary_tile: 16-row x 256-code blocks of 1 KB); "
+                             "row-major codes under rows_codes"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "timing": f"one HIP-graph replay of the K steps (one fused launch each), after "
                   f"{args.warmup} eager steps and {args.settle_ms:g} ms of untimed replays "
@@ -995,6 +1051,7 @@ def main():
                   "reported beside",
         "eager_value": round(eager_value, 1),
         "separate_launches_value": round(sep_value, 1),
+        "rows_codes": rows_dec,
         "roofline": roofline,
         "decode_shapes": shapes_out,
         "prefill": prefill,

@@ -36,7 +36,7 @@ def test_summarize_pmc_scales_by_copy_probe(tmp_path, monkeypatch):
     fam = {k: (tmp_path / f"{k}.txt", sub, what) for k, (_, sub, what) in bench.COUNTERS.items()}
     monkeypatch.setattr(bench, "COUNTERS", fam)
     neg = "at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda"
-    gemv = "ternary::gemv_stream_kernel<false, false, 1, false>(StreamBatch)"
+    gemv = "ternary::(anonymous namespace)::gemv_f4_kernel<false, 0, 1>(ternary::(anonymous namespace)::F4Batch)"
     gemm = "ternary::dma::gemm_dma_kernel<false, false, Cfg<256, 128, 4, 1, 4, 2> >(BigBatch)"
     # FETCH_SIZE reads half the bytes (scale 2), WRITE_SIZE all of them (scale 1)
     _write_counters(tmp_path / "F", "FETCH_SIZE", [
@@ -152,7 +152,7 @@ def test_summarize_mfma_relates_gemm_to_probe(tmp_path, monkeypatch):
 
 def test_summarize_valu_takes_the_fused_launch(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "VALU_FILE", tmp_path / "valu.txt")
-    gemv = "ternary::gemv_stream_kernel<false, false, 2, 1>(StreamBatch)"
+    gemv = "ternary::(anonymous namespace)::gemv_f4_kernel<false, 0, 1>(ternary::(anonymous namespace)::F4Batch)"
     d = tmp_path / "V"
     d.mkdir()
     with open(d / "bench_counter_collection.csv", "w", newline="") as f:
