@@ -112,6 +112,7 @@ class Layer:
         self.cfg = synth.CONFIGS[cfg_index]
         self.M = M
         self.layout = layout
+        self.path = "auto"
         self.g = self.cfg.group_size
         self.shapes = list(self.cfg.shapes)
         self.cases = []
@@ -139,7 +140,7 @@ class Layer:
 
     def launch(self, tl, j, r):
         tl.linear(self.x[j], self.packed[j][r % self.copies], self.scale[j][r % self.copies],
-                  self.g, out=self.y[j], layout=self.layout)
+                  self.g, out=self.y[j], layout=self.layout, path=self.path)
 
     def step(self, tl, r):
         """All projections of the layer in one ternary_linear_batch call."""
@@ -947,6 +948,15 @@ def main():
                     "shapes_us": {s.name: round(dur_r[j] * 1e6, 3)
                                   for j, s in enumerate(dr.shapes)}}
         log(f"[bench] decode with row-major codes {rows_dec}")
+        # the vector-ALU decode GEMV (add/sub per code, cross-lane reduction)
+        # on the same projections, one launch each
+        dr.path = "gemv_valu"
+        dur_v = time_per_shape(tl, dr)
+        rows_dec["valu_gemv_us"] = {s.name: round(dur_v[j] * 1e6, 3)
+                                    for j, s in enumerate(dr.shapes)}
+        rows_dec["valu_gemv_sum_us"] = round(sum(dur_v) * 1e6, 3)
+        rows_dec["f4_gemv_sum_us"] = round(sum(dur_r) * 1e6, 3)
+        log(f"[bench] VALU decode GEMV per launch {rows_dec['valu_gemv_us']}")
         del dr
         torch.cuda.empty_cache()
 

@@ -137,6 +137,10 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
             return TERNARY_ERR_PATH;
         break;
     case TERNARY_PATH_SIMPLE: break;
+    case TERNARY_PATH_GEMV_VALU:
+        if (!(M == 0 || N == 0 || ternary::gemv_valu_takes(M, K, group, tiled)))
+            return TERNARY_ERR_PATH;
+        break;
     default: return TERNARY_ERR_PATH;
     }
     if (M == 0 || N == 0)
@@ -153,6 +157,12 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
         e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
                                  tiled);
         break;
+    case TERNARY_PATH_GEMV_VALU: {
+        const ternary::GemvArgs a = {xv, packed, scale, yv, (int)M, (int)N, (int)K, group,
+                                     tiled ? 1 : 0};
+        e = ternary::launch_gemv_valu(a, fp16, stream);
+        break;
+    }
     default:
         e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv,
                                    stream, tiled);

@@ -91,6 +91,11 @@ bool gemv_f4_takes(int64_t M, int64_t K, int group, bool fp16);
 // one M) in one launch of the fp4 x fp8 decode kernel.
 hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, bool fp16,
                           int group, hipStream_t stream);
+// Decode GEMV on the vector ALU (gemv_valu.hip; a forced path only): M == 1,
+// K % 256 == 0, per-channel scales or groups of 64, 128 or 256, row-major
+// codes.
+bool gemv_valu_takes(int64_t M, int64_t K, int group, bool tiled);
+hipError_t launch_gemv_valu(const GemvArgs &a, bool fp16, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
 // Tiled codes need the pipelined kernel (gemm_big_takes with tiled).

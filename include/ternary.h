@@ -103,8 +103,14 @@ typedef enum {
     TERNARY_PATH_SIMPLE = 3,   /* plain one-output-per-thread kernel, any valid shape   */
     TERNARY_PATH_GEMV_F4 = 4,  /* decode GEMV on the scaled fp4 x fp8 matrix
                                   instruction (codes as fp4, x as exact fp8 pieces)     */
-    TERNARY_PATH_GEMV_B16 = 5  /* decode GEMV on the bf16/fp16 matrix instruction
+    TERNARY_PATH_GEMV_B16 = 5, /* decode GEMV on the bf16/fp16 matrix instruction
                                   (codes as 16-bit +-2 / 0)                            */
+    TERNARY_PATH_GEMV_VALU = 6 /* decode GEMV on the vector ALU: each code adds +x, -x
+                                  or nothing in fp32 ([nxbn §4.1]), lanes reduced by
+                                  cross-lane exchange; M == 1, K % 256 == 0, per
+                                  channel or groups of 64/128/256, row-major codes
+                                  only.  Never chosen by AUTO (measured slower); kept
+                                  for comparison                                        */
 } ternary_path;
 
 /*

@@ -111,7 +111,10 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(M=9, path=4), -8),                  # fp4 x fp8 decode kernel: M <= 8
     (dict(K=132, g=-1, path=4), -8),
     (dict(M=9, path=5), -8),
-    (dict(path=6), -8),
+    (dict(path=6), -8),                       # VALU decode kernel: K % 256 == 0
+    (dict(M=2, K=256, g=-1, path=6), -8),     # M == 1 only
+    (dict(K=256, g=32, path=6), -8),          # groups of 64, 128, 256 only
+    (dict(path=7), -8),
     # fp4 x fp8 kernel: 8 tokens of K = 65536 do not fit its LDS (x is 1 MB here)
     (dict(M=8, N=16, K=65536, g=-1, path=4, p=FAKE * 64, s=FAKE * 128, y=FAKE * 256), -8),
     # fp16 activations at g = 64 and M = 5 take 8 matrix passes there (at most 4)
