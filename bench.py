@@ -51,6 +51,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -749,6 +750,133 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
     return out, cross
 
 
+# Launch sets profiled on their own (one rocprofv3 run each): config, M, and
+# whether the step is one fused batch call or one call per projection.
+WORKLOADS = {
+    "27b_m16": (4, 16, False), "27b_m64": (4, 64, False), "27b_m256": (4, 256, False),
+    "7b_decode_single_m1": (2, 1, False), "7b_decode_fused_m8": (2, 8, True),
+}
+WORKLOAD_REPS = 6
+
+
+def run_workload(tl, name):
+    """Run one launch set of WORKLOADS (tiled codes): the copy probe, then
+    WORKLOAD_REPS launches of each projection (or fused steps), after one
+    untimed launch each."""
+    import torch
+    cfg, M, fused = WORKLOADS[name]
+    layer = Layer(tl, cfg, M, layout="tiled")
+    copy_probe()
+    if cfg == 4:  # MFMA reference for the GEMM launches' busy counters
+        buf = torch.empty(2048 * tl.PROBE_THREADS, dtype=torch.float32, device="cuda:0")
+        tl.probe_mfma(2048, PROBE_ITERS[2048], buf)
+        torch.cuda.synchronize()
+        del buf
+    if fused:
+        for i in range(WORKLOAD_REPS + 1):
+            layer.step(tl, i)
+    else:
+        for j in range(len(layer.shapes)):
+            for i in range(WORKLOAD_REPS + 1):
+                layer.launch(tl, j, i)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": name, "shapes": [s.name for s in layer.shapes], "M": M,
+                      "fused": fused, "reps": WORKLOAD_REPS + 1}))
+
+
+def summarize_workload(name: str, dirs) -> None:
+    """Digest the counter runs of one WORKLOADS entry: per (kernel, grid)
+    group of dispatches, in launch order, the mean of each counter; FETCH_SIZE
+    and WRITE_SIZE scaled to bytes by the copy probe and set against the
+    algorithmic bytes of the projection the group runs."""
+    import synth
+    cfg, M, fused = WORKLOADS[name]
+    shapes = list(synth.CONFIGS[cfg].shapes)
+    g = synth.CONFIGS[cfg].group_size
+    groups, probe, mprobe = {}, {}, {}
+    for d in dirs:
+        per = {}
+        for r in read_counter_csv(Path(d)):
+            key = r["Dispatch_Id"]
+            per.setdefault(key, [r["Kernel_Name"], int(r.get("Grid_Size", 0)), {}])
+            c = r["Counter_Name"]
+            per[key][2][c] = per[key][2].get(c, 0.0) + float(r["Counter_Value"])
+        n_main = 0
+        for key in sorted(per, key=int):
+            kname, grid, vals = per[key]
+            if "neg_kernel" in kname:
+                for c, v in vals.items():
+                    probe.setdefault(c, []).append(v)
+                continue
+            if "probe_mfma_kernel" in kname:
+                for c, v in vals.items():
+                    mprobe.setdefault(c, []).append(v)
+                continue
+            short = kname.replace("(anonymous namespace)::", "").replace("ternary::", "")
+            short = re.sub(r"^void ", "", short)
+            short = re.sub(r"\(.*$", "", short)
+            if not re.search(r"gemv|gemm|simple", short):
+                continue  # the layer's pack / tile kernels
+            # launches run projection by projection, WORKLOAD_REPS + 1 each; a
+            # split-K reduce belongs to the GEMM before it
+            if "split_reduce" in short:
+                idx = max(n_main - 1, 0) // (WORKLOAD_REPS + 1)
+            else:
+                idx = n_main // (WORKLOAD_REPS + 1)
+                n_main += 1
+            label = "fused step" if fused else (shapes[idx].name if idx < len(shapes) else "?")
+            grp = groups.setdefault((label, short, grid), {})
+            for c, v in vals.items():
+                grp.setdefault(c, []).append(v)
+    mean = lambda v: sum(v) / len(v)
+    k_fetch = COPY_PROBE_BYTES / (mean(probe["FETCH_SIZE"]) * 1024.0)
+    k_write = COPY_PROBE_BYTES / (mean(probe["WRITE_SIZE"]) * 1024.0)
+    by_name = {s.name: s for s in shapes}
+    tot = sum(alg_bytes(s.N, s.K, M, g) for s in shapes)
+    lines = [f"# Counters of the launch set '{name}' (config {cfg}, M={M}, tiled codes, "
+             f"{'one fused batch call per step' if fused else 'one call per projection'}),",
+             "# one rocprofv3 --pmc run per counter set, each of",
+             f"#   python3 bench.py --workload {name}",
+             "# e.g. rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o bench -- "
+             f"python3 bench.py --workload {name}",
+             "# (likewise WRITE_SIZE, and for GEMM launches SQ_VALU_MFMA_BUSY_CYCLES "
+             "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES), then",
+             f"#   python3 bench.py --summarize-workload {name} <F> <W> [<MFMA>]",
+             "# Per (kernel, grid) group in launch order: dispatches, mean KiB per dispatch",
+             "# mfma_busy_vs_probe: SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE of the group over",
+             "# that of the MFMA loop probe (probe_mfma_kernel, run in the same process).",
+             "# (summed over instances); traffic = FETCH*fetch_scale + WRITE*write_scale in",
+             f"# bytes, the scales from a copy kernel of known size (torch.neg over "
+             f"{COPY_PROBE_BYTES >> 20} MiB fp32).",
+             f"source_hash {kernel_source_hash()}",
+             f"fetch_scale {k_fetch:.5f}", f"write_scale {k_write:.5f}"]
+    if fused:
+        lines.append(f"alg_bytes_per_step {tot}")
+    for k, v in groups.items():
+        label, short, grid = k
+        n = len(next(iter(v.values())))
+        row = [f"[{label}] {short[:70]} grid={grid} n={n}"]
+        if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+            f_k, w_k = mean(v["FETCH_SIZE"]), mean(v["WRITE_SIZE"])
+            t = f_k * 1024 * k_fetch + w_k * 1024 * k_write
+            row.append(f"fetch_kib {f_k:.1f} write_kib {w_k:.1f} traffic_bytes {t:.0f}")
+            if label in by_name and "split_reduce" not in short:
+                a = alg_bytes(by_name[label].N, by_name[label].K, M, g)
+                row.append(f"alg_bytes {a} traffic/alg {t / a:.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "GRBM_GUI_ACTIVE" in v:
+            busy = mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / mean(v["GRBM_GUI_ACTIVE"])
+            row.append(f"mfma_busy_per_gui {busy:.3f}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mprobe:
+                pb = mean(mprobe["SQ_VALU_MFMA_BUSY_CYCLES"]) / mean(mprobe["GRBM_GUI_ACTIVE"])
+                row.append(f"mfma_busy_vs_probe {busy / pb:.3f}")
+        lines.append("  ".join(row))
+    fam = "gemm_dma" if cfg == 4 else "gemv_f4"
+    path = ROOT / "profiles" / f"{fam}_{name}_counters.txt"
+    path.parent.mkdir(exist_ok=True)
+    path.write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_probe():
     """A plain read+write kernel of known size, for counter calibration."""
     import torch
@@ -867,6 +995,10 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "LDS_DIR"))
     ap.add_argument("--summarize-valu", metavar="VALU_DIR")
     ap.add_argument("--detail", type=str, default=None, help="write per-shape results here")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS),
+                    help="run one launch set for counter collection (no timing)")
+    ap.add_argument("--summarize-workload", nargs="+", metavar="NAME_AND_DIRS",
+                    help="NAME DIR [DIR ...]: digest counter runs of --workload NAME")
     args = ap.parse_args()
     global SETTLE_S
     SETTLE_S = max(0.0, args.settle_ms) / 1e3
@@ -883,6 +1015,9 @@ def main():
     if args.summarize_valu:
         summarize_valu(args.summarize_valu)
         return
+    if args.summarize_workload:
+        summarize_workload(args.summarize_workload[0], args.summarize_workload[1:])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(a sharded layer would split the N rows of each projection across GPUs; "
@@ -894,6 +1029,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     tl.lib()
+    if args.workload:
+        run_workload(tl, args.workload)
+        return
 
     log("[bench] building the decode layer (config 2, M=1, tiled codes)")
     dec = Layer(tl, DECODE_CFG, 1, layout="tiled")

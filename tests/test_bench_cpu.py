@@ -176,3 +176,42 @@ def test_summarize_valu_takes_the_fused_launch(tmp_path, monkeypatch):
     assert float(kv["VALUBusy"]) == pytest.approx(38.0)
     assert float(kv["wait_share"]) == pytest.approx(28.0 / 58.0, rel=1e-3)
     assert float(kv["issue_share"]) == pytest.approx(0.25, rel=1e-3)
+
+
+def test_summarize_workload_labels_projections(tmp_path, monkeypatch):
+    # dispatches run projection by projection (WORKLOAD_REPS + 1 each); a
+    # split-K reduce belongs to the GEMM before it; pack/tile kernels are left out
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    cols = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    n = bench.WORKLOAD_REPS + 1
+    gemm = "void ternary::dma::gemm_dma_kernel<false, 128, ternary::dma::Cfg<128, 16> >(ternary::dma::BigBatch)"
+    red = "void ternary::dma::gemm_split_reduce<false, true, X>(float4 const*)"
+    for counter, scale in (("FETCH_SIZE", 1), ("WRITE_SIZE", 2)):
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=cols)
+            w.writeheader()
+            i = 1
+            rows = [("ternary::tile_kernel(x)", 5, 999.0),
+                    ("at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>", 7,
+                     (bench.COPY_PROBE_BYTES / 1024) / (2 if counter == "FETCH_SIZE" else 1))]
+            for shape, grid in (("up", 100), ("down", 70)):
+                for _ in range(n):
+                    rows.append((gemm, grid, 1000.0 * scale))
+                    rows.append((red, 3, 10.0))
+            for k, g, v in rows:
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Grid_Size": g,
+                            "Counter_Name": counter, "Counter_Value": v})
+                i += 1
+    bench.summarize_workload("27b_m16", [tmp_path / "FETCH_SIZE", tmp_path / "WRITE_SIZE"])
+    text = (tmp_path / "profiles" / "gemm_dma_27b_m16_counters.txt").read_text()
+    lines = [ln for ln in text.splitlines() if ln.startswith("[")]
+    assert len(lines) == 4, lines
+    assert lines[0].startswith("[up] dma::gemm_dma_kernel") and f"n={n}" in lines[0]
+    assert lines[1].startswith("[up] dma::gemm_split_reduce")
+    assert lines[2].startswith("[down] dma::gemm_dma_kernel") and "grid=70" in lines[2]
+    assert lines[3].startswith("[down] dma::gemm_split_reduce")
+    assert "tile_kernel" not in text
+    # 1000 KiB fetched (scale 2) + 2000 KiB written (scale 1) per dispatch
+    assert f"traffic_bytes {4000 * 1024}" in lines[0]
