@@ -712,15 +712,25 @@ int device_cus()
 }
 
 // K slices of the pipelined kernel (whole rounds of NS steps each, at most
-// one round apart): enough that tiles x slices cover the compute units once
-// (more slices would add partial-tile traffic), keeping at least two rounds
-// per slice, within a 2 GiB workspace.
+// one round apart): enough that tiles x slices cover the compute units once,
+// keeping at least two rounds per slice, within a 2 GiB workspace.  When the
+// tiles alone fill at most a quarter of the units and twice the slices would
+// still hold three rounds each, they cover the units twice (more workgroups
+// in flight).  Measured on MI355X: the 5120 x 25600 projection (group 128,
+// 40 or 20 tiles, 3.8 rounds per doubled slice) at M = 16 / 32 / 64 takes
+// 35 / 40 / 51 against 43 / 48 / 53 us; the 4096 x 18944 one (per channel,
+// 2.3 rounds per doubled slice) slowed from 19 / 22 / 23 to 21 / 24 / 31 us
+// and the 25600 x 5120 one at M = 64 (100 tiles) from 43 to 44.5 us, on the
+// extra partial-tile traffic.
 int big_ksplit(int tiles, int K, int ns, int tile_elems)
 {
     const int rounds = K / (dma::TK * ns), cus = device_cus();
     if ((int64_t)tiles >= cus)
         return 1;
     int ks = (cus + tiles - 1) / tiles;
+    const int ks2 = (2 * cus + tiles - 1) / tiles;
+    if (4 * tiles <= cus && rounds >= 3 * ks2)
+        ks = ks2;
     ks = std::min(ks, rounds / 2);
     while (ks > 1 && (int64_t)tiles * ks * tile_elems * 4 > (int64_t(1) << 31))
         --ks;
