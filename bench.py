@@ -870,7 +870,7 @@ def summarize_workload(name: str, dirs) -> None:
                 pb = mean(mprobe["SQ_VALU_MFMA_BUSY_CYCLES"]) / mean(mprobe["GRBM_GUI_ACTIVE"])
                 row.append(f"mfma_busy_vs_probe {busy / pb:.3f}")
         lines.append("  ".join(row))
-    fam = "gemm_dma" if cfg == 4 else "gemv_f4"
+    fam = "gemm_dma" if cfg == 4 else ("gemv_f4" if M == 1 else "gemv_stream")
     path = ROOT / "profiles" / f"{fam}_{name}_counters.txt"
     path.parent.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")

@@ -5,9 +5,18 @@
 // fused QKV weight share one launch, which pays the fixed launch and
 // first-byte latency once).  Two decode kernels exist: gemv_f4.hip (codes as
 // fp4, activations as exact fp8 pieces, on the scaled fp4 x fp8 matrix
-// instruction; the default wherever its LDS holds the activations) and
-// gemv_stream.hip (codes as 16-bit +-2 / 0 on the bf16/fp16 matrix
-// instruction; every other decode shape).  Both read row-major and tiled codes.
+// instruction) and gemv_stream.hip (codes as 16-bit +-2 / 0 on the bf16/fp16
+// matrix instruction).  Both read row-major and tiled codes.
+//
+// The automatic choice takes the fp4 kernel for one token and the 16-bit one
+// for 2 to 8 tokens wherever it takes the shape (the fp4 kernel otherwise):
+// every fp4 workgroup converts the whole activation block into fp8 pieces,
+// work that grows with the tokens, while the 16-bit kernel feeds x to the
+// matrix cores as it is.  Measured on MI355X (tiled codes, fused launches of
+// the 7B layer): 2 / 4 / 8 tokens 18.1 / 21.5 / 27.2 us on the 16-bit kernel
+// against 20.7 / 23.4 / 33.8 us with the fp4 one; the 27B group-128 pair at
+// 4 tokens 23.0 against 36.6 us; at one token the fp4 kernel wins (7B layer
+// 14.3 against 16.1 us).
 #include "internal.h"
 
 namespace ternary {
@@ -47,7 +56,9 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             const GemvArgs &a = args[order[oi]];
             if (a.group != group || a.M == 0 || a.N == 0)
                 continue;
-            const bool use_f4 = kernel != GemvKernel::B16 && gemv_f4_takes(a.M, a.K, group, fp16);
+            const bool use_f4 =
+                kernel != GemvKernel::B16 && gemv_f4_takes(a.M, a.K, group, fp16) &&
+                (kernel == GemvKernel::F4 || a.M == 1 || !gemv_stream_takes(a.M, a.K, group));
             if (use_f4)
                 f4[a.M - 1][nf[a.M - 1]++] = order[oi];
             else if (kernel != GemvKernel::F4 && gemv_stream_takes(a.M, a.K, group))

@@ -97,8 +97,9 @@ typedef enum { TERNARY_BF16 = 0, TERNARY_FP16 = 1 } ternary_dtype;
 typedef enum {
     TERNARY_PATH_AUTO = 0,
     TERNARY_PATH_GEMV = 1,     /* decode GEMV, requires 1 <= M <= ternary_gemv_max_m();
-                                  the fp4 x fp8 kernel where it takes the shape, else
-                                  the 16-bit one                                       */
+                                  at M == 1 the fp4 x fp8 kernel, at larger M the
+                                  16-bit one, each where it takes the shape, else
+                                  the other                                            */
     TERNARY_PATH_GEMM = 2,     /* prefill kernel (bf16/fp16 MFMA)                       */
     TERNARY_PATH_SIMPLE = 3,   /* plain one-output-per-thread kernel, any valid shape   */
     TERNARY_PATH_GEMV_F4 = 4,  /* decode GEMV on the scaled fp4 x fp8 matrix
