@@ -20,7 +20,7 @@ FLAGS = [
     # packed fp32 VALU forms stay off: all fp32 math is emitted as scalar ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_f4.hip", "gemv_stream.hip", "gemv_valu.hip",
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_f4.hip", "gemv_stream.hip", "gemv_valu.hip", "gemm_few.hip",
            "gemm.hip", "simple.hip", "noalloc.hip", "workspace.hip", "probe.hip", "quantize.hip"]
 
 

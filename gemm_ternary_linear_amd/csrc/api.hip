@@ -8,9 +8,11 @@
 #include "../../include/ternary.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -88,10 +90,20 @@ int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, cons
     return TERNARY_OK;
 }
 
-int select_path(int64_t M, int64_t K, int group)
+// Whether the automatic choice gives a problem to the few-token GEMM: the
+// token counts just past the decode GEMV (9 .. 16), where it runs every
+// measured shape faster than the GEMM.
+bool few_preferred(int64_t M, int64_t N, int64_t K, int group, const void *scale)
+{
+    return M > ternary::kGemvMaxM && ternary::gemm_few_takes(M, N, K, group, scale);
+}
+
+int select_path(int64_t M, int64_t N, int64_t K, int group, const void *scale)
 {
     if (ternary::gemv_preferred(M, K, group))
         return TERNARY_PATH_GEMV;
+    if (few_preferred(M, N, K, group, scale))
+        return TERNARY_PATH_FEW;
     if (ternary::gemm_takes(M, K, group))
         return TERNARY_PATH_GEMM;
     return TERNARY_PATH_SIMPLE;
@@ -104,6 +116,8 @@ int select_path_tiled(int64_t M, int64_t N, int64_t K, int group, const void *sc
 {
     if (ternary::gemv_preferred(M, K, group))
         return TERNARY_PATH_GEMV;
+    if (few_preferred(M, N, K, group, scale))
+        return TERNARY_PATH_FEW;
     if (ternary::gemm_big_takes((int)M, (int)N, (int)K, group, scale, true))
         return TERNARY_PATH_GEMM;
     return TERNARY_PATH_SIMPLE;
@@ -117,7 +131,7 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
     const int group = group_of(group_size);
     const bool fp16 = dtype == TERNARY_FP16;
     if (path == TERNARY_PATH_AUTO)
-        path = tiled ? select_path_tiled(M, N, K, group, scale) : select_path(M, K, group);
+        path = tiled ? select_path_tiled(M, N, K, group, scale) : select_path(M, N, K, group, scale);
     ternary::GemvKernel gk = ternary::GemvKernel::AUTO;
     switch (path) {
     case TERNARY_PATH_GEMV_F4:
@@ -141,6 +155,10 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
         if (!(M == 0 || N == 0 || ternary::gemv_valu_takes(M, K, group, tiled)))
             return TERNARY_ERR_PATH;
         break;
+    case TERNARY_PATH_FEW:
+        if (!(M == 0 || N == 0 || ternary::gemm_few_takes(M, N, K, group, scale)))
+            return TERNARY_ERR_PATH;
+        break;
     default: return TERNARY_ERR_PATH;
     }
     if (M == 0 || N == 0)
@@ -161,6 +179,13 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
         const ternary::GemvArgs a = {xv, packed, scale, yv, (int)M, (int)N, (int)K, group,
                                      tiled ? 1 : 0};
         e = ternary::launch_gemv_valu(a, fp16, stream);
+        break;
+    }
+    case TERNARY_PATH_FEW: {
+        const ternary::GemvArgs a = {xv, packed, scale, yv, (int)M, (int)N, (int)K, group,
+                                     tiled ? 1 : 0};
+        const int order = 0;
+        e = ternary::launch_gemm_few(&a, &order, 1, fp16, stream);
         break;
     }
     default:
@@ -221,9 +246,9 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
     // Plan every launch before the first one: decode problems fused, the
     // pipelined GEMM's problems grouped, the rest one call each.
     const bool fp16 = dtype == TERNARY_FP16;
-    GemvArgs fused[TERNARY_MAX_BATCH], grouped_gemm[TERNARY_MAX_BATCH];
+    GemvArgs fused[TERNARY_MAX_BATCH], grouped_gemm[TERNARY_MAX_BATCH], few[TERNARY_MAX_BATCH];
     int others[TERNARY_MAX_BATCH];
-    int nf = 0, ng = 0, no = 0;
+    int nf = 0, ng = 0, no = 0, nw = 0;
     for (int i = 0; i < count; ++i) {
         const ternary_problem &p = problems[i];
         if (p.M == 0 || p.N == 0)
@@ -234,17 +259,40 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
                             group_of(p.group_size), tiled ? 1 : 0};
         if (gemv_kernel_takes(GemvKernel::AUTO, p.M, p.K, a.group, fp16, tiled))
             fused[nf++] = a;
+        else if (few_preferred(p.M, p.N, p.K, a.group, a.scale))
+            few[nw++] = a;
         else if (gemm_takes(p.M, p.K, a.group) &&
                  gemm_big_takes(a.M, a.N, a.K, a.group, a.scale, tiled))
             grouped_gemm[ng++] = a;
         else
             others[no++] = i;
     }
+    // Few-token problems: one launch per scale mode, longest K first.
+    int few_order[TERNARY_MAX_BATCH], few_first[TERNARY_MAX_BATCH + 1], nfl = 0;
+    {
+        int n = 0;
+        for (const int group : {0, 128, 256}) {
+            const int first = n;
+            for (int i = 0; i < nw; ++i)
+                if (few[i].group == group)
+                    few_order[n++] = i;
+            for (int i = first + 1; i < n; ++i)  // stable insertion sort, K descending
+                for (int j = i; j > first && few[few_order[j]].K > few[few_order[j - 1]].K; --j)
+                    std::swap(few_order[j], few_order[j - 1]);
+            if (n > first)
+                few_first[nfl++] = first;
+        }
+        few_first[nfl] = n;
+    }
     FixedScratch fs = {nullptr, 0};
     if (noalloc) {
-        // split-K partials go to the library's static scratch: check its size
-        // before anything is enqueued
-        const size_t need = ng ? gemm_batch_scratch_need(grouped_gemm, ng) : 0;
+        // split-K partials go to the library's static scratch (one launch
+        // after another on the stream): check its size before anything is
+        // enqueued
+        size_t need = ng ? gemm_batch_scratch_need(grouped_gemm, ng) : 0;
+        for (int l = 0; l < nfl; ++l)
+            need = std::max(need, gemm_few_scratch_need(few, few_order + few_first[l],
+                                                        few_first[l + 1] - few_first[l]));
         if (need > noalloc_scratch_bytes())
             return TERNARY_ERR_SCRATCH;
         const int st = hip_status(noalloc_scratch(&fs.ptr));
@@ -263,6 +311,13 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
     if (ng) {
         const int st = hip_status(launch_gemm_batch(grouped_gemm, ng, fp16, stream,
                                                     noalloc ? &fs : nullptr));
+        if (st != TERNARY_OK)
+            return st;
+    }
+    for (int l = 0; l < nfl; ++l) {
+        const int st = hip_status(launch_gemm_few(few, few_order + few_first[l],
+                                                  few_first[l + 1] - few_first[l], fp16, stream,
+                                                  noalloc ? &fs : nullptr));
         if (st != TERNARY_OK)
             return st;
     }
@@ -372,7 +427,8 @@ int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size)
     const int sh = check_shape(M, N, K, group_size);
     if (sh != TERNARY_OK)
         return sh;
-    return select_path(M, K, group_of(group_size));
+    // (the few-token GEMM's group-128 scale alignment is assumed met)
+    return select_path(M, N, K, group_of(group_size), reinterpret_cast<const void *>(16));
 }
 
 int ternary_linear_ex(const void *x, int dtype, int64_t M, int64_t N, int64_t K,

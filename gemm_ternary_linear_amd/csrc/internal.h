@@ -97,6 +97,21 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
 // codes.
 bool gemv_valu_takes(int64_t M, int64_t K, int group, bool tiled);
 hipError_t launch_gemv_valu(const GemvArgs &a, bool fp16, hipStream_t stream);
+// Few-token streaming GEMM (gemm_few.hip): 1 <= M <= kFewMaxM, K % 256 == 0,
+// K <= kGemvMaxK, per-channel scales or groups of 128 (4-byte aligned scale
+// array) or 256; row-major and tiled codes.  One launch for up to
+// kGemvMaxBatch problems that share the scale mode and the token tile (M <= 8
+// or 8 < M <= 16).
+constexpr int kFewMaxM = 16;
+bool gemm_few_takes(int64_t M, int64_t N, int64_t K, int group, const void *scale);
+struct FixedScratch;
+// K ranges long against the launch's other problems, or launches with few
+// channel blocks, are sliced over workgroups: their fp32 sums go to `fixed`
+// when given (it must hold gemm_few_scratch_need() bytes), else to the
+// stream's workspace, and a second kernel adds the slices in order.
+hipError_t launch_gemm_few(const GemvArgs *args, const int *order, int count, bool fp16,
+                           hipStream_t stream, const struct FixedScratch *fixed = nullptr);
+size_t gemm_few_scratch_need(const GemvArgs *args, const int *order, int count);
 // Compute units of the current device (cached per device).
 int device_cus();
 // Tiled codes need the pipelined kernel (gemm_big_takes with tiled).

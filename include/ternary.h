@@ -106,12 +106,16 @@ typedef enum {
                                   instruction (codes as fp4, x as exact fp8 pieces)     */
     TERNARY_PATH_GEMV_B16 = 5, /* decode GEMV on the bf16/fp16 matrix instruction
                                   (codes as 16-bit +-2 / 0)                            */
-    TERNARY_PATH_GEMV_VALU = 6 /* decode GEMV on the vector ALU: each code adds +x, -x
+    TERNARY_PATH_GEMV_VALU = 6, /* decode GEMV on the vector ALU: each code adds +x, -x
                                   or nothing in fp32 ([nxbn §4.1]), lanes reduced by
                                   cross-lane exchange; M == 1, K % 256 == 0, per
                                   channel or groups of 64/128/256, row-major codes
                                   only.  Never chosen by AUTO (measured slower); kept
                                   for comparison                                        */
+    TERNARY_PATH_FEW = 7       /* few-token streaming GEMM: 1 <= M <= 16, K % 256 == 0,
+                                  K <= 65536, per channel or groups of 128 / 256; x
+                                  shared in LDS by the eight 16-channel blocks of a
+                                  workgroup, codes streamed into registers             */
 } ternary_path;
 
 /*
@@ -196,12 +200,14 @@ int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t gro
  * each group's (or the row's) fp32 partial sum; y is rounded from fp32 to the
  * output dtype, round-to-nearest-even.  x and s must be finite (results for
  * non-finite inputs are unspecified) and |x| < 2^126.
- * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV, larger M the
- * MFMA GEMM; shapes neither fast kernel takes (K % 128 != 0) run the plain
- * kernel.  The GEMV gives each token 2 MFMA columns (per channel, groups of
- * 128 or 256), 4 (groups of 64) or 8 (groups of 32) of 16, so it takes M <= 4
- * for groups of 64 and M <= 2 for groups of 32, and K <= 65536; the GEMM runs
- * the rest.  Results of different paths agree within the bound
+ * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (the fp4 x fp8
+ * kernel at M == 1, the 16-bit one at larger M, each where it takes the
+ * shape); 9 <= M <= 16 the few-token GEMM (TERNARY_PATH_FEW) where it takes
+ * the shape; larger M and the rest the MFMA GEMM; shapes no fast kernel
+ * takes (K % 128 != 0) run the plain kernel.  The GEMV gives each token 2
+ * MFMA columns (per channel, groups of 128 or 256), 4 (groups of 64) or 8
+ * (groups of 32) of 16, so it takes M <= 4 for groups of 64 and 32 (M <= 2
+ * where the fp4 kernel's LDS cannot hold x), and K <= 65536.  Results of different paths agree within the bound
  * |y - y_ref| <= 1e-3 * sum_k |x_k| * s(n,k) + 1e-6, not bitwise.
  */
 int ternary_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K,
@@ -261,7 +267,9 @@ typedef struct {
  * overlap any input or any other output of the batch (TERNARY_ERR_ALIAS).  On
  * any error nothing is launched.  Problems the automatic path sends to the
  * decode GEMV (see ternary_linear) run together in one launch per scale
- * mode (per channel, or each group size) and token count M;
+ * mode (per channel, or each group size) and token count M; problems the
+ * automatic path sends to the few-token GEMM run together in one launch per
+ * scale mode (plus one launch adding the K slices of sliced problems);
  * the GEMM problems the pipelined kernel takes (K % 256 == 0; group sizes 64,
  * 128 or 256 with an even number of groups per row and 4-byte-aligned scales)
  * run together in one grouped GEMM launch per scale mode and tile shape
@@ -275,7 +283,9 @@ int ternary_linear_batch(const ternary_problem *problems, int count, int dtype,
                          hipStream_t stream);
 
 /* The path ternary_linear_ex(..., TERNARY_PATH_AUTO, ...) takes for a shape
- * (a ternary_path value), or a negative status for invalid shapes. */
+ * (a ternary_path value), or a negative status for invalid shapes.  A
+ * group-128 scale array is assumed 4-byte aligned (else the few-token GEMM's
+ * shapes take the GEMM). */
 int ternary_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size);
 
 /* Largest M the decode GEMV accepts. */
@@ -305,7 +315,8 @@ int ternary_shutdown(void);
  * allocate device memory: code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, validation, results (the
  * same bits) and launches as ternary_linear_batch, but the fp32 partial tiles
- * of a split-K GEMM go to a static device array of the library
+ * of a split-K GEMM and the K-slice sums of the few-token GEMM (one launch
+ * after another, so they share it) go to a static device array of the library
  * (TERNARY_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead
  * of the per-stream workspace: the call never allocates or frees.  A batch
  * whose split-K partials need more returns TERNARY_ERR_SCRATCH and enqueues

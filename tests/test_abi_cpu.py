@@ -63,7 +63,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 5
+    assert tl.abi_version() == 6
     assert tl.gemv_max_m() == 8
     for st in range(0, -11, -1):
         s = tl.status_string(st)
@@ -114,7 +114,13 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(path=6), -8),                       # VALU decode kernel: K % 256 == 0
     (dict(M=2, K=256, g=-1, path=6), -8),     # M == 1 only
     (dict(K=256, g=32, path=6), -8),          # groups of 64, 128, 256 only
-    (dict(path=7), -8),
+    (dict(path=7), -8),                       # few-token GEMM: K % 256 == 0
+    (dict(path=8), -8),
+    (dict(M=17, K=256, g=-1, path=7), -8),    # M <= 16
+    (dict(K=256, g=64, path=7), -8),          # per channel, groups of 128 or 256
+    (dict(K=256, g=32, path=7), -8),
+    (dict(K=256, g=128, s=FAKE * 3 + 2, path=7), -8),  # group-128 scales 4-byte aligned
+    (dict(M=1, K=65792, g=-1, path=7, p=FAKE * 16, s=FAKE * 64, y=FAKE * 128), -8),
     # fp4 x fp8 kernel: 8 tokens of K = 65536 do not fit its LDS (x is 1 MB here)
     (dict(M=8, N=16, K=65536, g=-1, path=4, p=FAKE * 64, s=FAKE * 128, y=FAKE * 256), -8),
     # fp16 activations at g = 64 and M = 5 take 8 matrix passes there (at most 4)
@@ -169,7 +175,11 @@ def test_quantize_reject(tl):
 
 
 @pytest.mark.parametrize("M,K,g,path", [
-    (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "gemm"),
+    (1, 4096, -1, "gemv"), (8, 4096, 128, "gemv"), (9, 4096, 128, "few"),
+    # 9 .. 16 tokens: the few-token GEMM where it takes the shape (K % 256 == 0,
+    # per channel or groups of 128 / 256), else the GEMM
+    (16, 4096, -1, "few"), (12, 4352, 256, "few"), (17, 4096, -1, "gemm"),
+    (9, 4096, 64, "gemm"), (9, 384, 128, "gemm"), (16, 65792, -1, "gemm"),
     (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
     # long K up to 65536 stays on the GEMV at every M <= 8 (measured faster)
     (8, 18944, -1, "gemv"), (4, 25600, 128, "gemv"), (3, 18944, -1, "gemv"),
@@ -182,7 +192,7 @@ def test_quantize_reject(tl):
 ])
 def test_select_path(tl, M, K, g, path):
     if M == 0:
-        assert tl.select_path(M, 16, K, g) in ("gemv", "gemm", "simple")
+        assert tl.select_path(M, 16, K, g) in ("gemv", "few", "gemm", "simple")
     else:
         assert tl.select_path(M, 16, K, g) == path
 

@@ -65,9 +65,10 @@ def _run_and_check(tl, probs, dtype="bf16", samples=None):
             check_within(ya[ms, ns], y_ref, bound, f"single problem {i}")
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 8, 16])
 def test_batch_7b_decode_layer(tl, M):
-    # every output of the fused decode launch against the oracle
+    # every output of the fused decode launch (at 16 tokens: the fused
+    # few-token GEMM launch, the down projection K-sliced) against the oracle
     say(f"batch of the 7 decode projections, M={M}")
     specs = [(M, s.N, s.K, -1) for s in synth.CONFIGS[2].shapes]
     _run_and_check(tl, _problems(np.random.default_rng(40 + M), specs))
@@ -79,6 +80,16 @@ def test_batch_mixed(tl, dtype):
     specs = [(1, 300, 1024, 128), (3, 65, 2304, -1), (8, 129, 9216, 128), (64, 100, 512, 128),
              (2, 40, 132, -1), (5, 1, 128, 128), (1, 2000, 640, -1)]
     _run_and_check(tl, _problems(np.random.default_rng(41), specs, dtype), dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_batch_few_token_mixed(tl, dtype):
+    # 9 .. 16 tokens in one batch: two scale modes (two few-token launches),
+    # a K-sliced problem, a group size the few-token GEMM does not take (GEMM)
+    say(f"few-token batch {dtype}")
+    specs = [(16, 640, 4096, -1), (12, 320, 8192, 128), (9, 1000, 1024, 128),
+             (16, 130, 2304, -1), (10, 200, 1024, 64), (16, 48, 512, 256)]
+    _run_and_check(tl, _problems(np.random.default_rng(45), specs, dtype), dtype=dtype)
 
 
 def test_batch_big_k_chunked(tl):

@@ -32,9 +32,10 @@ def tl():
 
 def test_graph_replays_match_eager(tl):
     import torch
-    say("graph capture of GEMV (per-channel, grouped) and GEMM launches")
+    say("graph capture of GEMV (per-channel, grouped), few-token GEMM and GEMM launches")
     rng = np.random.default_rng(31)
-    specs = [(1, 1000, 4096, -1), (4, 700, 2048, 128), (96, 300, 1024, 128), (1, 64, 132, -1)]
+    specs = [(1, 1000, 4096, -1), (4, 700, 2048, 128), (96, 300, 1024, 128), (1, 64, 132, -1),
+             (16, 640, 4096, -1), (12, 320, 8192, 128)]
     cases = []
     for M, N, K, g in specs:
         codes = synth.draw_codes(rng, N, K, 0.3, 0.3)

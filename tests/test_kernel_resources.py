@@ -1,5 +1,5 @@
-"""Every decode GEMV kernel instance compiles without scratch (register
-spills): the decode kernels are short-lived bursts of waves, and per-wave
+"""Every decode GEMV and few-token GEMM kernel instance compiles without
+scratch (register spills): these kernels are short-lived bursts of waves, and per-wave
 scratch set-up and traffic would cost them directly.  Compiles the decode
 sources for gfx950 (device code only) with hipcc's resource-usage remarks."""
 
@@ -15,7 +15,7 @@ import pytest
 ROOT = Path(__file__).resolve().parent.parent
 CSRC = ROOT / "gemm_ternary_linear_amd" / "csrc"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-DECODE_SOURCES = ["gemv_f4.hip", "gemv_stream.hip"]
+DECODE_SOURCES = ["gemv_f4.hip", "gemv_stream.hip", "gemm_few.hip"]
 
 
 def _resources(src: str, out_dir: str) -> dict:
@@ -40,10 +40,11 @@ def _resources(src: str, out_dir: str) -> dict:
 
 @pytest.mark.skipif(not Path(HIPCC).exists(), reason="hipcc not available")
 def test_decode_kernels_use_no_scratch():
-    with tempfile.TemporaryDirectory() as d, ThreadPoolExecutor(2) as ex:
+    with tempfile.TemporaryDirectory() as d, ThreadPoolExecutor(3) as ex:
         results = list(ex.map(lambda s: _resources(s, d), DECODE_SOURCES))
     kernels = {k: v for r in results for k, v in r.items() if "kernel" in k}
     assert any("gemv_f4_kernel" in k for k in kernels)
     assert any("gemv_stream_kernel" in k for k in kernels)
+    assert any("few_kernel" in k for k in kernels)
     spills = {k: v.get("ScratchSize") for k, v in kernels.items() if v.get("ScratchSize", 0) != 0}
     assert not spills, f"kernel instances with scratch: {spills}"

@@ -3,8 +3,8 @@ ABI, against ternary_linear_batch on the same inputs: the same bits, and both
 within the stated bound of the oracle, |y - y_ref| <= 1e-3 * sum_k |x_k| s + 1e-6.
 
 Two calls in a row, the second smaller (the static scratch keeps the first
-call's partials; the second must not depend on them), a batch mixing decode
-and prefill problems, a batch whose split-K partials exceed the static buffer
+call's partials; the second must not depend on them), a batch mixing decode,
+few-token (K-sliced) and prefill problems, a batch whose split-K partials exceed the static buffer
 (rejected with nothing enqueued), and a capture on a stream that never ran the
 call (the allocation-free call needs no warm-up).
 """
@@ -98,9 +98,9 @@ def test_noalloc_two_calls_second_smaller(tl):
 
 
 def test_noalloc_mixed_batch(tl):
-    say("noalloc: decode + grouped prefill + 128x128 GEMM in one batch")
+    say("noalloc: decode + grouped prefill + 128x128 GEMM + few-token GEMM in one batch")
     specs = [(1, 4096, 4096, -1), (1, 512, 4096, -1), (256, 300, 2048, 128), (100, 200, 1152, 128),
-             (300, 260, 1024, -1)]
+             (300, 260, 1024, -1), (16, 640, 4096, -1), (12, 320, 8192, 128)]
     _check(tl, _problems(specs, 3), "mixed")
 
 
@@ -122,7 +122,7 @@ def test_noalloc_captures_without_warmup(tl):
     # times with eager work in between: every replay equals the eager result
     import torch
     say("noalloc: capture on a fresh stream")
-    probs = _problems([(2048, 512, 4096, -1), (1, 4096, 4096, -1)], 5)
+    probs = _problems([(2048, 512, 4096, -1), (1, 4096, 4096, -1), (16, 640, 4096, -1)], 5)
     st, eager = _call(tl, probs, noalloc=True)
     torch.cuda.synchronize()
     assert st == 0
