@@ -19,8 +19,8 @@
 //    return in issue order, so the compiler's wait for a slab's codes also
 //    covers the wave's x of that slab; the barrier then covers every wave's.
 //  * x stage layout: per part, per token, 256 elements as 32 chunks of 16
-//    bytes; logical chunk c of token row t sits at physical chunk c ^ (t & 15)
-//    so that the 16 token rows an MFMA B read touches fall on distinct banks.
+//    bytes; logical chunk c of token row t sits at physical chunk c ^ swz(t)
+//    so that the 16 token rows an MFMA B read touches spread over the banks.
 //    Each 1-KB DMA fills two token rows, every lane fetching the logical
 //    chunk of its physical slot; tokens past M and slabs past K read zeros.
 //  * MFMA: v_mfma_f32_16x16x32_{bf16,f16}, rows = channels, columns =
@@ -52,6 +52,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kS = 4;           // x stages in LDS = code slabs in registers per wave
 constexpr int kAhead = kS - 1;  // slabs loaded ahead of the one computed
+constexpr int kFN = 1;          // 16-channel blocks per wave
 constexpr int kOOB = 0x40000000;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
@@ -104,6 +105,13 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// x stage swizzle: logical chunk c of token row t sits at physical chunk
+// c ^ swz(t).  The low three bits spread the 8 rows t & 7 over one
+// 128-byte bank span, bit 4 moves rows 8 .. 15 half a row further: in an LDS
+// read-pattern probe on MI355X this layout read 151 B/clk per CU against 120
+// for c ^ t and 114 for plain contiguous 16-byte lanes.
+__device__ __forceinline__ int swz(int t) { return (t & 7) | ((t & 8) << 1); }
+
 // s_waitcnt with only the vector-memory count limited (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm()
@@ -113,9 +121,10 @@ __device__ __forceinline__ void wait_vm()
 }
 
 // GM: 0 per-channel scales, 1 groups of 256, 2 groups of 128.  MT: tokens of
-// the tile (8 or 16).  KP: K parts per block (the workgroup holds 8 / KP
-// blocks of 16 channels).
-template <bool FP16, int GM, int MT, int KP>
+// the tile (8 or 16).  KP: K parts (the workgroup's waves are RB = 8 / KP row
+// groups x KP parts).  FN: 16-channel blocks per wave (each B read of x feeds
+// FN MFMAs), so a workgroup holds RB * FN blocks.
+template <bool FP16, int GM, int MT, int KP, int FN>
 __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
 {
     constexpr int RB = kWaves / KP;
@@ -125,8 +134,10 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     constexpr int XW = (XI + kWaves - 1) / kWaves;    // x DMAs per wave and stage
     constexpr int ZC = KP * MT * 32;                  // chunk index of a stage's zero area
     constexpr int SU4 = ZC + 64;                      // stage: x chunks + 1 KB of zeros
+    constexpr int NSC = GM == 0 ? 0 : 4;              // scale loads per block and slab
     static_assert(MT == 8 || MT == 16, "tile tokens");
     static_assert(KP == 1 || KP == 2 || KP == 4, "parts");
+    static_assert(FN == 1 || FN == 2 || FN == 4, "blocks per wave");
     static_assert(KP * MT <= 32, "stage size");
     static_assert(KP == 1 || kWaves * 64 <= SU4, "the part reduction fits in stage 0");
     // One LDS object per stage, so that the compiler knows a DMA into one
@@ -153,30 +164,32 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     const int unit = (int)blockIdx.x - batch.unit0[pi];
     const int ks = P.ks, slice = unit % ks;
     const int kp = wave / RB, rb = wave % RB;
-    const int blk = (unit / ks) * RB + rb;
+    const int blk0 = ((unit / ks) * RB + rb) * FN;  // this wave's first block
     const int nblk = (N + 15) >> 4;
-    const int nrows = blk < nblk ? min(16, N - 16 * blk) : 0;
     const int nslabs = K >> 8;
     // K piece (slice, part) covers slabs [piece * L, piece * L + L)
     const int s_lo = (slice * KP + kp) * L;
 
-    // Codes: resource rebased at the block's first row (32-bit offsets).
+    // Codes and scales of block f: resources rebased at the block's first
+    // row (32-bit offsets).
     const int rowbytes = K >> 2;
-    __amdgpu_buffer_rsrc_t wr;
-    int woff, sstride;
-    if (P.tiled) {
-        wr = make_rsrc(P.packed + (int64_t)blk * nslabs * 1024, nrows ? nslabs * 1024u : 0u);
-        woff = lane * 16;
-        sstride = 1024;
-    } else {
-        wr = make_rsrc(P.packed + (int64_t)blk * 16 * rowbytes, (uint32_t)(nrows * rowbytes));
-        woff = col < nrows ? col * rowbytes + g * 16 : kOOB;
-        sstride = 64;
-    }
-    // Scales of the lane's four C rows (channels 16 blk + 4g + r).
     const int ngroups = GM == 0 ? 1 : (GM == 1 ? nslabs : 2 * nslabs);
-    const __amdgpu_buffer_rsrc_t sr =
-        make_rsrc(P.scale + (int64_t)blk * 16 * ngroups, (uint32_t)(nrows * ngroups * 2));
+    __amdgpu_buffer_rsrc_t wr[FN], sr[FN];
+    int nrows[FN], woff[FN];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+        const int blk = blk0 + f;
+        nrows[f] = blk < nblk ? min(16, N - 16 * blk) : 0;
+        if (P.tiled) {
+            wr[f] = make_rsrc(P.packed + (int64_t)blk * nslabs * 1024, nrows[f] ? nslabs * 1024u : 0u);
+            woff[f] = lane * 16;
+        } else {
+            wr[f] = make_rsrc(P.packed + (int64_t)blk * 16 * rowbytes, (uint32_t)(nrows[f] * rowbytes));
+            woff[f] = col < nrows[f] ? col * rowbytes + g * 16 : kOOB;
+        }
+        sr[f] = make_rsrc(P.scale + (int64_t)blk * 16 * ngroups, (uint32_t)(nrows[f] * ngroups * 2));
+    }
+    const int sstride = P.tiled ? 1024 : 64;
 
     // x: DMA xi of this wave is stage instruction q = wave + 8 xi; its lanes
     // fill physical chunks 64 q + lane: part qp, token row t, chunk p.
@@ -187,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         const int q = wave + kWaves * xi;
         const int c = 64 * q + lane;
         const int qp = c / (MT * 32), t = (c >> 5) % MT, p = c & 31;
-        const int lc = p ^ (t & 15);
+        const int lc = p ^ swz(t);
         xpart[xi] = qp;
         xbase[xi] = q < XI && t < M ? (t * K + 8 * lc) * 2 : kOOB;
     }
@@ -197,20 +210,20 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     // column lies outside the tile or outside its group read the zero area.
     int boff[CF];
 #pragma unroll
-    for (int f = 0; f < CF; ++f) {
+    for (int c = 0; c < CF; ++c) {
         int t, p;
         if constexpr (GC == 1) {
             t = col;
             p = 0;
         } else if constexpr (MT == 16) {
             t = col;
-            p = f;
+            p = c;
         } else {
             t = col & 7;
             p = col >> 3;
         }
         const bool on = t < MT && (GC == 1 || (g >> 1) == p);
-        boff[f] = on ? ((kp * MT + t) * 32 + (8 * (g ^ (t >> 3)))) * 16 + 16 * (t & 7) : ZC * 16;
+        boff[c] = on ? ((kp * MT + t) * 32 + ((8 * g) ^ (swz(t) & 24))) * 16 + 16 * (t & 7) : ZC * 16;
     }
     if (tid < 8) {  // B reads of masked lanes stay in the first 128 bytes
         const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -221,8 +234,8 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     __syncthreads();
 
     // ---- loads of slab j (x share, then codes and scales) ---------------
-    u32x4_t w[kS];
-    uint32_t sc[kS][GM == 0 ? 1 : 4];
+    u32x4_t w[kS][FN];
+    uint32_t sc[kS][FN][GM == 0 ? 1 : 4];
     auto issue = [&](auto SL, int j) {
         constexpr int s = decltype(SL)::value;
         const bool in = j < L;
@@ -236,7 +249,10 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         __builtin_amdgcn_sched_barrier(0);
         const int sl = s_lo + j;
         const bool live = in && sl < nslabs;
-        w[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? woff + sl * sstride : kOOB, 0, 0);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            w[s][f] = __builtin_amdgcn_raw_buffer_load_b128(wr[f], live ? woff[f] + sl * sstride : kOOB,
+                                                            0, 0);
         if constexpr (GM != 0) {
             // Offsets clamped into the block instead of selected, so that no
             // lane condition splits a load: rows past N and slabs past the
@@ -244,28 +260,31 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
             // resource reads zeros).
             const int slc = min(sl, nslabs - 1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = min(4 * g + r, nrows - 1);
-                if constexpr (GM == 2)
-                    sc[s][r] = __builtin_amdgcn_raw_buffer_load_b32(
-                        sr, (row * ngroups + 2 * slc) * 2, 0, 0);
-                else
-                    sc[s][r] = __builtin_amdgcn_raw_buffer_load_b16(sr, (row * ngroups + slc) * 2,
-                                                                    0, 0);
-            }
+            for (int f = 0; f < FN; ++f)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = min(4 * g + r, nrows[f] - 1);
+                    if constexpr (GM == 2)
+                        sc[s][f][r] = __builtin_amdgcn_raw_buffer_load_b32(
+                            sr[f], (row * ngroups + 2 * slc) * 2, 0, 0);
+                    else
+                        sc[s][f][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                            sr[f], (row * ngroups + slc) * 2, 0, 0);
+                }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};  // per channel: the running sum
-    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};  // groups: the scaled sum
+    f32x4_t acc[FN], tot[FN];  // per channel: running sums; groups: scaled sums
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+        acc[f] = tot[f] = zero4;
 
-    // Vector memory ops a wave issues per slab, and how many of them follow
-    // its code load of slab j when step j starts: slab j's scale loads, then
-    // the x DMAs, code and scale loads of slabs j+1 and j+2.
-    constexpr int NSC = GM == 0 ? 0 : 4;
-    constexpr int kAfter = NSC + (kAhead - 1) * (XW + 1 + NSC);
+    // Vector memory ops issued after this wave's last code load of slab j
+    // when step j starts: slab j's scale loads, then the x DMAs, code and
+    // scale loads of slabs j+1 .. j+kAhead-1.
+    constexpr int kAfter = FN * NSC + (kAhead - 1) * (XW + FN + FN * NSC);
     static_assert(kAfter <= 63, "vmcnt range");
 
     // One step: slab j from slot / stage s.
@@ -279,43 +298,55 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         issue(std::integral_constant<int, (s + kAhead) % kS>{}, j + kAhead);
-        uint32_t d[8];
-        decode16(w[s].x, d);
 
-        f32x4_t part[CF];
+        f32x4_t part[FN][CF];
 #pragma unroll
-        for (int f = 0; f < CF; ++f)
-            part[f] = GM == 0 ? acc : zero4;
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int c = 0; c < CF; ++c)
+                part[f][c] = GM == 0 ? acc[f] : zero4;
         const lds_u4 *stg = ls[s];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (i % 2 == 0 && i > 0)
-                decode16(w[s][i >> 1], d);
-            const uint4 a = (i & 1) ? make_uint4(d[4], d[5], d[6], d[7])
-                                    : make_uint4(d[0], d[1], d[2], d[3]);
+        for (int wd = 0; wd < 4; ++wd) {  // code word wd: MFMAs 2 wd, 2 wd + 1
+            uint32_t d[FN][8];
 #pragma unroll
-            for (int f = 0; f < CF; ++f) {
-                const u32x4_t bv = *(const lds_u4 *)((const __attribute__((address_space(3))) char *)stg +
-                                                     (boff[f] ^ (16 * i)));
-                part[f] = mfma16<FP16>(a, __builtin_bit_cast(uint4, bv), part[f]);
+            for (int f = 0; f < FN; ++f)
+                decode16(w[s][f][wd], d[f]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * wd + h;
+#pragma unroll
+                for (int c = 0; c < CF; ++c) {
+                    const u32x4_t bv = *(const lds_u4 *)((const __attribute__((address_space(3))) char *)stg +
+                                                         (boff[c] ^ (16 * i)));
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+                        const uint4 a = h ? make_uint4(d[f][4], d[f][5], d[f][6], d[f][7])
+                                          : make_uint4(d[f][0], d[f][1], d[f][2], d[f][3]);
+                        part[f][c] = mfma16<FP16>(a, __builtin_bit_cast(uint4, bv), part[f][c]);
+                    }
+                }
             }
         }
-        if constexpr (GM == 0) {
-            acc = part[0];
-        } else {
 #pragma unroll
-            for (int f = 0; f < CF; ++f)
+        for (int f = 0; f < FN; ++f) {
+            if constexpr (GM == 0) {
+                acc[f] = part[f][0];
+            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint32_t h;
-                    if constexpr (GM == 1)
-                        h = sc[s][r];
-                    else if constexpr (MT == 16)
-                        h = f ? sc[s][r] >> 16 : sc[s][r];
-                    else
-                        h = (col >> 3) ? sc[s][r] >> 16 : sc[s][r];
-                    tot[r] += f16_bits_to_f32((uint16_t)h) * part[f][r];
-                }
+                for (int c = 0; c < CF; ++c)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        uint32_t h;
+                        if constexpr (GM == 1)
+                            h = sc[s][f][r];
+                        else if constexpr (MT == 16)
+                            h = c ? sc[s][f][r] >> 16 : sc[s][f][r];
+                        else
+                            h = (col >> 3) ? sc[s][f][r] >> 16 : sc[s][f][r];
+                        tot[f][r] += f16_bits_to_f32((uint16_t)h) * part[f][c][r];
+                    }
+            }
         }
     };
 
@@ -335,67 +366,70 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     // No DMA may still write LDS when it is reused or the workgroup ends.
     wait_vm<0>();
 
-    f32x4_t res = GM == 0 ? acc : tot;
-    if constexpr (GC == 2 && MT == 8) {
-        // columns t and t + 8 hold token t's two groups
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            res[r] += __shfl_xor(res[r], 8);
-    }
-    if constexpr (KP > 1) {
-        // parts meet in stage 0: [part][block][lane] f32x4
-        __syncthreads();
-        f32x4_t *red = (f32x4_t *)st0;
-        red[(kp * RB + rb) * 64 + lane] = res;
-        __syncthreads();
-        if (kp != 0)
-            return;
-#pragma unroll
-        for (int q = 1; q < KP; ++q) {
-            const f32x4_t o = red[(q * RB + rb) * 64 + lane];
+    for (int f = 0; f < FN; ++f) {
+        f32x4_t res = GM == 0 ? acc[f] : tot[f];
+        if constexpr (GC == 2 && MT == 8) {
+            // columns t and t + 8 hold token t's two groups
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                res[r] += o[r];
+                res[r] += __shfl_xor(res[r], 8);
         }
-    }
-
-    // Epilogue: lane holds channels 16 blk + 4 g + r of token column col.
-    const int t = col;
-    if (t >= M || t >= MT || 4 * g >= nrows)
-        return;
-    const int n = 16 * blk + 4 * g;
-    if (ks > 1) {
-        // this slice's sums (group scales in, per-channel scale not)
-        float *pr = P.partial + ((int64_t)slice * M + t) * N + n;
-        if ((N & 3) == 0 && 4 * g + 3 < nrows) {
-            *reinterpret_cast<float4 *>(pr) = make_float4(res[0], res[1], res[2], res[3]);
+        if constexpr (KP > 1) {
+            // parts meet in stage 0: [part][row group][lane] f32x4, one
+            // block of each wave at a time
+            __syncthreads();
+            f32x4_t *red = (f32x4_t *)st0;
+            red[(kp * RB + rb) * 64 + lane] = res;
+            __syncthreads();
+            if (kp == 0) {
+#pragma unroll
+                for (int q = 1; q < KP; ++q) {
+                    const f32x4_t o = red[(q * RB + rb) * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        res[r] += o[r];
+                }
+            }
+        }
+        // Epilogue: lane holds channels 16 blk + 4 g + r of token column col.
+        const int t = col;
+        if (kp != 0 || t >= M || t >= MT || 4 * g >= nrows[f])
+            continue;
+        const int n = 16 * (blk0 + f) + 4 * g;
+        if (ks > 1) {
+            // this slice's sums (group scales in, per-channel scale not)
+            float *pr = P.partial + ((int64_t)slice * M + t) * N + n;
+            if ((N & 3) == 0 && 4 * g + 3 < nrows[f]) {
+                *reinterpret_cast<float4 *>(pr) = make_float4(res[0], res[1], res[2], res[3]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < nrows[f])
+                        pr[r] = res[r];
+            }
+            continue;
+        }
+        float post[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            post[r] = 4 * g + r >= nrows[f] ? 0.f
+                      : GM == 0             ? 0.5f * f16_bits_to_f32(P.scale[n + r])
+                                            : 0.5f;
+        uint16_t o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            o[r] = round_out<FP16>(res[r] * post[r]);
+        uint16_t *yr = P.y + (int64_t)t * N + n;
+        if ((N & 3) == 0 && 4 * g + 3 < nrows[f]) {
+            *reinterpret_cast<uint2 *>(yr) = make_uint2((uint32_t)o[0] | (uint32_t)o[1] << 16,
+                                                        (uint32_t)o[2] | (uint32_t)o[3] << 16);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * g + r < nrows)
-                    pr[r] = res[r];
+                if (4 * g + r < nrows[f])
+                    yr[r] = o[r];
         }
-        return;
-    }
-    float post[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        post[r] = 4 * g + r >= nrows ? 0.f
-                  : GM == 0          ? 0.5f * f16_bits_to_f32(P.scale[n + r])
-                                     : 0.5f;
-    uint16_t o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        o[r] = round_out<FP16>(res[r] * post[r]);
-    uint16_t *yr = P.y + (int64_t)t * N + n;
-    if ((N & 3) == 0 && 4 * g + 3 < nrows) {
-        *reinterpret_cast<uint2 *>(yr) =
-            make_uint2((uint32_t)o[0] | (uint32_t)o[1] << 16, (uint32_t)o[2] | (uint32_t)o[3] << 16);
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * g + r < nrows)
-                yr[r] = o[r];
     }
 }
 
@@ -448,7 +482,7 @@ __global__ void __launch_bounds__(kReduceThreads) few_reduce(const FewReduceBatc
 template <bool FP16, int GM, int MT, int KP>
 hipError_t launch_inst(unsigned grid, hipStream_t stream, const FewBatch &b)
 {
-    hipLaunchKernelGGL((few_kernel<FP16, GM, MT, KP>), dim3(grid), dim3(kThreads), 0, stream, b);
+    hipLaunchKernelGGL((few_kernel<FP16, GM, MT, KP, kFN>), dim3(grid), dim3(kThreads), 0, stream, b);
     return hipGetLastError();
 }
 
@@ -524,10 +558,10 @@ hipError_t plan_few(const GemvArgs *args, const int *order, int count, FewPlan &
     }
     const int cus = device_cus();
     int kp = 1;
-    while (kp < 4 && 2 * kp * pl.mt <= 32 && (blocks * kp + kWaves - 1) / kWaves < cus)
+    while (kp < 4 && 2 * kp * pl.mt <= 32 && (blocks * kp + kWaves * kFN - 1) / (kWaves * kFN) < cus)
         kp *= 2;
     pl.kp = kp;
-    const int rb = kWaves / kp;
+    const int rb = kWaves / kp * kFN;  // blocks per workgroup
     auto units = [&]() {
         int64_t u = 0;
         for (int oi = 0; oi < count; ++oi)
@@ -593,7 +627,7 @@ hipError_t launch_gemm_few(const GemvArgs *args, const int *order, int count, bo
     FewBatch b = {};
     FewReduceBatch rb = {};
     int units = 0, runits = 0;
-    const int rbk = kWaves / pl.kp;
+    const int rbk = kWaves / pl.kp * kFN;  // blocks per workgroup
     for (int oi = 0; oi < count; ++oi) {
         const GemvArgs &a = args[order[oi]];
         FewProblem &p = b.p[b.count];
