@@ -660,6 +660,59 @@ def bench_pack(tl):
             "unpack_GBps": round(nbytes / tu / 1e9, 1), "roundtrip_exact": ok}
 
 
+def measure_zero_skip(tl, launches=16, reps=3):
+    """The zero-skipping pipelined GEMM (path gemm_zskip) against the plain one
+    on the 7B gate projection (18944 x 4096) at 2048 tokens, tiled codes: i.i.d.
+    codes (the prefill layer's distribution) and the same codes with about half
+    of their 64 x 256 or 256 x 256 blocks zeroed.  Mean us per launch of each path, from a
+    graph of `launches` launches replayed `reps` times after settle()."""
+    import numpy as np
+    import torch
+    import synth
+    N, K, M = 18944, 4096, 2048
+    rng = np.random.default_rng(2024)
+    codes = synth.draw_codes(rng, N, K, 0.3, 0.3)
+    inputs = [("iid", codes)]
+    out = {"shape": f"{N}x{K}, M={M}, per-channel, tiled codes"}
+    for bn in (64, 256):  # half of the bn x 256 blocks zero (256: the tile height)
+        zero = rng.random((N // bn, K // 256)) < 0.5
+        sparse = codes.copy()
+        sparse[np.repeat(np.repeat(zero, bn, axis=0), 256, axis=1)] = 0
+        inputs.append((f"zero_blocks_{bn}x256", sparse))
+        out[f"zero_fraction_{bn}x256"] = round(float(zero.mean()), 4)
+    scale = to_dev(synth.draw_scales(rng, N, K, -1), torch.float16)
+    x = to_dev(synth.draw_x(rng, M, K), torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    side = capture_stream()
+    for name, c in inputs:
+        t = tl.tile(tl.pack(to_dev(c)))
+        res = {}
+        for path in ("gemm", "gemm_zskip"):
+            def call():
+                tl.linear(x, t, scale, -1, out=y, path=path, layout="tiled")
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(launches):
+                    call()
+            settle(g.replay)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[path + "_us"] = round(e0.elapsed_time(e1) * 1e3 / (launches * reps), 2)
+            del g
+        out[name] = res
+        del t
+    torch.cuda.empty_cache()
+    return out
+
+
 def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
     """Every (config, shape, M) of the five workloads that the headline lines do
     not already time (codes in the tiled layout): per-launch time on the automatic path, as GB/s and
@@ -986,7 +1039,7 @@ def main():
                     help="untimed graph replays before each graph-timed figure (clocks settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4)")
+                    help="skip the per-config sweep (configs 0, 1, 2 at M=8, 4) and the zero-skip timing")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the row-major-codes figures reported beside the tiled ones "
                          "(profiled runs: only tiled launches then)")
@@ -1160,6 +1213,8 @@ def main():
     prefill["roofline"]["frac_of_mfma_loop"] = round(
         ach_p / ceilings["mfma_loop"]["TFLOPs_sustained"], 4)
     configs, crossover = (None, None) if args.no_sweep else sweep_configs(tl)
+    zero_skip = None if args.no_sweep else measure_zero_skip(tl)
+    log(f"[bench] zero skip {zero_skip}")
 
     cpu = None
     if not args.no_cpu:
@@ -1205,6 +1260,7 @@ def main():
         "prefill": prefill,
         "configs": configs,
         "crossover": crossover,
+        "zero_skip": zero_skip,
         "pack": pack,
         "ceilings": ceilings,
         "cpu_baseline": cpu,

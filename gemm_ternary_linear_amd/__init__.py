@@ -34,7 +34,7 @@ LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
 
 BF16, FP16 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3, "gemv_f4": 4, "gemv_b16": 5,
-         "gemv_valu": 6, "few": 7}
+         "gemv_valu": 6, "few": 7, "gemm_zskip": 8}
 LAYOUTS = {"rows": 0, "tiled": 1}
 
 # Every symbol include/ternary.h declares.

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -159,6 +159,11 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
         if (!(M == 0 || N == 0 || ternary::gemm_few_takes(M, N, K, group, scale)))
             return TERNARY_ERR_PATH;
         break;
+    case TERNARY_PATH_GEMM_ZSKIP:
+        if (!(M == 0 || N == 0 ||
+              ternary::gemm_big_takes((int)M, (int)N, (int)K, group, scale, tiled)))
+            return TERNARY_ERR_PATH;
+        break;
     default: return TERNARY_ERR_PATH;
     }
     if (M == 0 || N == 0)
@@ -188,6 +193,10 @@ int linear_one(const void *x, int dtype, int64_t M, int64_t N, int64_t K, const 
         e = ternary::launch_gemm_few(&a, &order, 1, fp16, stream);
         break;
     }
+    case TERNARY_PATH_GEMM_ZSKIP:
+        e = ternary::launch_gemm(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv, stream,
+                                 tiled, true);
+        break;
     default:
         e = ternary::launch_simple(xv, fp16, (int)M, (int)N, (int)K, packed, scale, group, yv,
                                    stream, tiled);

@@ -302,8 +302,13 @@ struct BigBatch {
 };
 
 // GS: 0 for per-channel scales, else the group size (64, 128 or 256 K: one,
-// two or four K steps).
-template <bool FP16, int GS, class C>
+// two or four K steps).  ZS: skip zero blocks ([trdm] trdm.cn
+// "三元量化模型接入vLLM：从逆向加载到Kernel优化的完整实战" §6: ternary weights often
+// come with block sparsity, and a kernel can skip all-zero blocks): a wave
+// whose channels (16 FN) x 64 K of a step are all code 00 or 11 skips the
+// step's decode and MFMAs (their products are zeros; the sums are the same
+// bits).
+template <bool FP16, int GS, class C, bool ZS = false>
 __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigBatch batch)
 {
     constexpr int NS = C::NS, FN = C::FN, FM = C::FM, THREADS = C::THREADS;
@@ -474,8 +479,24 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
         for (int f = 0; f < FN; ++f)
             wv[f] = lw[s][wa + f * 64];
+        bool skip = false;
+        if constexpr (ZS) {
+            // one decision per wave and step: codes 00 and 11 both decode to zero
+            uint32_t nz = 0;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+            for (int f = 0; f < FN; ++f)
+                nz |= (wv[f] ^ (wv[f] >> 1)) & 0x55555555u;
+            skip = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
+            if constexpr (GROUPED)
+                if (skip && s % SPG == 0)
+#pragma unroll
+                    for (int f = 0; f < FN; ++f)
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            part[f][j] = zero4;
+        }
+#pragma unroll
+        for (int kk = 0; kk < (skip ? 0 : 2); ++kk) {
             uint4 xf[FM];
 #pragma unroll
             for (int j = 0; j < FM; ++j)
@@ -775,7 +796,7 @@ size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order
 // per problem whose K range is split.  The fp32 partials of split problems go
 // to `fixed` when given (the caller checked its size), else to the stream's
 // workspace.
-template <bool FP16, int GS, class C>
+template <bool FP16, int GS, class C, bool ZS>
 hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipStream_t stream,
                            const FixedScratch *fixed)
 {
@@ -820,7 +841,7 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
         b.wg0[r] = wg;
         wg += tiles[i] * ks[i];
     }
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, GS, C>), dim3(wg), dim3(C::THREADS), 0,
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<FP16, GS, C, ZS>), dim3(wg), dim3(C::THREADS), 0,
                        stream, b);
     hipError_t e = hipGetLastError();
     for (int r = 0; r < count && e == hipSuccess; ++r) {
@@ -837,20 +858,20 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
     return e;
 }
 
-template <bool FP16, int GS>
+template <bool FP16, int GS, bool ZS>
 hipError_t launch_big_group(const GemvArgs *args, const int (*idx)[kGemvMaxBatch], const int *n,
                             hipStream_t stream, const FixedScratch *fixed)
 {
     hipError_t e = hipSuccess;
     if (n[0] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, TinyCfg>(args, idx[0], n[0], stream, fixed);
+        e = launch_big_mode<FP16, GS, TinyCfg, ZS>(args, idx[0], n[0], stream, fixed);
     if (n[1] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, SmallCfg>(args, idx[1], n[1], stream, fixed);
+        e = launch_big_mode<FP16, GS, SmallCfg, ZS>(args, idx[1], n[1], stream, fixed);
     if (n[2] && e == hipSuccess)
-        e = launch_big_mode<FP16, GS, MidCfg>(args, idx[2], n[2], stream, fixed);
+        e = launch_big_mode<FP16, GS, MidCfg, ZS>(args, idx[2], n[2], stream, fixed);
     if constexpr (GS == 0)  // group-scaled problems never take the large configuration
         if (n[3] && e == hipSuccess)
-            e = launch_big_mode<FP16, GS, BigCfg>(args, idx[3], n[3], stream, fixed);
+            e = launch_big_mode<FP16, GS, BigCfg, ZS>(args, idx[3], n[3], stream, fixed);
     return e;
 }
 
@@ -870,18 +891,18 @@ struct BigClasses {
     }
 };
 
-template <bool FP16>
+template <bool FP16, bool ZS>
 hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t stream,
                                  const FixedScratch *fixed)
 {
     const BigClasses cl(args, count);
-    hipError_t e = launch_big_group<FP16, 0>(args, cl.idx[0], cl.n[0], stream, fixed);
+    hipError_t e = launch_big_group<FP16, 0, ZS>(args, cl.idx[0], cl.n[0], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 64>(args, cl.idx[1], cl.n[1], stream, fixed);
+        e = launch_big_group<FP16, 64, ZS>(args, cl.idx[1], cl.n[1], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 128>(args, cl.idx[2], cl.n[2], stream, fixed);
+        e = launch_big_group<FP16, 128, ZS>(args, cl.idx[2], cl.n[2], stream, fixed);
     if (e == hipSuccess)
-        e = launch_big_group<FP16, 256>(args, cl.idx[3], cl.n[3], stream, fixed);
+        e = launch_big_group<FP16, 256, ZS>(args, cl.idx[3], cl.n[3], stream, fixed);
     return e;
 }
 
@@ -907,21 +928,24 @@ size_t gemm_batch_scratch_need(const GemvArgs *args, int count)
 }
 
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
-                             const FixedScratch *fixed)
+                             const FixedScratch *fixed, bool zero_skip)
 {
-    return fp16 ? launch_gemm_big_batch<true>(args, count, stream, fixed)
-                : launch_gemm_big_batch<false>(args, count, stream, fixed);
+    if (zero_skip)
+        return fp16 ? launch_gemm_big_batch<true, true>(args, count, stream, fixed)
+                    : launch_gemm_big_batch<false, true>(args, count, stream, fixed);
+    return fp16 ? launch_gemm_big_batch<true, false>(args, count, stream, fixed)
+                : launch_gemm_big_batch<false, false>(args, count, stream, fixed);
 }
 
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
-                       bool tiled)
+                       bool tiled, bool zero_skip)
 {
     if (gemm_big_takes(M, N, K, group, scale, tiled)) {
         const GemvArgs a = {x, packed, scale, y, M, N, K, group, tiled ? 1 : 0};
-        return launch_gemm_batch(&a, 1, fp16, stream);
+        return launch_gemm_batch(&a, 1, fp16, stream, nullptr, zero_skip);
     }
-    if (tiled)  // the 128 x 128 kernel reads row-major codes only
+    if (tiled || zero_skip)  // the 128 x 128 kernel: row-major codes, no zero skipping
         return hipErrorInvalidValue;
     const int glog = group ? group_log2(group) : 0;
     if (fp16)

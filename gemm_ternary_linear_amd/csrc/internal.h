@@ -114,10 +114,11 @@ hipError_t launch_gemm_few(const GemvArgs *args, const int *order, int count, bo
 size_t gemm_few_scratch_need(const GemvArgs *args, const int *order, int count);
 // Compute units of the current device (cached per device).
 int device_cus();
-// Tiled codes need the pipelined kernel (gemm_big_takes with tiled).
+// Tiled codes need the pipelined kernel (gemm_big_takes with tiled), and so
+// does zero_skip (the pipelined kernel skipping a wave's all-zero steps).
 hipError_t launch_gemm(const uint16_t *x, bool fp16, int M, int N, int K, const uint8_t *packed,
                        const uint16_t *scale, int group, uint16_t *y, hipStream_t stream,
-                       bool tiled = false);
+                       bool tiled = false, bool zero_skip = false);
 // Whether the pipelined (grouped) prefill kernel takes a problem (it reads
 // row-major and tiled codes; the 128 x 128 kernel only row-major ones).
 bool gemm_big_takes(int M, int N, int K, int group, const void *scale, bool tiled = false);
@@ -132,7 +133,7 @@ struct FixedScratch {
 // split).  Split-K partials go to `fixed` if given (it must hold
 // gemm_batch_scratch_need() bytes), else to the stream's workspace.
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
-                             const FixedScratch *fixed = nullptr);
+                             const FixedScratch *fixed = nullptr, bool zero_skip = false);
 // Scratch bytes launch_gemm_batch needs for these problems (0: no K split).
 size_t gemm_batch_scratch_need(const GemvArgs *args, int count);
 

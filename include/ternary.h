@@ -112,10 +112,16 @@ typedef enum {
                                   channel or groups of 64/128/256, row-major codes
                                   only.  Never chosen by AUTO (measured slower); kept
                                   for comparison                                        */
-    TERNARY_PATH_FEW = 7       /* few-token streaming GEMM: 1 <= M <= 16, K % 256 == 0,
+    TERNARY_PATH_FEW = 7,      /* few-token streaming GEMM: 1 <= M <= 16, K % 256 == 0,
                                   K <= 65536, per channel or groups of 128 / 256; x
                                   shared in LDS by the eight 16-channel blocks of a
                                   workgroup, codes streamed into registers             */
+    TERNARY_PATH_GEMM_ZSKIP = 8 /* the pipelined GEMM skipping all-zero code blocks
+                                  ([trdm §6]; a wave's channels x 64 K): the shapes
+                                  TERNARY_PATH_GEMM takes on the pipelined kernel
+                                  (K % 256 == 0, ...); the same bits as that path.
+                                  Pays only on block-sparse codes; never chosen by
+                                  AUTO                                                 */
 } ternary_path;
 
 /*

@@ -63,7 +63,7 @@ def test_no_oracle_linkage(tl):
 
 
 def test_versions_and_strings(tl):
-    assert tl.abi_version() == 6
+    assert tl.abi_version() == 7
     assert tl.gemv_max_m() == 8
     for st in range(0, -11, -1):
         s = tl.status_string(st)
@@ -115,7 +115,11 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(M=2, K=256, g=-1, path=6), -8),     # M == 1 only
     (dict(K=256, g=32, path=6), -8),          # groups of 64, 128, 256 only
     (dict(path=7), -8),                       # few-token GEMM: K % 256 == 0
-    (dict(path=8), -8),
+    (dict(path=8), -8),                       # zero-skipping GEMM: K % 256 == 0
+    (dict(path=9), -8),
+    (dict(M=64, K=384, g=128, path=8), -8),
+    (dict(M=64, K=512, g=32, path=8), -8),    # the pipelined kernel's group sizes only
+    (dict(M=64, K=512, g=128, s=FAKE * 3 + 2, path=8), -8),
     (dict(M=17, K=256, g=-1, path=7), -8),    # M <= 16
     (dict(K=256, g=64, path=7), -8),          # per channel, groups of 128 or 256
     (dict(K=256, g=32, path=7), -8),
