@@ -808,6 +808,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
 WORKLOADS = {
     "27b_m16": (4, 16, False), "27b_m64": (4, 64, False), "27b_m256": (4, 256, False),
     "7b_decode_single_m1": (2, 1, False), "7b_decode_fused_m8": (2, 8, True),
+    "7b_fused_m16": (2, 16, True),
 }
 WORKLOAD_REPS = 6
 
@@ -868,11 +869,11 @@ def summarize_workload(name: str, dirs) -> None:
             short = kname.replace("(anonymous namespace)::", "").replace("ternary::", "")
             short = re.sub(r"^void ", "", short)
             short = re.sub(r"\(.*$", "", short)
-            if not re.search(r"gemv|gemm|simple", short):
+            if not re.search(r"gemv|gemm|simple|few", short):
                 continue  # the layer's pack / tile kernels
             # launches run projection by projection, WORKLOAD_REPS + 1 each; a
-            # split-K reduce belongs to the GEMM before it
-            if "split_reduce" in short:
+            # split-K or K-slice reduce belongs to the launch before it
+            if "split_reduce" in short or "few_reduce" in short:
                 idx = max(n_main - 1, 0) // (WORKLOAD_REPS + 1)
             else:
                 idx = n_main // (WORKLOAD_REPS + 1)
@@ -913,7 +914,7 @@ def summarize_workload(name: str, dirs) -> None:
             f_k, w_k = mean(v["FETCH_SIZE"]), mean(v["WRITE_SIZE"])
             t = f_k * 1024 * k_fetch + w_k * 1024 * k_write
             row.append(f"fetch_kib {f_k:.1f} write_kib {w_k:.1f} traffic_bytes {t:.0f}")
-            if label in by_name and "split_reduce" not in short:
+            if label in by_name and "reduce" not in short:
                 a = alg_bytes(by_name[label].N, by_name[label].K, M, g)
                 row.append(f"alg_bytes {a} traffic/alg {t / a:.3f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "GRBM_GUI_ACTIVE" in v:
@@ -923,7 +924,8 @@ def summarize_workload(name: str, dirs) -> None:
                 pb = mean(mprobe["SQ_VALU_MFMA_BUSY_CYCLES"]) / mean(mprobe["GRBM_GUI_ACTIVE"])
                 row.append(f"mfma_busy_vs_probe {busy / pb:.3f}")
         lines.append("  ".join(row))
-    fam = "gemm_dma" if cfg == 4 else ("gemv_f4" if M == 1 else "gemv_stream")
+    fam = ("gemv_f4" if M == 1 else "gemv_stream" if M <= 8 else "gemm_few" if M <= 16
+           else "gemm_dma")
     path = ROOT / "profiles" / f"{fam}_{name}_counters.txt"
     path.parent.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")

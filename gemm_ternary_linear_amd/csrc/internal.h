@@ -59,8 +59,9 @@ hipError_t launch_quantize(const uint16_t *w, bool fp16, int N, int K, int group
 // All linear launchers: x/y are 2-byte elements (bf16 or fp16 by `fp16`),
 // `group` as in GemvArgs, shapes already validated by the caller.
 // Which decode kernel runs a GEMV problem: AUTO takes the fp4 x fp8 one for
-// M == 1 and the 16-bit one for larger M, each where it takes the shape, else
-// the other; F4 and B16 force one (parity tests, tuning).
+// M == 1 (the 16-bit one for a launch's lone one-token problem of fewer than
+// 8192 channels) and the 16-bit one for larger M, each where it takes the
+// shape, else the other; F4 and B16 force one (parity tests, tuning).
 // Both read row-major and tiled codes.
 enum class GemvKernel { AUTO, F4, B16 };
 bool gemv_kernel_takes(GemvKernel k, int64_t M, int64_t K, int group, bool fp16,

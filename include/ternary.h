@@ -97,9 +97,10 @@ typedef enum { TERNARY_BF16 = 0, TERNARY_FP16 = 1 } ternary_dtype;
 typedef enum {
     TERNARY_PATH_AUTO = 0,
     TERNARY_PATH_GEMV = 1,     /* decode GEMV, requires 1 <= M <= ternary_gemv_max_m();
-                                  at M == 1 the fp4 x fp8 kernel, at larger M the
-                                  16-bit one, each where it takes the shape, else
-                                  the other                                            */
+                                  at M == 1 the fp4 x fp8 kernel (a single call of
+                                  fewer than 8192 channels: the 16-bit one), at
+                                  larger M the 16-bit one, each where it takes the
+                                  shape, else the other                                */
     TERNARY_PATH_GEMM = 2,     /* prefill kernel (bf16/fp16 MFMA)                       */
     TERNARY_PATH_SIMPLE = 3,   /* plain one-output-per-thread kernel, any valid shape   */
     TERNARY_PATH_GEMV_F4 = 4,  /* decode GEMV on the scaled fp4 x fp8 matrix
@@ -207,8 +208,8 @@ int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t gro
  * output dtype, round-to-nearest-even.  x and s must be finite (results for
  * non-finite inputs are unspecified) and |x| < 2^126.
  * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (the fp4 x fp8
- * kernel at M == 1, the 16-bit one at larger M, each where it takes the
- * shape); 9 <= M <= 16 the few-token GEMM (TERNARY_PATH_FEW) where it takes
+ * kernel at M == 1 except for N < 8192, the 16-bit one otherwise, each where
+ * it takes the shape); 9 <= M <= 16 the few-token GEMM (TERNARY_PATH_FEW) where it takes
  * the shape; larger M and the rest the MFMA GEMM; shapes no fast kernel
  * takes (K % 128 != 0) run the plain kernel.  The GEMV gives each token 2
  * MFMA columns (per channel, groups of 128 or 256), 4 (groups of 64) or 8

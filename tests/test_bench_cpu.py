@@ -204,8 +204,8 @@ def test_summarize_workload_labels_projections(tmp_path, monkeypatch):
                 w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Grid_Size": g,
                             "Counter_Name": counter, "Counter_Value": v})
                 i += 1
-    bench.summarize_workload("27b_m16", [tmp_path / "FETCH_SIZE", tmp_path / "WRITE_SIZE"])
-    text = (tmp_path / "profiles" / "gemm_dma_27b_m16_counters.txt").read_text()
+    bench.summarize_workload("27b_m64", [tmp_path / "FETCH_SIZE", tmp_path / "WRITE_SIZE"])
+    text = (tmp_path / "profiles" / "gemm_dma_27b_m64_counters.txt").read_text()
     lines = [ln for ln in text.splitlines() if ln.startswith("[")]
     assert len(lines) == 4, lines
     assert lines[0].startswith("[up] dma::gemm_dma_kernel") and f"n={n}" in lines[0]
@@ -215,3 +215,33 @@ def test_summarize_workload_labels_projections(tmp_path, monkeypatch):
     assert "tile_kernel" not in text
     # 1000 KiB fetched (scale 2) + 2000 KiB written (scale 1) per dispatch
     assert f"traffic_bytes {4000 * 1024}" in lines[0]
+
+
+def test_summarize_workload_few_token_fused(tmp_path, monkeypatch):
+    # the 16-token fused step: few-token GEMM launches and their K-slice
+    # reduce, named after the kernel family that runs it
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    cols = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    n = bench.WORKLOAD_REPS + 1
+    few = "void ternary::(anonymous namespace)::few_kernel<false, 0, 16, 1, 1>(ternary::(anonymous namespace)::FewBatch)"
+    red = "void ternary::(anonymous namespace)::few_reduce<false, true>(ternary::(anonymous namespace)::FewReduceBatch)"
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=cols)
+            w.writeheader()
+            rows = [("at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>", 7,
+                     (bench.COPY_PROBE_BYTES / 1024) / (2 if counter == "FETCH_SIZE" else 1))]
+            for _ in range(n):
+                rows += [(few, 270336, 100.0), (red, 16384, 5.0)]
+            for i, (k, g, v) in enumerate(rows, 1):
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Grid_Size": g,
+                            "Counter_Name": counter, "Counter_Value": v})
+    bench.summarize_workload("7b_fused_m16", [tmp_path / "FETCH_SIZE", tmp_path / "WRITE_SIZE"])
+    text = (tmp_path / "profiles" / "gemm_few_7b_fused_m16_counters.txt").read_text()
+    lines = [ln for ln in text.splitlines() if ln.startswith("[")]
+    assert len(lines) == 2, lines
+    assert lines[0].startswith("[fused step] few_kernel") and f"n={n}" in lines[0]
+    assert lines[1].startswith("[fused step] few_reduce")
+    assert "alg_bytes_per_step" in text
