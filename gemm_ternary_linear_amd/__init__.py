@@ -26,11 +26,14 @@ import torch
 __all__ = [
     "TernaryError", "lib", "pack", "unpack", "linear", "linear_batch", "select_path", "gemv_max_m",
     "PATHS", "BF16", "FP16", "abi_version", "shutdown", "LIB_PATH", "probe_read", "probe_copy",
-    "probe_mfma", "probe_mfma_flops", "quantize", "linear_batch_noalloc", "tile", "untile",
+    "probe_mfma", "probe_mfma_flops", "probe_lib", "PROBE_LIB_PATH", "quantize",
+    "linear_batch_noalloc", "tile", "untile",
     "tiled_bytes", "LAYOUTS",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libternary.so"
+# Measurement probes (include/ternary_probe.h) live in a library of their own.
+PROBE_LIB_PATH = Path(__file__).resolve().parent / "libternary_probe.so"
 
 BF16, FP16 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "simple": 3, "gemv_f4": 4, "gemv_b16": 5,
@@ -91,18 +94,37 @@ def lib() -> ctypes.CDLL:
     L.ternary_linear_batch_noalloc.argtypes = [p, i32, i32, p]
     L.ternary_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p]
     L.ternary_select_path.argtypes = [i64, i64, i64, i64]
-    L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
-    L.ternary_probe_copy.argtypes = [p, p, i64, i32, p]
-    L.ternary_probe_mfma.argtypes = [i32, i32, p, p]
     L.ternary_status_string.argtypes = [i32]
     L.ternary_status_string.restype = ctypes.c_char_p
     for nm in ("ternary_pack", "ternary_unpack", "ternary_linear", "ternary_linear_ex",
                "ternary_linear_batch", "ternary_select_path", "ternary_gemv_max_m",
                "ternary_abi_version", "ternary_shutdown", "ternary_quantize",
                "ternary_linear_batch_noalloc", "ternary_linear_tiled", "ternary_tile",
-               "ternary_untile", *PROBE_EXPORTS):
+               "ternary_untile"):
         getattr(L, nm).restype = i32
     _lib = L
+    return L
+
+
+_probe_lib = None
+
+
+def probe_lib() -> ctypes.CDLL:
+    """The measurement-probe library (bench and its tests only); raises if it
+    has not been built."""
+    global _probe_lib
+    if _probe_lib is not None:
+        return _probe_lib
+    if not PROBE_LIB_PATH.exists():
+        raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build the HIP libraries first")
+    L = ctypes.CDLL(str(PROBE_LIB_PATH))
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
+    L.ternary_probe_copy.argtypes = [p, p, i64, i32, p]
+    L.ternary_probe_mfma.argtypes = [i32, i32, p, p]
+    for nm in PROBE_EXPORTS:
+        getattr(L, nm).restype = i32
+    _probe_lib = L
     return L
 
 
@@ -362,8 +384,9 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int) -> None:
     _dev(buf, "buf")
     _dev(sink, "sink")
     nbytes = buf.numel() * buf.element_size()
-    _check(int(lib().ternary_probe_read(buf.data_ptr(), nbytes, workgroups, sink.data_ptr(),
-                                        _stream(buf))), "ternary_probe_read")
+    _check(int(probe_lib().ternary_probe_read(buf.data_ptr(), nbytes, workgroups,
+                                              sink.data_ptr(), _stream(buf))),
+           "ternary_probe_read")
 
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> None:
@@ -373,8 +396,9 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> None:
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("src and dst must hold the same number of bytes")
-    _check(int(lib().ternary_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, workgroups,
-                                        _stream(src))), "ternary_probe_copy")
+    _check(int(probe_lib().ternary_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                              workgroups, _stream(src))),
+           "ternary_probe_copy")
 
 
 def probe_mfma(workgroups: int, iters: int, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -386,7 +410,7 @@ def probe_mfma(workgroups: int, iters: int, out: torch.Tensor | None = None) -> 
     elif out.dtype != torch.float32 or out.numel() < n:
         raise ValueError(f"out must be float32 with at least {n} elements")
     _dev(out, "out")
-    _check(int(lib().ternary_probe_mfma(workgroups, iters, out.data_ptr(), _stream(out))),
+    _check(int(probe_lib().ternary_probe_mfma(workgroups, iters, out.data_ptr(), _stream(out))),
            "ternary_probe_mfma")
     return out
 

@@ -1,4 +1,6 @@
-"""Build the gfx950 HIP library libternary.so in-tree (hipcc, no GPU needed)."""
+"""Build the gfx950 HIP libraries in-tree (hipcc, no GPU needed): libternary.so
+(the layer) and libternary_probe.so (measurement probes, used by the bench and
+its tests only)."""
 
 from __future__ import annotations
 
@@ -12,6 +14,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libternary.so"
+PROBE_LIB = PKG / "libternary_probe.so"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -20,8 +23,9 @@ FLAGS = [
     # packed fp32 VALU forms stay off: all fp32 math is emitted as scalar ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_f4.hip", "gemv_stream.hip", "gemv_valu.hip", "gemm_few.hip",
-           "gemm.hip", "simple.hip", "noalloc.hip", "workspace.hip", "probe.hip", "quantize.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_f4.hip", "gemv_stream.hip", "gemv_valu.hip",
+           "gemm_few.hip", "gemm.hip", "simple.hip", "noalloc.hip", "workspace.hip", "quantize.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 
 def _compile(src: str) -> Path:
@@ -37,18 +41,24 @@ def _compile(src: str) -> Path:
     return obj
 
 
-def build(verbose: bool = False) -> Path:
-    BUILD.mkdir(exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4, 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
+def _link(objs, out: Path) -> None:
+    tmp = out.with_suffix(".so.tmp")
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4, 8)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB.name}")
     return LIB
 
 

@@ -1,6 +1,7 @@
 /*
- * Measurement probes of libternary.so: the device's achievable HBM stream and
- * bf16 MFMA rates, measured with kernels of known traffic and flop counts.
+ * Measurement probes (libternary_probe.so, a library apart from the layer's): the
+ * device's achievable HBM stream and bf16 MFMA rates, measured with kernels of
+ * known traffic and flop counts.
  *
  * They are not part of the layer.  A roofline fraction is the layer's rate
  * over a published peak; these kernels measure how much of that peak plain

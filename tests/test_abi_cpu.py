@@ -39,18 +39,22 @@ def test_header_declares_expected(tl):
 
 
 def test_library_exports_every_declared_symbol(tl):
-    L = tl.lib()
-    for name in declared_functions():
+    L, P = tl.lib(), tl.probe_lib()
+    for name in declared_functions((HEADER,)):
         assert hasattr(L, name), name
+    for name in declared_functions((PROBE_HEADER,)):
+        assert hasattr(P, name), name
+        assert not hasattr(L, name), f"{name} is a probe: not in the layer's library"
 
 
 def test_exported_symbols_in_dynamic_table(tl):
     import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", str(tl.LIB_PATH)],
-                         capture_output=True, text=True, check=True).stdout
-    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
-    for name in declared_functions():
-        assert name in names, name
+    for path, header in ((tl.LIB_PATH, HEADER), (tl.PROBE_LIB_PATH, PROBE_HEADER)):
+        out = subprocess.run(["nm", "-D", "--defined-only", str(path)],
+                             capture_output=True, text=True, check=True).stdout
+        names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+        for name in declared_functions((header,)):
+            assert name in names, (path.name, name)
 
 
 def test_no_oracle_linkage(tl):
@@ -240,7 +244,7 @@ def test_batch_rejects(tl):
 
 
 def test_probe_rejects(tl):
-    L = tl.lib()
+    L = tl.probe_lib()
     A, B = 1 << 20, 1 << 21   # 16-byte aligned, never dereferenced
     SHAPE, NULL, ALIGN, ALIAS = -2, -1, -5, -6
     assert L.ternary_probe_read(A, 17, 64, A, None) == SHAPE
