@@ -952,6 +952,8 @@ def measure_ceilings(tl, layer_bytes, steps):
     - read_layer_size: `steps` reads of `layer_bytes` each (the decode layer's
       algorithmic bytes), rotating over 1 GiB and replayed from one HIP graph,
       timed like the decode step;
+      both reads with plain and with non-temporal loads (the policy of the
+      decode kernels' code loads), the faster one reported, the plain one beside;
     - copy_512MiB: a 512 MiB -> 512 MiB copy (reads plus writes);
     - mfma_loop: four independent bf16 MFMA chains per wave on register
       operands, 1.1e12 flops per launch; cold (the first launches) and
@@ -971,32 +973,42 @@ def measure_ceilings(tl, layer_bytes, steps):
     out = {}
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     big = torch.ones(ROTATE_BYTES // 4, dtype=torch.int32, device="cuda:0")
-    best = (0.0, None)
-    for wg in (1024, 2048, 4096, 8192):
-        tl.probe_read(big, sink, wg)
-        t = ev_time(lambda r: tl.probe_read(big, sink, wg), 5)
-        best = max(best, (ROTATE_BYTES / t / 1e9, wg), key=lambda b: b[0])
-    out["read_1GiB"] = {"GBps": round(best[0], 1), "workgroups": best[1],
-                        "frac": round(best[0] / HBM_PEAK_GBPS, 4)}
+    best = {}
+    for nt in (False, True):
+        best[nt] = (0.0, None)
+        for wg in (1024, 2048, 4096, 8192):
+            tl.probe_read(big, sink, wg, nontemporal=nt)
+            t = ev_time(lambda r: tl.probe_read(big, sink, wg, nontemporal=nt), 5)
+            best[nt] = max(best[nt], (ROTATE_BYTES / t / 1e9, wg), key=lambda b: b[0])
+    nt = best[True][0] > best[False][0]
+    out["read_1GiB"] = {"GBps": round(best[nt][0], 1), "workgroups": best[nt][1],
+                        "loads": "non-temporal" if nt else "plain",
+                        "plain_GBps": round(best[False][0], 1),
+                        "frac": round(best[nt][0] / HBM_PEAK_GBPS, 4)}
 
     chunk = layer_bytes // 16 * 4               # int32 elements, 16-byte multiple
     nchunk = big.numel() // chunk
     views = [big[i * chunk:(i + 1) * chunk] for i in range(nchunk)]
-    best = (0.0, None)
-    for wg in (512, 1024, 2048):
-        tl.probe_read(views[0], sink, wg)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                tl.probe_read(views[i % nchunk], sink, wg)
-        settle(g.replay)
-        t = ev_time(lambda r: g.replay(), 1) / steps
-        del g
-        best = max(best, (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
-    out["read_layer_size"] = {"GBps": round(best[0], 1), "workgroups": best[1],
-                              "bytes": chunk * 4, "us": round(chunk * 4 / best[0] / 1e3, 3),
-                              "frac": round(best[0] / HBM_PEAK_GBPS, 4)}
+    best = {}
+    for nt in (False, True):
+        best[nt] = (0.0, None)
+        for wg in (512, 1024, 2048):
+            tl.probe_read(views[0], sink, wg, nontemporal=nt)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    tl.probe_read(views[i % nchunk], sink, wg, nontemporal=nt)
+            settle(g.replay)
+            t = ev_time(lambda r: g.replay(), 1) / steps
+            del g
+            best[nt] = max(best[nt], (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
+    nt = best[True][0] > best[False][0]
+    out["read_layer_size"] = {"GBps": round(best[nt][0], 1), "workgroups": best[nt][1],
+                              "loads": "non-temporal" if nt else "plain",
+                              "plain_GBps": round(best[False][0], 1),
+                              "bytes": chunk * 4, "us": round(chunk * 4 / best[nt][0] / 1e3, 3),
+                              "frac": round(best[nt][0] / HBM_PEAK_GBPS, 4)}
     del views
 
     half = big.numel() // 2

@@ -49,7 +49,8 @@ EXPORTS = (
     "ternary_linear_tiled",
 )
 # Every symbol include/ternary_probe.h declares (measurement probes).
-PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_copy", "ternary_probe_mfma")
+PROBE_EXPORTS = ("ternary_probe_read", "ternary_probe_read_nt", "ternary_probe_copy",
+                 "ternary_probe_mfma")
 MAX_BATCH = 8
 PROBE_THREADS = 256
 
@@ -120,6 +121,7 @@ def probe_lib() -> ctypes.CDLL:
     L = ctypes.CDLL(str(PROBE_LIB_PATH))
     i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     L.ternary_probe_read.argtypes = [p, i64, i32, p, p]
+    L.ternary_probe_read_nt.argtypes = [p, i64, i32, p, p]
     L.ternary_probe_copy.argtypes = [p, p, i64, i32, p]
     L.ternary_probe_mfma.argtypes = [i32, i32, p, p]
     for nm in PROBE_EXPORTS:
@@ -378,15 +380,17 @@ def linear_batch_noalloc(problems) -> list:
 
 # ---------------------------------------------------------------- probes
 
-def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int) -> None:
-    """Read all bytes of ``buf`` once (ternary_probe_read); ``sink`` is a
-    one-element int32 device tensor."""
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int,
+               nontemporal: bool = False) -> None:
+    """Read all bytes of ``buf`` once (ternary_probe_read, or
+    ternary_probe_read_nt with non-temporal loads); ``sink`` is a one-element
+    int32 device tensor."""
     _dev(buf, "buf")
     _dev(sink, "sink")
     nbytes = buf.numel() * buf.element_size()
-    _check(int(probe_lib().ternary_probe_read(buf.data_ptr(), nbytes, workgroups,
-                                              sink.data_ptr(), _stream(buf))),
-           "ternary_probe_read")
+    name = "ternary_probe_read_nt" if nontemporal else "ternary_probe_read"
+    _check(int(getattr(probe_lib(), name)(buf.data_ptr(), nbytes, workgroups, sink.data_ptr(),
+                                          _stream(buf))), name)
 
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> None:

@@ -11,6 +11,42 @@
 
 namespace ternary {
 
+// Cache policy of the code loads of the decode and few-token kernels, a
+// template parameter of each kernel (the immediate of the buffer load):
+// kStreamLoad, non-temporal (the `nt` bit of gfx950 buffer loads), for
+// launches whose problems all hold tiled codes, where every code byte is read
+// once: the code stream then passes through the caches without displacing
+// lines that are reused (x, scales).  On MI355X it took the fused 7B-shaped
+// decode layer at one token from 14.2 to 12.9 us.  Row-major codes keep the
+// default policy (0): consecutive slabs read the two halves of a row's
+// 128-byte line, and a non-temporal first half loses the line before the
+// second (the same layer slowed by 7 %).  Group scales keep it too (one line
+// of a row's scales serves many slabs), and so does the prefill GEMM, which
+// reads each weight tile once per token tile.  The policy is chosen per launch
+// on the host rather than by a branch in the kernel: a branch between two
+// load variants made the compiler's wait counts coarser (full drains instead
+// of per-load waits) and cost more than the policy gained.
+constexpr int kStreamLoad = 2;
+
+template <int CP>
+__device__ __forceinline__ auto load_codes(__amdgpu_buffer_rsrc_t rsrc, int off)
+{
+    static_assert(CP == 0 || CP == kStreamLoad, "code-load policy");
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, CP);
+}
+
+// N such loads, w[j] from byte offset off(j), issued in order (a scheduling
+// fence after each).
+template <int CP, int N, class V, class Off>
+__device__ __forceinline__ void load_code_run(V (&w)[N], __amdgpu_buffer_rsrc_t rsrc, Off off)
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        w[j] = load_codes<CP>(rsrc, off(j));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;

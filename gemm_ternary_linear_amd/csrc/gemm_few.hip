@@ -123,8 +123,9 @@ __device__ __forceinline__ void wait_vm()
 // GM: 0 per-channel scales, 1 groups of 256, 2 groups of 128.  MT: tokens of
 // the tile (8 or 16).  KP: K parts (the workgroup's waves are RB = 8 / KP row
 // groups x KP parts).  FN: 16-channel blocks per wave (each B read of x feeds
-// FN MFMAs), so a workgroup holds RB * FN blocks.
-template <bool FP16, int GM, int MT, int KP, int FN>
+// FN MFMAs), so a workgroup holds RB * FN blocks.  CP: the cache policy of the
+// code loads (kStreamLoad when every problem holds tiled codes).
+template <bool FP16, int GM, int MT, int KP, int FN, int CP>
 __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
 {
     constexpr int RB = kWaves / KP;
@@ -251,8 +252,7 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         const bool live = in && sl < nslabs;
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-            w[s][f] = __builtin_amdgcn_raw_buffer_load_b128(wr[f], live ? woff[f] + sl * sstride : kOOB,
-                                                            0, 0);
+            w[s][f] = load_codes<CP>(wr[f], live ? woff[f] + sl * sstride : kOOB);
         if constexpr (GM != 0) {
             // Offsets clamped into the block instead of selected, so that no
             // lane condition splits a load: rows past N and slabs past the
@@ -479,37 +479,50 @@ __global__ void __launch_bounds__(kReduceThreads) few_reduce(const FewReduceBatc
             yr[r] = round_out<FP16>(sum[r] * (PC ? 0.5f * f16_bits_to_f32(R.scale[n + r]) : 0.5f));
 }
 
-template <bool FP16, int GM, int MT, int KP>
+template <bool FP16, int GM, int MT, int KP, int CP>
 hipError_t launch_inst(unsigned grid, hipStream_t stream, const FewBatch &b)
 {
-    hipLaunchKernelGGL((few_kernel<FP16, GM, MT, KP, kFN>), dim3(grid), dim3(kThreads), 0, stream, b);
+    hipLaunchKernelGGL((few_kernel<FP16, GM, MT, KP, kFN, CP>), dim3(grid), dim3(kThreads), 0,
+                       stream, b);
     return hipGetLastError();
 }
 
-template <bool FP16, int GM, int MT>
+template <bool FP16, int GM, int MT, int CP>
 hipError_t launch_kp(int kp, unsigned grid, hipStream_t stream, const FewBatch &b)
 {
     if (kp == 1)
-        return launch_inst<FP16, GM, MT, 1>(grid, stream, b);
+        return launch_inst<FP16, GM, MT, 1, CP>(grid, stream, b);
     if (kp == 2)
-        return launch_inst<FP16, GM, MT, 2>(grid, stream, b);
+        return launch_inst<FP16, GM, MT, 2, CP>(grid, stream, b);
     if constexpr (MT * 4 <= 32)
-        return launch_inst<FP16, GM, MT, 4>(grid, stream, b);
+        return launch_inst<FP16, GM, MT, 4, CP>(grid, stream, b);
     return hipErrorInvalidValue;
 }
 
-template <bool FP16>
+template <bool FP16, int CP>
 hipError_t launch_mode(int gm, int mt, int kp, unsigned grid, hipStream_t stream,
                        const FewBatch &b)
 {
     switch (gm * 2 + (mt == 16 ? 1 : 0)) {
-    case 0: return launch_kp<FP16, 0, 8>(kp, grid, stream, b);
-    case 1: return launch_kp<FP16, 0, 16>(kp, grid, stream, b);
-    case 2: return launch_kp<FP16, 1, 8>(kp, grid, stream, b);
-    case 3: return launch_kp<FP16, 1, 16>(kp, grid, stream, b);
-    case 4: return launch_kp<FP16, 2, 8>(kp, grid, stream, b);
-    default: return launch_kp<FP16, 2, 16>(kp, grid, stream, b);
+    case 0: return launch_kp<FP16, 0, 8, CP>(kp, grid, stream, b);
+    case 1: return launch_kp<FP16, 0, 16, CP>(kp, grid, stream, b);
+    case 2: return launch_kp<FP16, 1, 8, CP>(kp, grid, stream, b);
+    case 3: return launch_kp<FP16, 1, 16, CP>(kp, grid, stream, b);
+    case 4: return launch_kp<FP16, 2, 8, CP>(kp, grid, stream, b);
+    default: return launch_kp<FP16, 2, 16, CP>(kp, grid, stream, b);
     }
+}
+
+// Code-load policy of a launch (kStreamLoad when every problem holds tiled codes).
+template <bool FP16>
+hipError_t launch_policy(int gm, int mt, int kp, unsigned grid, hipStream_t stream,
+                         const FewBatch &b)
+{
+    bool all_tiled = true;
+    for (int i = 0; i < b.count; ++i)
+        all_tiled = all_tiled && b.p[i].tiled != 0;
+    return all_tiled ? launch_mode<FP16, kStreamLoad>(gm, mt, kp, grid, stream, b)
+                     : launch_mode<FP16, 0>(gm, mt, kp, grid, stream, b);
 }
 
 }  // namespace
@@ -661,8 +674,8 @@ hipError_t launch_gemm_few(const GemvArgs *args, const int *order, int count, bo
     if (units == 0)
         return hipSuccess;
     const int gm = pl.group == 0 ? 0 : (pl.group == 256 ? 1 : 2);
-    e = fp16 ? launch_mode<true>(gm, pl.mt, pl.kp, (unsigned)units, stream, b)
-             : launch_mode<false>(gm, pl.mt, pl.kp, (unsigned)units, stream, b);
+    e = fp16 ? launch_policy<true>(gm, pl.mt, pl.kp, (unsigned)units, stream, b)
+             : launch_policy<false>(gm, pl.mt, pl.kp, (unsigned)units, stream, b);
     if (e != hipSuccess || runits == 0)
         return e;
     const bool pc = pl.group == 0;

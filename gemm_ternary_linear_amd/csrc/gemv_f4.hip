@@ -236,8 +236,9 @@ __device__ __forceinline__ void convert8(u32x4_t v, int tok, int b, int mq, bool
     }
 }
 
-// GMODE as in Geo; MT: the instance's token count (M <= MT).
-template <bool FP16, int GMODE, int MT>
+// GMODE as in Geo; MT: the instance's token count (M <= MT); CP: the cache
+// policy of the code loads (kStreamLoad when every problem holds tiled codes).
+template <bool FP16, int GMODE, int MT, int CP>
 __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
 {
     using G = Geo<FP16, GMODE, MT>;
@@ -303,12 +304,8 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     constexpr int kSP = G::SP;
     u32x4_t w[kSP];
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kSP; ++j) {
-        w[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, j < S ? woff + (s_begin + j) * sstride : kOOB, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    load_code_run<CP>(w, wr,
+                      [&](int j) { return j < S ? woff + (s_begin + j) * sstride : kOOB; });
     // channel scale of row 4g + (lane & 3): each quad of lanes holds the four
     // rows its C fragment covers (shared by DPP in the epilogue)
     const int ch0 = rb * 16 + 4 * g;
@@ -388,12 +385,9 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     for (int c0 = 0; c0 < S; c0 += kSP) {
         if (c0 > 0) {
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < kSP; ++j) {
-                w[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    wr, c0 + j < S ? woff + (s_begin + c0 + j) * sstride : kOOB, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            load_code_run<CP>(w, wr, [&](int j) {
+                return c0 + j < S ? woff + (s_begin + c0 + j) * sstride : kOOB;
+            });
         }
         if constexpr (GROUPED) {
             // stage the chunk's group scales: [local group][16 rows]
@@ -575,10 +569,10 @@ int lds_need_of(bool fp16, int group, int M, int K)
     }
 }
 
-template <bool FP16, int GMODE, int MT>
+template <bool FP16, int GMODE, int MT, int CP>
 hipError_t launch_inst(unsigned grid, int lds, hipStream_t stream, const F4Batch &b)
 {
-    auto *k = gemv_f4_kernel<FP16, GMODE, MT>;
+    auto *k = gemv_f4_kernel<FP16, GMODE, MT, CP>;
     // dynamic LDS above 64 KB needs the function's limit raised (once)
     static std::atomic<bool> raised{false};
     if (lds > 64 * 1024 && !raised.load(std::memory_order_acquire)) {
@@ -592,27 +586,27 @@ hipError_t launch_inst(unsigned grid, int lds, hipStream_t stream, const F4Batch
     return hipGetLastError();
 }
 
-template <bool FP16, int GMODE>
+template <bool FP16, int GMODE, int CP>
 hipError_t launch_mt(int mt, unsigned grid, int lds, hipStream_t stream, const F4Batch &b)
 {
     switch (mt) {
-    case 1: return launch_inst<FP16, GMODE, 1>(grid, lds, stream, b);
-    case 2: return launch_inst<FP16, GMODE, 2>(grid, lds, stream, b);
-    case 4: return launch_inst<FP16, GMODE, 4>(grid, lds, stream, b);
-    default: return launch_inst<FP16, GMODE, 8>(grid, lds, stream, b);
+    case 1: return launch_inst<FP16, GMODE, 1, CP>(grid, lds, stream, b);
+    case 2: return launch_inst<FP16, GMODE, 2, CP>(grid, lds, stream, b);
+    case 4: return launch_inst<FP16, GMODE, 4, CP>(grid, lds, stream, b);
+    default: return launch_inst<FP16, GMODE, 8, CP>(grid, lds, stream, b);
     }
 }
 
-template <bool FP16>
+template <bool FP16, int CP>
 hipError_t launch_mode(int gm, int mt, unsigned grid, int lds, hipStream_t stream,
                        const F4Batch &b)
 {
     switch (gm) {
-    case 0: return launch_mt<FP16, 0>(mt, grid, lds, stream, b);
-    case 1: return launch_mt<FP16, 1>(mt, grid, lds, stream, b);
-    case 2: return launch_mt<FP16, 2>(mt, grid, lds, stream, b);
-    case 3: return launch_mt<FP16, 3>(mt, grid, lds, stream, b);
-    default: return launch_mt<FP16, 4>(mt, grid, lds, stream, b);
+    case 0: return launch_mt<FP16, 0, CP>(mt, grid, lds, stream, b);
+    case 1: return launch_mt<FP16, 1, CP>(mt, grid, lds, stream, b);
+    case 2: return launch_mt<FP16, 2, CP>(mt, grid, lds, stream, b);
+    case 3: return launch_mt<FP16, 3, CP>(mt, grid, lds, stream, b);
+    default: return launch_mt<FP16, 4, CP>(mt, grid, lds, stream, b);
     }
 }
 
@@ -703,8 +697,16 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
     if (b.count == 0)
         return hipSuccess;
     const int gm = gmode_of(group);
-    return fp16 ? launch_mode<true>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b)
-                : launch_mode<false>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b);
+    bool all_tiled = true;
+    for (int i = 0; i < b.count; ++i)
+        all_tiled = all_tiled && b.p[i].tiled != 0;
+    if (all_tiled)
+        return fp16 ? launch_mode<true, kStreamLoad>(gm, kernel_mt(mt), (unsigned)units, lds,
+                                                     stream, b)
+                    : launch_mode<false, kStreamLoad>(gm, kernel_mt(mt), (unsigned)units, lds,
+                                                      stream, b);
+    return fp16 ? launch_mode<true, 0>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b)
+                : launch_mode<false, 0>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b);
 }
 
 }  // namespace ternary

@@ -295,7 +295,7 @@ __device__ __forceinline__ void fold_scales(const WaveCtx &c, int col, f32x4_t p
 
 // Run a K part of exactly S <= one_shot<MT, GROUPED>() slabs, every load
 // issued up front; returns this lane's fp32 accumulator.
-template <bool FP16, bool GROUPED, int GC, int MT, int S>
+template <int CP, bool FP16, bool GROUPED, int GC, int MT, int S>
 __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
 {
     // ---- issue every load of the part: scales, x (by DMA into this wave's
@@ -326,12 +326,8 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
             dma16_to_lds(c.xr, c.xbuf + 512 * j, xoff[j]);
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t w[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-        w[i] = __builtin_amdgcn_raw_buffer_load_b128(c.wr, c.woff + (c.s_begin + i) * c.sstride,
-                                                     0, 0);
-        __builtin_amdgcn_sched_barrier(0);  // keep issue order = consumption order
-    }
+    // in issue order = consumption order
+    load_code_run<CP>(w, c.wr, [&](int i) { return c.woff + (c.s_begin + i) * c.sstride; });
     chs = channel_scale_load<GROUPED>(c);
 
     // ---- scales into this wave's LDS ---------------------------------------
@@ -364,7 +360,7 @@ __device__ __forceinline__ f32x4_t run_part(const WaveCtx &c, uint32_t &chs)
 // i % kWindow, and the loads of slab i + kWindow are issued as soon as slab i
 // is consumed.  Slots past the part load as zeros without touching memory, so
 // every pass issues the same loads and the compiler's waits stay exact.
-template <bool FP16, int GC, int MT>
+template <int CP, bool FP16, int GC, int MT>
 __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t &chs)
 {
     constexpr int W = kWindow;
@@ -373,8 +369,7 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
     auto issue = [&](int slot, int i) {
         const bool in = i < S;
         xv[slot] = x_piece_load<MT>(c, in ? c.s_begin + i : (1 << 20));
-        w[slot] = __builtin_amdgcn_raw_buffer_load_b128(
-            c.wr, in ? c.woff + (c.s_begin + i) * c.sstride : kOOB, 0, 0);
+        w[slot] = load_codes<CP>(c.wr, in ? c.woff + (c.s_begin + i) * c.sstride : kOOB);
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
@@ -404,13 +399,13 @@ __device__ __forceinline__ f32x4_t run_rolling(const WaveCtx &c, int S, uint32_t
 }
 
 // A part of exactly n <= one_shot<MT, GROUPED>() slabs (S counts up to n).
-template <bool FP16, bool GROUPED, int GC, int MT, int S = 1>
+template <int CP, bool FP16, bool GROUPED, int GC, int MT, int S = 1>
 __device__ __forceinline__ f32x4_t run_short(const WaveCtx &c, int n, uint32_t &chs)
 {
     if (n == S || S == one_shot<MT, GROUPED>())
-        return run_part<FP16, GROUPED, GC, MT, S>(c, chs);
+        return run_part<CP, FP16, GROUPED, GC, MT, S>(c, chs);
     if constexpr (S < one_shot<MT, GROUPED>())
-        return run_short<FP16, GROUPED, GC, MT, S + 1>(c, n, chs);
+        return run_short<CP, FP16, GROUPED, GC, MT, S + 1>(c, n, chs);
     else
         return f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
@@ -420,7 +415,7 @@ __device__ __forceinline__ f32x4_t run_short(const WaveCtx &c, int n, uint32_t &
 // (grouped parts, whose scales take registers of their own, and 4 or 8 tokens,
 // whose x per slab would take too many) as ceil(n / L) one-shot chunks of
 // near-equal length in turn.
-template <bool FP16, bool GROUPED, int GC, int MT>
+template <int CP, bool FP16, bool GROUPED, int GC, int MT>
 __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t &chs)
 {
     constexpr int L = one_shot<MT, GROUPED>();
@@ -429,16 +424,17 @@ __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t 
         return f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     if (n <= L)
-        return run_short<FP16, GROUPED, GC, MT>(c, n, chs);
+        return run_short<CP, FP16, GROUPED, GC, MT>(c, n, chs);
     if constexpr (MT <= 2 && !GROUPED) {
-        return run_rolling<FP16, GC, MT>(c, n, chs);
+        return run_rolling<CP, FP16, GC, MT>(c, n, chs);
     } else {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         WaveCtx cc = c;
         const int chunks = (n + L - 1) / L, len = (n + chunks - 1) / chunks;
         for (int done = 0; done < n; done += len) {
             cc.s_begin = c.s_begin + done;
-            const f32x4_t part = run_short<FP16, GROUPED, GC, MT>(cc, min(len, n - done), chs);
+            const f32x4_t part =
+                run_short<CP, FP16, GROUPED, GC, MT>(cc, min(len, n - done), chs);
             acc[0] += part[0];
             acc[1] += part[1];
             acc[2] += part[2];
@@ -454,7 +450,7 @@ __device__ __forceinline__ f32x4_t run_part_n(const WaveCtx &c, int n, uint32_t 
 // (per-channel instances of 2 or more tokens are held to 64 VGPRs, 8 waves per
 // SIMD; the 1-token per-channel instance, whose one-shot parts hold 8 slabs of
 // codes, and the group-scaled ones keep the registers they need: no scratch)
-template <bool FP16, bool GROUPED, int GC, int MT>
+template <bool FP16, bool GROUPED, int GC, int MT, int CP>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(GROUPED || MT == 1 ? 1 : 8))) gemv_stream_kernel(const StreamBatch batch)
 {
@@ -536,7 +532,7 @@ __global__ void __launch_bounds__(kThreads)
     c.chs_off = chs_r < nrows ? chs_r * 2 : kOOB;
 
     uint32_t chs = 0u;
-    const f32x4_t acc = run_part_n<FP16, GROUPED, GC, MT>(c, S, chs);
+    const f32x4_t acc = run_part_n<CP, FP16, GROUPED, GC, MT>(c, S, chs);
 
     // ---- K-part reduction (the last wave of the block, fixed order) --------
     f32x4_t sum = acc;
@@ -631,41 +627,56 @@ namespace {
 // Token count of the kernel instance that runs M tokens.
 int kernel_mt(int M) { return M <= 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8)); }
 
-template <bool FP16, bool GROUPED, int GC, int MT>
+template <bool FP16, bool GROUPED, int GC, int MT, int CP>
 void launch_one(dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
 {
     constexpr size_t lds = lds_bytes<GC, MT, GROUPED>();
-    hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, MT>), grid, block, lds, stream, b);
+    hipLaunchKernelGGL((gemv_stream_kernel<FP16, GROUPED, GC, MT, CP>), grid, block, lds, stream,
+                       b);
 }
 
 // MT * GC <= 16: the instances that exist.
-template <bool FP16, bool GROUPED, int GC>
+template <bool FP16, bool GROUPED, int GC, int CP>
 void launch_m(int mt, dim3 grid, dim3 block, hipStream_t stream, const StreamBatch &b)
 {
     if (mt == 1)
-        launch_one<FP16, GROUPED, GC, 1>(grid, block, stream, b);
+        launch_one<FP16, GROUPED, GC, 1, CP>(grid, block, stream, b);
     else if (mt == 2)
-        launch_one<FP16, GROUPED, GC, 2>(grid, block, stream, b);
+        launch_one<FP16, GROUPED, GC, 2, CP>(grid, block, stream, b);
     else if constexpr (GC <= 4) {
         if (mt == 4)
-            launch_one<FP16, GROUPED, GC, 4>(grid, block, stream, b);
+            launch_one<FP16, GROUPED, GC, 4, CP>(grid, block, stream, b);
         else if constexpr (GC == 2)
-            launch_one<FP16, GROUPED, GC, 8>(grid, block, stream, b);
+            launch_one<FP16, GROUPED, GC, 8, CP>(grid, block, stream, b);
     }
 }
 
-template <bool FP16>
+template <bool FP16, int CP>
 void launch_group(int group, int mt, dim3 grid, dim3 block, hipStream_t stream,
                   const StreamBatch &b)
 {
     if (group == 0)
-        launch_m<FP16, false, 2>(mt, grid, block, stream, b);
+        launch_m<FP16, false, 2, CP>(mt, grid, block, stream, b);
     else if (group == 32)
-        launch_m<FP16, true, 8>(mt, grid, block, stream, b);
+        launch_m<FP16, true, 8, CP>(mt, grid, block, stream, b);
     else if (group == 64)
-        launch_m<FP16, true, 4>(mt, grid, block, stream, b);
+        launch_m<FP16, true, 4, CP>(mt, grid, block, stream, b);
     else
-        launch_m<FP16, true, 2>(mt, grid, block, stream, b);
+        launch_m<FP16, true, 2, CP>(mt, grid, block, stream, b);
+}
+
+// Code-load policy of a launch (kStreamLoad when every problem holds tiled codes).
+template <bool FP16>
+void launch_policy(int group, int mt, dim3 grid, dim3 block, hipStream_t stream,
+                   const StreamBatch &b)
+{
+    bool all_tiled = true;
+    for (int i = 0; i < b.count; ++i)
+        all_tiled = all_tiled && b.p[i].tiled != 0;
+    if (all_tiled)
+        launch_group<FP16, kStreamLoad>(group, mt, grid, block, stream, b);
+    else
+        launch_group<FP16, 0>(group, mt, grid, block, stream, b);
 }
 
 // One-shot part length of the instance (one_shot<MT, GROUPED>() at run time).
@@ -735,9 +746,9 @@ hipError_t launch_gemv_stream(const GemvArgs *args, const int *order, int count,
         return hipSuccess;
     const dim3 grid(units), block(kThreads);
     if (fp16)
-        launch_group<true>(group, kernel_mt(mt), grid, block, stream, b);
+        launch_policy<true>(group, kernel_mt(mt), grid, block, stream, b);
     else
-        launch_group<false>(group, kernel_mt(mt), grid, block, stream, b);
+        launch_policy<false>(group, kernel_mt(mt), grid, block, stream, b);
     return hipGetLastError();
 }
 

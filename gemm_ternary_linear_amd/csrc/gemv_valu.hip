@@ -74,11 +74,13 @@ __global__ void __launch_bounds__(kValuThreads)
     for (int c0 = wave * kChunk; c0 < K; c0 += kValuWaves * kChunk) {
         const int k0 = c0 + 16 * lane;  // this lane's first code of the chunk
         const bool live = k0 < K;       // K % 256 == 0: a lane's 16 codes are all in or all out
+        // a wave's load covers 256 whole bytes of one row, read once:
+        // non-temporal, like the tiled codes of the matrix-core kernels
         uint32_t w[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             w[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                wr, live && r < nrows ? r * rowbytes + (k0 >> 2) : kOOBv, 0, 0);
+                wr, live && r < nrows ? r * rowbytes + (k0 >> 2) : kOOBv, 0, kStreamLoad);
         float xf[16];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

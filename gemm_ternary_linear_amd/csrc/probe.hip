@@ -12,7 +12,21 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t fold(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// One 16-byte load, plain or non-temporal (the `nt` cache-policy bit).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4 *p)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
 // Grid-stride read of n 16-byte words, four loads in flight per lane.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4 *__restrict__ src,
                                                               int64_t n, uint32_t *sink)
 {
@@ -20,12 +34,12 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4 *__res
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t acc = 0;
     for (; i + 3 * stride < n; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-                    d = src[i + 3 * stride];
+        const uint4 a = load16<NT>(src + i), b = load16<NT>(src + i + stride),
+                    c = load16<NT>(src + i + 2 * stride), d = load16<NT>(src + i + 3 * stride);
         acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
     }
     for (; i < n; i += stride)
-        acc ^= fold(src[i]);
+        acc ^= fold(load16<NT>(src + i));
     // A store that depends on every load keeps them live; it almost never runs.
     if (acc == 0x9e3779b9u)
         sink[0] = acc;
@@ -89,12 +103,9 @@ bool bad_grid(int32_t workgroups) { return workgroups < 1 || workgroups > TERNAR
 
 int launched() { return hipGetLastError() == hipSuccess ? TERNARY_OK : TERNARY_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int ternary_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink,
-                       hipStream_t stream)
+template <bool NT>
+int probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink,
+               hipStream_t stream)
 {
     if (bytes < 0 || bytes % 16 != 0 || bad_grid(workgroups))
         return TERNARY_ERR_SHAPE;
@@ -104,9 +115,25 @@ int ternary_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint3
         return TERNARY_ERR_NULL;
     if (!aligned(src, 16) || !aligned(sink, 4))
         return TERNARY_ERR_ALIGN;
-    hipLaunchKernelGGL(probe_read_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(probe_read_kernel<NT>, dim3(workgroups), dim3(kThreads), 0, stream,
                        (const uint4 *)src, bytes / 16, sink);
     return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ternary_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink,
+                       hipStream_t stream)
+{
+    return probe_read<false>(src, bytes, workgroups, sink, stream);
+}
+
+int ternary_probe_read_nt(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink,
+                          hipStream_t stream)
+{
+    return probe_read<true>(src, bytes, workgroups, sink, stream);
 }
 
 int ternary_probe_copy(const void *src, void *dst, int64_t bytes, int32_t workgroups,

@@ -43,6 +43,14 @@ int ternary_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint3
                        hipStream_t stream);
 
 /*
+ * ternary_probe_read_nt - ternary_probe_read with non-temporal loads (the `nt`
+ * cache-policy bit, the policy the decode kernels give their code loads);
+ * same arguments, errors and traffic.
+ */
+int ternary_probe_read_nt(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink,
+                          hipStream_t stream);
+
+/*
  * ternary_probe_copy - copy `bytes` bytes from src to dst with 16-byte loads
  * and stores (grid-stride, four in flight per lane); it reads and writes
  * `bytes` bytes each.

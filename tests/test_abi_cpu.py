@@ -254,6 +254,11 @@ def test_probe_rejects(tl):
     assert L.ternary_probe_read(A, 0, 64, None, None) == 0
     assert L.ternary_probe_read(None, 1024, 64, A, None) == NULL
     assert L.ternary_probe_read(A + 4, 1024, 64, A, None) == ALIGN
+    assert L.ternary_probe_read_nt(A, 17, 64, A, None) == SHAPE
+    assert L.ternary_probe_read_nt(A, 1024, 65537, A, None) == SHAPE
+    assert L.ternary_probe_read_nt(A, 0, 64, None, None) == 0
+    assert L.ternary_probe_read_nt(None, 1024, 64, A, None) == NULL
+    assert L.ternary_probe_read_nt(A + 4, 1024, 64, A, None) == ALIGN
     assert L.ternary_probe_copy(A, B, 24, 64, None) == SHAPE
     assert L.ternary_probe_copy(A, None, 1024, 64, None) == NULL
     assert L.ternary_probe_copy(A, B + 8, 1024, 64, None) == ALIGN

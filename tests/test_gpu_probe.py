@@ -34,13 +34,14 @@ def test_probe_copy_exact(tl, nbytes, wg):
     assert torch.equal(src, dst)
 
 
+@pytest.mark.parametrize("nt", [False, True])
 @pytest.mark.parametrize("nbytes,wg", [(16, 1), (16 * 1001, 7), ((1 << 22) + 48, 300)])
-def test_probe_read_runs(tl, nbytes, wg):
+def test_probe_read_runs(tl, nbytes, wg, nt):
     import torch
-    say(f"probe read bytes={nbytes} wg={wg}")
+    say(f"probe read bytes={nbytes} wg={wg} nontemporal={nt}")
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    tl.probe_read(src, sink, wg)
+    tl.probe_read(src, sink, wg, nontemporal=nt)
     torch.cuda.synchronize()
 
 
