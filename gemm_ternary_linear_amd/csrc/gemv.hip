@@ -15,13 +15,14 @@
 // matrix cores as it is.  Measured on MI355X (tiled codes, fused launches of
 // the 7B layer): 2 / 4 / 8 tokens 18.1 / 21.5 / 27.2 us on the 16-bit kernel
 // against 20.7 / 23.4 / 33.8 us with the fp4 one; the 27B group-128 pair at
-// 4 tokens 23.0 against 36.6 us; at one token the fp4 kernel wins in fused
-// launches (7B layer 14.3 against 16.1 us) and on lone wide projections (7B
-// gate 7.3 against 8.2 us, 27B up 12.5 against 12.9 us), while a lone
-// projection of fewer than 8192 channels runs faster on the 16-bit kernel,
-// whose workgroups stage only their own part of x (27B down 15.4 against 16.2
-// us, 7B down 8.6 against 9.2, 7B k 3.5 against 3.9, 1024 x 1024 3.3 against
-// 3.7).
+// 4 tokens 23.0 against 36.6 us.  At one token the fp4 kernel wins in fused
+// launches (7B layer 13.0 against 16.1 us) and on lone projections with
+// K <= 8192 (tiled codes, weights rotating over 1 GiB: 7B gate 6.7 against
+// 7.5 us, 27B up 10.5 against 12.7, 7B q 3.8 against 4.1, 1024 x 1024 3.8
+// against 3.9), while a lone projection of fewer than 8192 channels with
+// longer K runs faster on the 16-bit kernel, whose workgroups stage only their
+// own part of x instead of converting all of it (27B down 15.0 against 16.1
+// us, 7B down 7.9 against 8.8).
 #include "internal.h"
 
 namespace ternary {
@@ -53,7 +54,8 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
         }
     // Each group value (per channel, 32, 64, 128, 256), each M and each kernel
     // is a separate instance: one launch per non-empty class.  A lone
-    // one-token problem of fewer than 8192 channels prefers the 16-bit kernel.
+    // one-token problem of fewer than 8192 channels and K > 8192 prefers the
+    // 16-bit kernel.
     int n_m1 = 0;
     for (int i = 0; i < count; ++i)
         n_m1 += args[i].M == 1 && args[i].N > 0 ? 1 : 0;
@@ -65,7 +67,7 @@ hipError_t launch_gemv_batch(const GemvArgs *args, int count, bool fp16, hipStre
             const GemvArgs &a = args[order[oi]];
             if (a.group != group || a.M == 0 || a.N == 0)
                 continue;
-            const bool f4_first = a.M == 1 && !(n_m1 == 1 && a.N < 8192);
+            const bool f4_first = a.M == 1 && !(n_m1 == 1 && a.N < 8192 && a.K > 8192);
             const bool use_f4 =
                 kernel != GemvKernel::B16 && gemv_f4_takes(a.M, a.K, group, fp16) &&
                 (kernel == GemvKernel::F4 || f4_first || !gemv_stream_takes(a.M, a.K, group));

@@ -50,6 +50,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 namespace ternary {
 
@@ -569,11 +570,13 @@ int lds_need_of(bool fp16, int group, int M, int K)
     }
 }
 
+// The kernel instance of (fp16, group mode, token tile, code-load policy),
+// with its dynamic-LDS limit raised to kGemvF4MaxLds when `lds` exceeds the
+// default 64 KB (once per instance).
 template <bool FP16, int GMODE, int MT, int CP>
-hipError_t launch_inst(unsigned grid, int lds, hipStream_t stream, const F4Batch &b)
+hipError_t instance(int lds, const void **fn)
 {
     auto *k = gemv_f4_kernel<FP16, GMODE, MT, CP>;
-    // dynamic LDS above 64 KB needs the function's limit raised (once)
     static std::atomic<bool> raised{false};
     if (lds > 64 * 1024 && !raised.load(std::memory_order_acquire)) {
         const hipError_t e = hipFuncSetAttribute(
@@ -582,32 +585,57 @@ hipError_t launch_inst(unsigned grid, int lds, hipStream_t stream, const F4Batch
             return e;
         raised.store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), (size_t)lds, stream, b);
-    return hipGetLastError();
+    *fn = (const void *)k;
+    return hipSuccess;
 }
 
-template <bool FP16, int GMODE, int CP>
-hipError_t launch_mt(int mt, unsigned grid, int lds, hipStream_t stream, const F4Batch &b)
+hipError_t instance_of(bool fp16, int gm, int mt, int cp, int lds, const void **fn)
 {
-    switch (mt) {
-    case 1: return launch_inst<FP16, GMODE, 1, CP>(grid, lds, stream, b);
-    case 2: return launch_inst<FP16, GMODE, 2, CP>(grid, lds, stream, b);
-    case 4: return launch_inst<FP16, GMODE, 4, CP>(grid, lds, stream, b);
-    default: return launch_inst<FP16, GMODE, 8, CP>(grid, lds, stream, b);
-    }
+    auto by_mt = [&]<bool FP16, int GMODE, int CP>() -> hipError_t {
+        switch (mt) {
+        case 1: return instance<FP16, GMODE, 1, CP>(lds, fn);
+        case 2: return instance<FP16, GMODE, 2, CP>(lds, fn);
+        case 4: return instance<FP16, GMODE, 4, CP>(lds, fn);
+        default: return instance<FP16, GMODE, 8, CP>(lds, fn);
+        }
+    };
+    auto by_gm = [&]<bool FP16, int CP>() -> hipError_t {
+        switch (gm) {
+        case 0: return by_mt.template operator()<FP16, 0, CP>();
+        case 1: return by_mt.template operator()<FP16, 1, CP>();
+        case 2: return by_mt.template operator()<FP16, 2, CP>();
+        case 3: return by_mt.template operator()<FP16, 3, CP>();
+        default: return by_mt.template operator()<FP16, 4, CP>();
+        }
+    };
+    if (cp == kStreamLoad)
+        return fp16 ? by_gm.template operator()<true, kStreamLoad>()
+                    : by_gm.template operator()<false, kStreamLoad>();
+    return fp16 ? by_gm.template operator()<true, 0>() : by_gm.template operator()<false, 0>();
 }
 
-template <bool FP16, int CP>
-hipError_t launch_mode(int gm, int mt, unsigned grid, int lds, hipStream_t stream,
-                       const F4Batch &b)
+// Workgroups of kernel `fn` with `lds` bytes of dynamic LDS that one compute
+// unit holds at once (the occupancy calculator; cached per kernel and size).
+int resident_per_cu(const void *fn, int lds)
 {
-    switch (gm) {
-    case 0: return launch_mt<FP16, 0, CP>(mt, grid, lds, stream, b);
-    case 1: return launch_mt<FP16, 1, CP>(mt, grid, lds, stream, b);
-    case 2: return launch_mt<FP16, 2, CP>(mt, grid, lds, stream, b);
-    case 3: return launch_mt<FP16, 3, CP>(mt, grid, lds, stream, b);
-    default: return launch_mt<FP16, 4, CP>(mt, grid, lds, stream, b);
-    }
+    struct Entry {
+        const void *fn;
+        int lds, n;
+    };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].lds == lds)
+            return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, (size_t)lds) != hipSuccess ||
+        n < 1)
+        n = 1;
+    if (used < 64)
+        cache[used++] = {fn, lds, n};
+    return n;
 }
 
 // K parts per block: the smallest power of two (up to kWaves) whose parts hold
@@ -696,17 +724,52 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
         return e;
     if (b.count == 0)
         return hipSuccess;
-    const int gm = gmode_of(group);
     bool all_tiled = true;
     for (int i = 0; i < b.count; ++i)
         all_tiled = all_tiled && b.p[i].tiled != 0;
-    if (all_tiled)
-        return fp16 ? launch_mode<true, kStreamLoad>(gm, kernel_mt(mt), (unsigned)units, lds,
-                                                     stream, b)
-                    : launch_mode<false, kStreamLoad>(gm, kernel_mt(mt), (unsigned)units, lds,
-                                                      stream, b);
-    return fp16 ? launch_mode<true, 0>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b)
-                : launch_mode<false, 0>(gm, kernel_mt(mt), (unsigned)units, lds, stream, b);
+    const void *fn = nullptr;
+    e = instance_of(fp16, gmode_of(group), kernel_mt(mt), all_tiled ? kStreamLoad : 0, lds, &fn);
+    if (e != hipSuccess)
+        return e;
+    if (b.count == 1 && (b.p[0].N + 15) / 16 >= kWaves) {
+        // One problem: its workgroups are all alike.  A wave loads its part in
+        // chunks of SP slabs, one memory round trip each, so a part of 5
+        // slabs costs two round trips for 5 KB where one of 4 costs one.
+        // Take the most K parts per block whose parts are whole chunks (or at
+        // least two), whose workgroups fit in one round of what the device
+        // holds at once and cover half the compute units; failing that, the
+        // most parts that fit in one round.  Measured on MI355X at one token:
+        // the 25600 x 5120 projection (20 slabs) with 2 parts (400
+        // workgroups) 10.5 us, against 11.9 with 4 (800, 5-slab parts) and
+        // 13.3 with 8; the 18944 x 4096 one with 4 parts (592) 6.8 us,
+        // against 6.9 with 2 and 8.2 with 8.
+        F4Problem &p = b.p[0];
+        const int nblocks = (p.N + 15) / 16, nslabs = (p.K + 255) / 256;
+        const int slots = resident_per_cu(fn, lds) * device_cus();
+        const int sp = passes_of(fp16, group, mt) == 1 ? 4 : 8;
+        int best = 0, fit = 0;
+        for (int kp = kWaves; kp >= 1; kp /= 2) {
+            const int n = (nblocks + kWaves / kp - 1) / (kWaves / kp);
+            const int per = (nslabs + kp - 1) / kp;
+            if (kp > nslabs || n > slots)
+                continue;
+            if (fit == 0)
+                fit = kp;
+            if ((per % sp == 0 || per >= 2 * sp) && 2 * n >= device_cus()) {
+                best = kp;
+                break;
+            }
+        }
+        if (best == 0)
+            best = fit;
+        if (best != 0) {
+            p.kp = best;
+            p.rb = kWaves / best;
+            units = (nblocks + p.rb - 1) / p.rb;
+        }
+    }
+    void *kargs[] = {&b};
+    return hipLaunchKernel(fn, dim3(units), dim3(kThreads), kargs, (size_t)lds, stream);
 }
 
 }  // namespace ternary

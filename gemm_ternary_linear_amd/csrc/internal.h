@@ -60,7 +60,7 @@ hipError_t launch_quantize(const uint16_t *w, bool fp16, int N, int K, int group
 // `group` as in GemvArgs, shapes already validated by the caller.
 // Which decode kernel runs a GEMV problem: AUTO takes the fp4 x fp8 one for
 // M == 1 (the 16-bit one for a launch's lone one-token problem of fewer than
-// 8192 channels) and the 16-bit one for larger M, each where it takes the
+// 8192 channels and K > 8192) and the 16-bit one for larger M, each where it takes the
 // shape, else the other; F4 and B16 force one (parity tests, tuning).
 // Both read row-major and tiled codes.
 enum class GemvKernel { AUTO, F4, B16 };

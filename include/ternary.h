@@ -98,7 +98,8 @@ typedef enum {
     TERNARY_PATH_AUTO = 0,
     TERNARY_PATH_GEMV = 1,     /* decode GEMV, requires 1 <= M <= ternary_gemv_max_m();
                                   at M == 1 the fp4 x fp8 kernel (a single call of
-                                  fewer than 8192 channels: the 16-bit one), at
+                                  fewer than 8192 channels and K > 8192: the
+                                  16-bit one), at
                                   larger M the 16-bit one, each where it takes the
                                   shape, else the other                                */
     TERNARY_PATH_GEMM = 2,     /* prefill kernel (bf16/fp16 MFMA)                       */
@@ -208,7 +209,7 @@ int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t gro
  * output dtype, round-to-nearest-even.  x and s must be finite (results for
  * non-finite inputs are unspecified) and |x| < 2^126.
  * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (the fp4 x fp8
- * kernel at M == 1 except for N < 8192, the 16-bit one otherwise, each where
+ * kernel at M == 1 except for N < 8192 with K > 8192, the 16-bit one otherwise, each where
  * it takes the shape); 9 <= M <= 16 the few-token GEMM (TERNARY_PATH_FEW) where it takes
  * the shape; larger M and the rest the MFMA GEMM; shapes no fast kernel
  * takes (K % 128 != 0) run the plain kernel.  The GEMV gives each token 2
