@@ -55,6 +55,7 @@ constexpr int kAhead = kS - 1;  // slabs loaded ahead of the one computed
 constexpr int kFN = 1;          // 16-channel blocks per wave
 constexpr int kOOB = 0x40000000;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kMaxSlices = 16;  // K slices of one problem over workgroups
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u4;
@@ -466,13 +467,48 @@ __global__ void __launch_bounds__(kReduceThreads) few_reduce(const FewReduceBatc
     const int nv = min(4, R.N - n);
     const int64_t slice_stride = (int64_t)R.M * R.N;
     const float *src = R.partial + (int64_t)t * R.N + n;
+    uint16_t *yr = R.y + (int64_t)t * R.N + n;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    if (nv == 4 && (R.N & 3) == 0 && (int64_t)R.ks * slice_stride * 4 < ((int64_t)1 << 31)) {
+        // 16-byte aligned, whole, 32-bit offsets: the scales and every slice's partials
+        // are loaded before the first add (one memory round trip instead of
+        // one per slice), then the sums are taken in slice order
+        uint16_t sc[4] = {0, 0, 0, 0};
+        if constexpr (PC)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sc[r] = R.scale[n + r];
+        // (slices past ks take an offset past the resource: no load issued
+        // to memory, no branch between the loads; they are not added)
+        const __amdgpu_buffer_rsrc_t pr =
+            make_rsrc(R.partial, (uint32_t)((int64_t)R.ks * slice_stride * 4));
+        const int off0 = (int)(((int64_t)t * R.N + n) * 4);
+        u32x4_t v[kMaxSlices];
+#pragma unroll
+        for (int s = 0; s < kMaxSlices; ++s)
+            v[s] = __builtin_amdgcn_raw_buffer_load_b128(
+                pr, s < R.ks ? off0 + (int)(s * slice_stride * 4) : kOOB, 0, 0);
+        // (each element is copied to a scalar before the bit cast: this
+        // compiler's __builtin_bit_cast of a vector element expression read
+        // element 0 whatever the index)
+#pragma unroll
+        for (int s = 0; s < kMaxSlices; ++s)
+            if (s < R.ks)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t u = v[s][r];
+                    sum[r] += __builtin_bit_cast(float, u);
+                }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            yr[r] = round_out<FP16>(sum[r] * (PC ? 0.5f * f16_bits_to_f32(sc[r]) : 0.5f));
+        return;
+    }
     for (int s = 0; s < R.ks; ++s)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (r < nv)
                 sum[r] += src[s * slice_stride + r];
-    uint16_t *yr = R.y + (int64_t)t * R.N + n;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         if (r < nv)
@@ -538,7 +574,6 @@ namespace {
 // Slab steps a workgroup aims at: long K ranges are sliced over workgroups
 // so that the workgroups of one launch run about equally long.
 constexpr int kFewSteps = 16;
-constexpr int kMaxSlices = 16;
 
 struct FewPlan {
     int kp, mt, group;
