@@ -634,16 +634,36 @@ __global__ void __launch_bounds__(256)
     const int m = (tile / ntn) * C::TM + ((wave / C::WGN) * FM + j) * 16 + (lane & 15);
     if (m >= M || n >= N)
         return;
-    const float4 *src = partial + (int64_t)tile * ksplit * TILE4 + e;
-    float4 v = src[0];
-    for (int q = 1; q < ksplit; ++q) {
-        const float4 w = src[(int64_t)q * TILE4];
-        v.x += w.x;
-        v.y += w.y;
-        v.z += w.z;
-        v.w += w.w;
+    // Slices in batches of kBatch loads issued together (one memory round
+    // trip per batch, not per slice); slices past ksplit take an offset past
+    // the resource (no memory access) and are not added.  The partial tiles
+    // of one launch hold at most 2 GiB, so byte offsets fit in 32 bits.
+    constexpr int kBatch = 8;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float4 *>(partial), (short)0,
+        (int)((int64_t)ntn * ntm * ksplit * TILE4 * 16), 0x00020000);
+    const int64_t first = (int64_t)tile * ksplit * TILE4 + e;  // float4 index of slice 0
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < ksplit; q0 += kBatch) {
+        u32x4_t w[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            w[b] = __builtin_amdgcn_raw_buffer_load_b128(
+                pr, q0 + b < ksplit ? (int)((first + (int64_t)(q0 + b) * TILE4) * 16) : kOOB, 0,
+                0);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            if (q0 + b < ksplit)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // (element copied to a scalar before the bit cast: this
+                    // compiler's bit cast of a vector element expression read
+                    // element 0 whatever the index)
+                    const uint32_t u = w[b][r];
+                    const float x = __builtin_bit_cast(float, u);
+                    a[r] = q0 + b == 0 ? x : a[r] + x;  // slice 0 as is, then in order
+                }
     }
-    const float a[4] = {v.x, v.y, v.z, v.w};
     uint16_t *yr = y + (int64_t)m * N;
     if ((N & 3) == 0 && n + 3 < N) {
         uint32_t o[4];
@@ -780,11 +800,31 @@ size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order
             order[j] = order[j - 1];
             order[j - 1] = t;
         }
+    // Tiles that cover the compute units but differ in length (a long-K
+    // problem among short ones): a problem whose tiles run at least twice a
+    // workgroup slot's fair share of the launch (the sum of tiles x K over
+    // the compute units x workgroups per unit) is split into slices of about
+    // that share, whole rounds of NS steps, at least two per slice.  Measured
+    // on MI355X: the 7B-shaped layer at M = 32, whose 32 down tiles (K =
+    // 18944) ran 4.6 times as long as the other 368, from 102 us unsplit.
+    int64_t work = 0;
+    for (int i = 0; i < count; ++i)
+        work += (int64_t)tiles[i] * args[idx[i]].K;
+    const int64_t share = std::max<int64_t>(1, work / ((int64_t)device_cus() * C::OCC));
     size_t ws_bytes = 0;
     for (int i = 0; i < count; ++i) {
-        ks[i] = total < device_cus()
-                    ? big_ksplit(tiles[i], args[idx[i]].K, C::NS, C::TN * C::TM)
-                    : 1;
+        const int K = args[idx[i]].K;
+        if (total < device_cus()) {
+            ks[i] = big_ksplit(tiles[i], K, C::NS, C::TN * C::TM);
+        } else if (count > 1 && K >= 2 * share) {
+            const int rounds = K / (dma::TK * C::NS);
+            ks[i] = (int)std::min<int64_t>((K + share - 1) / share, rounds / 2);
+            while (ks[i] > 1 && (int64_t)tiles[i] * ks[i] * C::TN * C::TM * 4 > (int64_t(1) << 31))
+                --ks[i];
+            ks[i] = std::max(ks[i], 1);
+        } else {
+            ks[i] = 1;
+        }
         if (ks[i] > 1)
             ws_bytes += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
     }
