@@ -808,7 +808,7 @@ def sweep_configs(tl, min_rotate=ROTATE_BYTES, max_copies=4096):
 WORKLOADS = {
     "27b_m16": (4, 16, False), "27b_m64": (4, 64, False), "27b_m256": (4, 256, False),
     "7b_decode_single_m1": (2, 1, False), "7b_decode_fused_m8": (2, 8, True),
-    "7b_fused_m16": (2, 16, True),
+    "7b_fused_m16": (2, 16, True), "7b_fused_m32": (2, 32, True),
 }
 WORKLOAD_REPS = 6
 
@@ -821,7 +821,7 @@ def run_workload(tl, name):
     cfg, M, fused = WORKLOADS[name]
     layer = Layer(tl, cfg, M, layout="tiled")
     copy_probe()
-    if cfg == 4:  # MFMA reference for the GEMM launches' busy counters
+    if cfg == 4 or M >= 16:  # MFMA reference for the matrix-core launches' busy counters
         buf = torch.empty(2048 * tl.PROBE_THREADS, dtype=torch.float32, device="cuda:0")
         tl.probe_mfma(2048, PROBE_ITERS[2048], buf)
         torch.cuda.synchronize()
