@@ -138,3 +138,17 @@ def test_batch_rejects_alias_on_device(tl):
     with pytest.raises(tl.TernaryError) as e:
         tl.linear_batch([(x, p, s, 128, y), (x, p, s, 128, y)])
     assert e.value.status == -6
+
+
+@pytest.mark.parametrize("cfg,M", [(2, 32), (4, 256)])
+def test_batch_balanced_split(tl, cfg, M):
+    # Grouped GEMM launches whose tiles cover the compute units but whose one
+    # long-K problem runs far longer per tile than the rest: the 7B-shaped
+    # layer at 32 tokens (368 tiles of K = 4096, 32 down tiles of K = 18944)
+    # and the 27B-class group-128 pair at 256 tokens (up K = 5120, down
+    # K = 25600).  The long problem's K range is sliced over workgroups and
+    # reduced in slice order; 1500 sampled outputs per problem.
+    c = synth.CONFIGS[cfg]
+    say(f"balanced K slices in a grouped launch: {c.name}, M={M}")
+    specs = [(M, s.N, s.K, c.group_size) for s in c.shapes]
+    _run_and_check(tl, _problems(np.random.default_rng(46 + M), specs), samples=1500)
