@@ -951,7 +951,8 @@ def measure_ceilings(tl, layer_bytes, steps):
     - read_1GiB: one 16-byte-load streaming read of 1 GiB;
     - read_layer_size: `steps` reads of `layer_bytes` each (the decode layer's
       algorithmic bytes), rotating over 1 GiB and replayed from one HIP graph,
-      timed like the decode step;
+      timed like the decode step; read_gate_size: the same at the 18944 x 4096
+      projection's bytes (a lone launch of that size);
       both reads with plain and with non-temporal loads (the policy of the
       decode kernels' code loads), the faster one reported, the plain one beside;
     - copy_512MiB: a 512 MiB -> 512 MiB copy (reads plus writes);
@@ -986,30 +987,37 @@ def measure_ceilings(tl, layer_bytes, steps):
                         "plain_GBps": round(best[False][0], 1),
                         "frac": round(best[nt][0] / HBM_PEAK_GBPS, 4)}
 
-    chunk = layer_bytes // 16 * 4               # int32 elements, 16-byte multiple
-    nchunk = big.numel() // chunk
-    views = [big[i * chunk:(i + 1) * chunk] for i in range(nchunk)]
-    best = {}
-    for nt in (False, True):
-        best[nt] = (0.0, None)
-        for wg in (512, 1024, 2048):
-            tl.probe_read(views[0], sink, wg, nontemporal=nt)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(steps):
-                    tl.probe_read(views[i % nchunk], sink, wg, nontemporal=nt)
-            settle(g.replay)
-            t = ev_time(lambda r: g.replay(), 1) / steps
-            del g
-            best[nt] = max(best[nt], (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
-    nt = best[True][0] > best[False][0]
-    out["read_layer_size"] = {"GBps": round(best[nt][0], 1), "workgroups": best[nt][1],
-                              "loads": "non-temporal" if nt else "plain",
-                              "plain_GBps": round(best[False][0], 1),
-                              "bytes": chunk * 4, "us": round(chunk * 4 / best[nt][0] / 1e3, 3),
-                              "frac": round(best[nt][0] / HBM_PEAK_GBPS, 4)}
-    del views
+    def graph_read(nbytes):
+        """Best streaming read of `nbytes` per launch, `steps` launches rotating
+        over 1 GiB in one HIP graph, plain and non-temporal loads."""
+        chunk = nbytes // 16 * 4               # int32 elements, 16-byte multiple
+        nchunk = big.numel() // chunk
+        views = [big[i * chunk:(i + 1) * chunk] for i in range(nchunk)]
+        best = {}
+        for nt in (False, True):
+            best[nt] = (0.0, None)
+            for wg in (512, 1024, 2048):
+                tl.probe_read(views[0], sink, wg, nontemporal=nt)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(steps):
+                        tl.probe_read(views[i % nchunk], sink, wg, nontemporal=nt)
+                settle(g.replay)
+                t = ev_time(lambda r: g.replay(), 1) / steps
+                del g
+                best[nt] = max(best[nt], (chunk * 4 / t / 1e9, wg), key=lambda b: b[0])
+        nt = best[True][0] > best[False][0]
+        return {"GBps": round(best[nt][0], 1), "workgroups": best[nt][1],
+                "loads": "non-temporal" if nt else "plain",
+                "plain_GBps": round(best[False][0], 1),
+                "bytes": chunk * 4, "us": round(chunk * 4 / best[nt][0] / 1e3, 3),
+                "frac": round(best[nt][0] / HBM_PEAK_GBPS, 4)}
+
+    out["read_layer_size"] = graph_read(layer_bytes)
+    # the 18944 x 4096 projection's bytes at one token: the ceiling of a lone
+    # launch of that size, which pays the ramp-up and drain once per launch
+    out["read_gate_size"] = graph_read(alg_bytes(18944, 4096, 1, -1))
 
     half = big.numel() // 2
     src, dst = big[:half], big[half:]
@@ -1221,6 +1229,9 @@ def main():
     pack = bench_pack(tl)
     log(f"[bench] pack {pack}")
     ceilings = measure_ceilings(tl, step_bytes, min(args.steps, 200))
+    for sh in shapes_out.values():  # lone launches of the gate shape against its read
+        if (sh["N"], sh["K"]) == (18944, 4096):
+            sh["frac_of_measured_read"] = round(ceilings["read_gate_size"]["us"] / sh["us"], 4)
     log(f"[bench] ceilings {ceilings}")
     roofline["frac_of_measured_read"] = round(
         achieved / ceilings["read_layer_size"]["GBps"], 4)
