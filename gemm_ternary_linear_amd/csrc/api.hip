@@ -298,7 +298,7 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
         // split-K partials go to the library's static scratch (one launch
         // after another on the stream): check its size before anything is
         // enqueued
-        size_t need = ng ? gemm_batch_scratch_need(grouped_gemm, ng) : 0;
+        size_t need = ng ? gemm_batch_scratch_need(grouped_gemm, ng, noalloc_scratch_bytes()) : 0;
         for (int l = 0; l < nfl; ++l)
             need = std::max(need, gemm_few_scratch_need(few, few_order + few_first[l],
                                                         few_first[l + 1] - few_first[l]));

@@ -17,6 +17,7 @@
 // Rows are padded to 72 elements (144 bytes) so the 16 rows a fragment read
 // touches fall on distinct LDS banks.
 #include <algorithm>
+#include <cstdint>
 #include <type_traits>
 
 #include "common.h"
@@ -785,7 +786,7 @@ int big_ksplit(int tiles, int K, int ns, int tile_elems)
 // big_ksplit() says.
 template <class C>
 size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order, int *tiles,
-                     int *ks)
+                     int *ks, size_t cap = SIZE_MAX)
 {
     int64_t total = 0;
     for (int i = 0; i < count; ++i) {
@@ -811,12 +812,18 @@ size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order
     for (int i = 0; i < count; ++i)
         work += (int64_t)tiles[i] * args[idx[i]].K;
     const int64_t share = std::max<int64_t>(1, work / ((int64_t)device_cus() * C::OCC));
-    size_t ws_bytes = 0;
+    // The balanced slices are a speed-up, not a need: when their partial
+    // tiles would not fit in `cap` (the fixed scratch of the allocation-free
+    // call), the launch runs without them.
+    bool balance = true;
+    size_t ws_bytes;
+again:
+    ws_bytes = 0;
     for (int i = 0; i < count; ++i) {
         const int K = args[idx[i]].K;
         if (total < device_cus()) {
             ks[i] = big_ksplit(tiles[i], K, C::NS, C::TN * C::TM);
-        } else if (count > 1 && K >= 2 * share) {
+        } else if (balance && count > 1 && K >= 2 * share) {
             const int rounds = K / (dma::TK * C::NS);
             ks[i] = (int)std::min<int64_t>((K + share - 1) / share, rounds / 2);
             while (ks[i] > 1 && (int64_t)tiles[i] * ks[i] * C::TN * C::TM * 4 > (int64_t(1) << 31))
@@ -827,6 +834,10 @@ size_t plan_big_mode(const GemvArgs *args, const int *idx, int count, int *order
         }
         if (ks[i] > 1)
             ws_bytes += (size_t)tiles[i] * ks[i] * C::TN * C::TM * 4;
+    }
+    if (balance && total >= device_cus() && ws_bytes > cap) {
+        balance = false;
+        goto again;
     }
     return ws_bytes;
 }
@@ -841,7 +852,8 @@ hipError_t launch_big_mode(const GemvArgs *args, const int *idx, int count, hipS
                            const FixedScratch *fixed)
 {
     int order[kGemvMaxBatch], tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
-    const size_t ws_bytes = plan_big_mode<C>(args, idx, count, order, tiles, ks);
+    const size_t ws_bytes =
+        plan_big_mode<C>(args, idx, count, order, tiles, ks, fixed ? fixed->bytes : SIZE_MAX);
     char *ws = nullptr;
     if (ws_bytes) {
         if (fixed) {
@@ -946,23 +958,24 @@ hipError_t launch_gemm_big_batch(const GemvArgs *args, int count, hipStream_t st
     return e;
 }
 
-size_t gemm_batch_scratch_need(const GemvArgs *args, int count)
+size_t gemm_batch_scratch_need(const GemvArgs *args, int count, size_t cap)
 {
     // the launches of one call run in stream order and reuse the buffer from
-    // its start: the need is the largest single launch's
+    // its start: the need is the largest single launch's (planned as the
+    // launch will be planned with a fixed scratch of `cap` bytes)
     const BigClasses cl(args, count);
     int order[kGemvMaxBatch], tiles[kGemvMaxBatch], ks[kGemvMaxBatch];
     size_t need = 0;
     for (int mode = 0; mode < 4; ++mode) {
         const int *n = cl.n[mode];
         if (n[0])
-            need = std::max(need, plan_big_mode<TinyCfg>(args, cl.idx[mode][0], n[0], order, tiles, ks));
+            need = std::max(need, plan_big_mode<TinyCfg>(args, cl.idx[mode][0], n[0], order, tiles, ks, cap));
         if (n[1])
-            need = std::max(need, plan_big_mode<SmallCfg>(args, cl.idx[mode][1], n[1], order, tiles, ks));
+            need = std::max(need, plan_big_mode<SmallCfg>(args, cl.idx[mode][1], n[1], order, tiles, ks, cap));
         if (n[2])
-            need = std::max(need, plan_big_mode<MidCfg>(args, cl.idx[mode][2], n[2], order, tiles, ks));
+            need = std::max(need, plan_big_mode<MidCfg>(args, cl.idx[mode][2], n[2], order, tiles, ks, cap));
         if (n[3] && mode == 0)
-            need = std::max(need, plan_big_mode<BigCfg>(args, cl.idx[mode][3], n[3], order, tiles, ks));
+            need = std::max(need, plan_big_mode<BigCfg>(args, cl.idx[mode][3], n[3], order, tiles, ks, cap));
     }
     return need;
 }

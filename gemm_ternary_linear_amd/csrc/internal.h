@@ -135,8 +135,10 @@ struct FixedScratch {
 // gemm_batch_scratch_need() bytes), else to the stream's workspace.
 hipError_t launch_gemm_batch(const GemvArgs *args, int count, bool fp16, hipStream_t stream,
                              const FixedScratch *fixed = nullptr, bool zero_skip = false);
-// Scratch bytes launch_gemm_batch needs for these problems (0: no K split).
-size_t gemm_batch_scratch_need(const GemvArgs *args, int count);
+// Scratch bytes launch_gemm_batch needs for these problems (0: no K split)
+// when its fixed scratch holds `cap` bytes (work-balanced K slices that would
+// not fit are left out).
+size_t gemm_batch_scratch_need(const GemvArgs *args, int count, size_t cap);
 
 // Library-owned scratch of at least `bytes` for work on `stream` of the
 // current device.  While `stream` is being captured nothing is allocated: a

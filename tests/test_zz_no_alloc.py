@@ -4,9 +4,10 @@ within the stated bound of the oracle, |y - y_ref| <= 1e-3 * sum_k |x_k| s + 1e-
 
 Two calls in a row, the second smaller (the static scratch keeps the first
 call's partials; the second must not depend on them), a batch mixing decode,
-few-token (K-sliced) and prefill problems, a batch whose split-K partials exceed the static buffer
-(rejected with nothing enqueued), and a capture on a stream that never ran the
-call (the allocation-free call needs no warm-up).
+few-token (K-sliced) and prefill problems, a grouped launch with a work-balanced
+K split, a batch whose split-K partials exceed the static buffer (rejected
+with nothing enqueued), and a capture on a stream that never ran the call (the
+allocation-free call needs no warm-up).
 """
 
 import ctypes
@@ -102,6 +103,15 @@ def test_noalloc_mixed_batch(tl):
     specs = [(1, 4096, 4096, -1), (1, 512, 4096, -1), (256, 300, 2048, 128), (100, 200, 1152, 128),
              (300, 260, 1024, -1), (16, 640, 4096, -1), (12, 320, 8192, 128)]
     _check(tl, _problems(specs, 3), "mixed")
+
+
+def test_noalloc_balanced_split(tl):
+    # the 7B-shaped layer at 32 tokens: one grouped launch whose down
+    # projection's K range is sliced for balance (2.6 MB of partials, within
+    # the static buffer): the same plan and bits as the allocating call
+    say("noalloc: grouped launch with a work-balanced K split")
+    specs = [(32, s.N, s.K, -1) for s in synth.CONFIGS[2].shapes]
+    _check(tl, _problems(specs, 6), "balanced")
 
 
 def test_noalloc_rejects_oversize(tl):
