@@ -46,7 +46,9 @@
  *     caller memory.
  *   - The library owns one device workspace per (device, stream) for GEMM
  *     shapes whose K range it splits over several workgroups (fp32 partial
- *     tiles, added in a fixed order by a second kernel).  The first call on a
+ *     tiles, added in a fixed order by a second kernel): shapes with few
+ *     output tiles, few-token shapes with long K, and batches in which one
+ *     problem's K is much longer than the others'.  The first call on a
  *     stream that needs a larger one allocates it (hipMalloc); the one it
  *     replaces stays allocated (a graph captured earlier may use it) until
  *     ternary_shutdown(), which frees them all.  Under stream capture nothing
