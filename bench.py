@@ -924,8 +924,8 @@ def summarize_workload(name: str, dirs) -> None:
                 pb = mean(mprobe["SQ_VALU_MFMA_BUSY_CYCLES"]) / mean(mprobe["GRBM_GUI_ACTIVE"])
                 row.append(f"mfma_busy_vs_probe {busy / pb:.3f}")
         lines.append("  ".join(row))
-    fam = ("gemv_f4" if M == 1 else "gemv_stream" if M <= 8 else "gemm_few" if M <= 16
-           else "gemm_dma")
+    fam = ("gemv_f4" if M == 1 else "gemv_stream" if M <= 8
+           else "gemm_few" if M <= (16 if g == 128 else 32) else "gemm_dma")
     path = ROOT / "profiles" / f"{fam}_{name}_counters.txt"
     path.parent.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")

@@ -91,8 +91,8 @@ int check_linear(const void *x, int dtype, int64_t M, int64_t N, int64_t K, cons
 }
 
 // Whether the automatic choice gives a problem to the few-token GEMM: the
-// token counts just past the decode GEMV (9 .. 16), where it runs every
-// measured shape faster than the GEMM.
+// token counts just past the decode GEMV (9 .. 32, groups of 128 up to 16),
+// where it runs every measured shape faster than the GEMM.
 bool few_preferred(int64_t M, int64_t N, int64_t K, int group, const void *scale)
 {
     return M > ternary::kGemvMaxM && ternary::gemm_few_takes(M, N, K, group, scale);
@@ -276,14 +276,16 @@ int linear_batch(const ternary_problem *problems, int count, int dtype, hipStrea
         else
             others[no++] = i;
     }
-    // Few-token problems: one launch per scale mode, longest K first.
+    // Few-token problems: one launch per scale mode and token tile, longest K
+    // first.
     int few_order[TERNARY_MAX_BATCH], few_first[TERNARY_MAX_BATCH + 1], nfl = 0;
     {
         int n = 0;
-        for (const int group : {0, 128, 256}) {
+        for (const int group : {0, 128, 256})
+        for (const int tile : {8, 16, 32}) {
             const int first = n;
             for (int i = 0; i < nw; ++i)
-                if (few[i].group == group)
+                if (few[i].group == group && few_tile(few[i].M) == tile)
                     few_order[n++] = i;
             for (int i = first + 1; i < n; ++i)  // stable insertion sort, K descending
                 for (int j = i; j > first && few[few_order[j]].K > few[few_order[j - 1]].K; --j)

@@ -1,4 +1,4 @@
-// Few-token streaming GEMM (1 <= M <= 16) for the ternary linear layer on gfx950.
+// Few-token streaming GEMM (1 <= M <= 32) for the ternary linear layer on gfx950.
 //
 // The layer y = x @ (unpack(q) * s)^T ([xxqk] m.xxqk.cn/news/593501 §4.3) at a
 // handful of tokens still reads every packed weight byte once and does
@@ -24,7 +24,9 @@
 //    Each 1-KB DMA fills two token rows, every lane fetching the logical
 //    chunk of its physical slot; tokens past M and slabs past K read zeros.
 //  * MFMA: v_mfma_f32_16x16x32_{bf16,f16}, rows = channels, columns =
-//    tokens.  Lane group g of the A operand holds codes 64g .. 64g+63 of the
+//    tokens (a 32-token tile runs two MFMAs per decoded A operand, one per
+//    16-token half; groups of 128 need two columns per token, so they stop
+//    at 16 tokens).  Lane group g of the A operand holds codes 64g .. 64g+63 of the
 //    slab (its 16-byte load), decoded to 16-bit +-2 / 0 (decode16); MFMA i
 //    takes codes 64g + 8i .. 64g + 8i + 7 from every lane group, and the B
 //    read of lane group g takes the same K positions of x (logical chunk
@@ -122,7 +124,7 @@ __device__ __forceinline__ void wait_vm()
 }
 
 // GM: 0 per-channel scales, 1 groups of 256, 2 groups of 128.  MT: tokens of
-// the tile (8 or 16).  KP: K parts (the workgroup's waves are RB = 8 / KP row
+// the tile (8, 16 or 32).  KP: K parts (the workgroup's waves are RB = 8 / KP row
 // groups x KP parts).  FN: 16-channel blocks per wave (each B read of x feeds
 // FN MFMAs), so a workgroup holds RB * FN blocks.  CP: the cache policy of the
 // code loads (kStreamLoad when every problem holds tiled codes).
@@ -132,12 +134,14 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     constexpr int RB = kWaves / KP;
     constexpr int GC = GM == 2 ? 2 : 1;               // B columns per token
     constexpr int CF = MT * GC > 16 ? 2 : 1;          // 16-column B fragments
+    constexpr int TH = GC == 1 ? CF : 1;              // 16-token halves of the tile
     constexpr int XI = KP * MT / 2;                   // 1-KB x DMAs per stage
     constexpr int XW = (XI + kWaves - 1) / kWaves;    // x DMAs per wave and stage
     constexpr int ZC = KP * MT * 32;                  // chunk index of a stage's zero area
     constexpr int SU4 = ZC + 64;                      // stage: x chunks + 1 KB of zeros
     constexpr int NSC = GM == 0 ? 0 : 4;              // scale loads per block and slab
-    static_assert(MT == 8 || MT == 16, "tile tokens");
+    static_assert(MT == 8 || MT == 16 || MT == 32, "tile tokens");
+    static_assert(MT <= 16 || GC == 1, "32-token tiles take one B column per token");
     static_assert(KP == 1 || KP == 2 || KP == 4, "parts");
     static_assert(FN == 1 || FN == 2 || FN == 4, "blocks per wave");
     static_assert(KP * MT <= 32, "stage size");
@@ -215,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     for (int c = 0; c < CF; ++c) {
         int t, p;
         if constexpr (GC == 1) {
-            t = col;
+            t = 16 * c + col;  // fragment c: tokens 16c .. 16c + 15
             p = 0;
         } else if constexpr (MT == 16) {
             t = col;
@@ -276,11 +280,14 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    f32x4_t acc[FN], tot[FN];  // per channel: running sums; groups: scaled sums
+    // per channel: running sums; groups: scaled sums; per 16-token half
+    f32x4_t acc[FN][TH], tot[FN][TH];
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int f = 0; f < FN; ++f)
-        acc[f] = tot[f] = zero4;
+#pragma unroll
+        for (int th = 0; th < TH; ++th)
+            acc[f][th] = tot[f][th] = zero4;
 
     // Vector memory ops issued after this wave's last code load of slab j
     // when step j starts: slab j's scale loads, then the x DMAs, code and
@@ -305,7 +312,7 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int c = 0; c < CF; ++c)
-                part[f][c] = GM == 0 ? acc[f] : zero4;
+                part[f][c] = GM == 0 ? acc[f][c] : zero4;  // per channel: GC == 1, TH == CF
         const lds_u4 *stg = ls[s];
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {  // code word wd: MFMAs 2 wd, 2 wd + 1
@@ -332,7 +339,9 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
             if constexpr (GM == 0) {
-                acc[f] = part[f][0];
+#pragma unroll
+                for (int c = 0; c < CF; ++c)
+                    acc[f][c] = part[f][c];
             } else {
 #pragma unroll
                 for (int c = 0; c < CF; ++c)
@@ -345,7 +354,7 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
                             h = c ? sc[s][f][r] >> 16 : sc[s][f][r];
                         else
                             h = (col >> 3) ? sc[s][f][r] >> 16 : sc[s][f][r];
-                        tot[f][r] += f16_bits_to_f32((uint16_t)h) * part[f][c][r];
+                        tot[f][GC == 1 ? c : 0][r] += f16_bits_to_f32((uint16_t)h) * part[f][c][r];
                     }
             }
         }
@@ -368,8 +377,9 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     wait_vm<0>();
 
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-        f32x4_t res = GM == 0 ? acc[f] : tot[f];
+    for (int ft = 0; ft < FN * TH; ++ft) {
+        const int f = ft / TH, th = ft % TH;
+        f32x4_t res = GM == 0 ? acc[f][th] : tot[f][th];
         if constexpr (GC == 2 && MT == 8) {
             // columns t and t + 8 hold token t's two groups
 #pragma unroll
@@ -393,8 +403,8 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
                 }
             }
         }
-        // Epilogue: lane holds channels 16 blk + 4 g + r of token column col.
-        const int t = col;
+        // Epilogue: lane holds channels 16 blk + 4 g + r of token 16 th + col.
+        const int t = 16 * th + col;
         if (kp != 0 || t >= M || t >= MT || 4 * g >= nrows[f])
             continue;
         const int n = 16 * (blk0 + f) + 4 * g;
@@ -528,10 +538,12 @@ hipError_t launch_kp(int kp, unsigned grid, hipStream_t stream, const FewBatch &
 {
     if (kp == 1)
         return launch_inst<FP16, GM, MT, 1, CP>(grid, stream, b);
-    if (kp == 2)
-        return launch_inst<FP16, GM, MT, 2, CP>(grid, stream, b);
+    if constexpr (MT * 2 <= 32)
+        if (kp == 2)
+            return launch_inst<FP16, GM, MT, 2, CP>(grid, stream, b);
     if constexpr (MT * 4 <= 32)
-        return launch_inst<FP16, GM, MT, 4, CP>(grid, stream, b);
+        if (kp == 4)
+            return launch_inst<FP16, GM, MT, 4, CP>(grid, stream, b);
     return hipErrorInvalidValue;
 }
 
@@ -539,13 +551,16 @@ template <bool FP16, int CP>
 hipError_t launch_mode(int gm, int mt, int kp, unsigned grid, hipStream_t stream,
                        const FewBatch &b)
 {
-    switch (gm * 2 + (mt == 16 ? 1 : 0)) {
+    switch (gm * 3 + (mt == 32 ? 2 : mt == 16 ? 1 : 0)) {
     case 0: return launch_kp<FP16, 0, 8, CP>(kp, grid, stream, b);
     case 1: return launch_kp<FP16, 0, 16, CP>(kp, grid, stream, b);
-    case 2: return launch_kp<FP16, 1, 8, CP>(kp, grid, stream, b);
-    case 3: return launch_kp<FP16, 1, 16, CP>(kp, grid, stream, b);
-    case 4: return launch_kp<FP16, 2, 8, CP>(kp, grid, stream, b);
-    default: return launch_kp<FP16, 2, 16, CP>(kp, grid, stream, b);
+    case 2: return launch_kp<FP16, 0, 32, CP>(kp, grid, stream, b);
+    case 3: return launch_kp<FP16, 1, 8, CP>(kp, grid, stream, b);
+    case 4: return launch_kp<FP16, 1, 16, CP>(kp, grid, stream, b);
+    case 5: return launch_kp<FP16, 1, 32, CP>(kp, grid, stream, b);
+    case 6: return launch_kp<FP16, 2, 8, CP>(kp, grid, stream, b);
+    case 7: return launch_kp<FP16, 2, 16, CP>(kp, grid, stream, b);
+    default: return hipErrorInvalidValue;  // groups of 128 take at most 16 tokens
     }
 }
 
@@ -565,7 +580,10 @@ hipError_t launch_policy(int gm, int mt, int kp, unsigned grid, hipStream_t stre
 
 bool gemm_few_takes(int64_t M, int64_t N, int64_t K, int group, const void *scale)
 {
-    return M >= 1 && M <= kFewMaxM && N >= 1 && K >= 256 && K % 256 == 0 && K <= kGemvMaxK &&
+    // 32-token tiles take one B column per token: per-channel scales and
+    // groups of 256; groups of 128 (two columns per token) stop at 16
+    return M >= 1 && M <= (group == 128 ? 16 : kFewMaxM) && N >= 1 && K >= 256 &&
+           K % 256 == 0 && K <= kGemvMaxK &&
            (group == 0 || group == 256 || (group == 128 && ((uintptr_t)scale & 3) == 0));
 }
 
@@ -597,7 +615,7 @@ hipError_t plan_few(const GemvArgs *args, const int *order, int count, FewPlan &
         const GemvArgs &a = args[order[oi]];
         if (!gemm_few_takes(a.M, a.N, a.K, a.group, a.scale))
             return hipErrorInvalidValue;
-        const int t = a.M <= 8 ? 8 : 16;
+        const int t = few_tile(a.M);
         if ((pl.group >= 0 && a.group != pl.group) || (pl.mt && t != pl.mt))
             return hipErrorInvalidValue;
         pl.group = a.group;

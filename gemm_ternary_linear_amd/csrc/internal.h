@@ -98,12 +98,13 @@ hipError_t launch_gemv_f4(const GemvArgs *args, const int *order, int count, boo
 // codes.
 bool gemv_valu_takes(int64_t M, int64_t K, int group, bool tiled);
 hipError_t launch_gemv_valu(const GemvArgs &a, bool fp16, hipStream_t stream);
-// Few-token streaming GEMM (gemm_few.hip): 1 <= M <= kFewMaxM, K % 256 == 0,
-// K <= kGemvMaxK, per-channel scales or groups of 128 (4-byte aligned scale
-// array) or 256; row-major and tiled codes.  One launch for up to
-// kGemvMaxBatch problems that share the scale mode and the token tile (M <= 8
-// or 8 < M <= 16).
-constexpr int kFewMaxM = 16;
+// Few-token streaming GEMM (gemm_few.hip): 1 <= M <= kFewMaxM (16 for groups
+// of 128), K % 256 == 0, K <= kGemvMaxK, per-channel scales or groups of 128
+// (4-byte aligned scale array) or 256; row-major and tiled codes.  One launch
+// for up to kGemvMaxBatch problems that share the scale mode and the token
+// tile (few_tile(M): 8, 16 or 32 tokens).
+constexpr int kFewMaxM = 32;
+inline int few_tile(int64_t M) { return M <= 8 ? 8 : (M <= 16 ? 16 : 32); }
 bool gemm_few_takes(int64_t M, int64_t N, int64_t K, int group, const void *scale);
 struct FixedScratch;
 // K ranges long against the launch's other problems, or launches with few

@@ -116,8 +116,9 @@ typedef enum {
                                   channel or groups of 64/128/256, row-major codes
                                   only.  Never chosen by AUTO (measured slower); kept
                                   for comparison                                        */
-    TERNARY_PATH_FEW = 7,      /* few-token streaming GEMM: 1 <= M <= 16, K % 256 == 0,
-                                  K <= 65536, per channel or groups of 128 / 256; x
+    TERNARY_PATH_FEW = 7,      /* few-token streaming GEMM: 1 <= M <= 32 (16 for groups
+                                  of 128), K % 256 == 0, K <= 65536, per channel or
+                                  groups of 128 / 256; x
                                   shared in LDS by the eight 16-channel blocks of a
                                   workgroup, codes streamed into registers             */
     TERNARY_PATH_GEMM_ZSKIP = 8 /* the pipelined GEMM skipping all-zero code blocks
@@ -212,8 +213,8 @@ int ternary_quantize(const void *w, int dtype, int64_t N, int64_t K, int64_t gro
  * non-finite inputs are unspecified) and |x| < 2^126.
  * Path choice: M <= ternary_gemv_max_m() runs the decode GEMV (the fp4 x fp8
  * kernel at M == 1 except for N < 8192 with K > 8192, the 16-bit one otherwise, each where
- * it takes the shape); 9 <= M <= 16 the few-token GEMM (TERNARY_PATH_FEW) where it takes
- * the shape; larger M and the rest the MFMA GEMM; shapes no fast kernel
+ * it takes the shape); 9 <= M <= 32 the few-token GEMM (TERNARY_PATH_FEW) where it takes
+ * the shape (groups of 128: M <= 16); larger M and the rest the MFMA GEMM; shapes no fast kernel
  * takes (K % 128 != 0) run the plain kernel.  The GEMV gives each token 2
  * MFMA columns (per channel, groups of 128 or 256), 4 (groups of 64) or 8
  * (groups of 32) of 16, so it takes M <= 4 for groups of 64 and 32 (M <= 2

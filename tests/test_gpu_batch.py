@@ -84,11 +84,14 @@ def test_batch_mixed(tl, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_batch_few_token_mixed(tl, dtype):
-    # 9 .. 16 tokens in one batch: two scale modes (two few-token launches),
-    # a K-sliced problem, a group size the few-token GEMM does not take (GEMM)
+    # 9 .. 32 tokens in one batch: three scale modes and two token tiles
+    # (16 and 32: one few-token launch per pair present), a K-sliced problem, a group
+    # size the few-token GEMM does not take and groups of 128 past 16 tokens
+    # (GEMM)
     say(f"few-token batch {dtype}")
     specs = [(16, 640, 4096, -1), (12, 320, 8192, 128), (9, 1000, 1024, 128),
-             (16, 130, 2304, -1), (10, 200, 1024, 64), (16, 48, 512, 256)]
+             (10, 200, 1024, 64), (24, 300, 2048, -1), (17, 520, 6144, -1),
+             (32, 130, 4352, 256), (20, 100, 1024, 128)]
     _run_and_check(tl, _problems(np.random.default_rng(45), specs, dtype), dtype=dtype)
 
 

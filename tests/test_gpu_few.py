@@ -1,10 +1,10 @@
 """The few-token streaming GEMM (TERNARY_PATH_FEW) against the oracle.
 
-The kernel serves 1 <= M <= 16 with x shared in LDS by the eight 16-channel
+The kernel serves 1 <= M <= 32 with x shared in LDS by the eight 16-channel
 blocks of a workgroup ([xxqk] m.xxqk.cn/news/593501 §4.3 for the layer); it is
 held to the layer's bound |y - y_ref| <= 1e-3 * sum_k |x_k| s(n,k) + 1e-6 on
 every output it writes, on row-major and tiled codes, with the same bits on
-both layouts.  Shapes cover 8- and 16-token tiles, ragged channel blocks,
+both layouts.  Shapes cover 8-, 16- and 32-token tiles, ragged channel blocks,
 parts of unequal length, every K-part count (1, 2, 4) and the three scale
 modes it takes (per channel, groups of 128 and 256).
 """
@@ -65,6 +65,13 @@ CASES = [
     (16, 1024, 5120, 128, "bf16"),
     (16, 96, 1024, -1, "fp16"),
     (16, 50, 7936, 256, "bf16"),
+    # 32-token tiles (one K part; per channel and groups of 256): ragged M
+    # and N, a K long enough to slice over workgroups
+    (17, 300, 2048, -1, "bf16"),
+    (24, 130, 4096, 256, "fp16"),
+    (31, 1000, 1024, -1, "fp16"),
+    (32, 64, 18944, -1, "bf16"),
+    (32, 520, 5120, 256, "bf16"),
 ]
 
 

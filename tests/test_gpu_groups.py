@@ -117,9 +117,11 @@ BIG = [(16, 300, 2048, 64), (16, 300, 2048, 256), (64, 257, 1536, 64), (64, 257,
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("M,N,K,g", BIG)
 def test_groups_pipelined_gemm(tl, M, N, K, g, dtype):
-    # the GEMM forced (at 16 tokens the automatic path takes the few-token
-    # GEMM for groups of 256, which tests/test_gpu_few.py covers)
-    auto = "few" if M <= 16 and g in (128, 256) and K % 256 == 0 else "gemm"
+    # the GEMM forced (up to 16 tokens for groups of 128, 32 for groups of
+    # 256, the automatic path takes the few-token GEMM, which
+    # tests/test_gpu_few.py covers)
+    few_m = {128: 16, 256: 32}.get(g, 0)
+    auto = "few" if M <= few_m and K % 256 == 0 else "gemm"
     assert tl.select_path(M, N, K, g) == auto
     _check(tl, M, N, K, g, dtype, path="gemm", tag="big")
 
