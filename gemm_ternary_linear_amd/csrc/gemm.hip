@@ -316,12 +316,22 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     constexpr bool GROUPED = GS != 0;
     constexpr int SPG = GROUPED ? GS / TK : 1;  // K steps per group
     constexpr int GSH = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);
-    // Group scales: every stage also carries one dword per channel, the
-    // scales of the pair of groups its K step belongs to.
+    // Group scales: a channel's dword holds the scales of a pair of groups
+    // (2 SPG K steps).  The workgroup gathers it once per LS steps (the
+    // pair's steps, at most one round of NS) into one of NB buffers of the
+    // round's parity, the buffer of the step's position in the round; the
+    // stages in between issue, in its place, a DMA that reads past the
+    // resource (no memory access) into a buffer that is never read, so every
+    // stage still issues the same number of DMAs.  Rounds alternate between
+    // the two parities, so a gather into the next round's buffer never
+    // overwrites scales that the current round still reads.
     static_assert(!GROUPED || (C::TN == THREADS && NS % 4 == 0 && (GS == 64 || GS == 128 ||
                                                                    GS == 256)),
                   "one scale dword per thread; groups of 1, 2 or 4 steps");
     constexpr int VPS = C::VPS + (GROUPED ? 1 : 0);  // vector memory ops per thread and stage
+    constexpr int LS = !GROUPED ? NS : (2 * SPG < NS ? 2 * SPG : NS);  // steps per scale gather
+    constexpr int NB = NS / LS;  // scale buffers per round parity
+    static_assert(NS % LS == 0 && NB <= 4, "scale gathers per round");
     // One LDS object per stage: the compiler then knows that a DMA into one
     // stage does not write the stage being read and waits for nothing there.
     constexpr int XS = C::XSTAGE, WS = C::WSTAGE, SS = GROUPED ? C::TN : 1;
@@ -331,14 +341,18 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         name##6[NS > 6 ? n : 1], name##7[NS > 7 ? n : 1]
     TERNARY_STAGES(uint4, sx, XS);
     TERNARY_STAGES(uint32_t, sw, WS);
-    TERNARY_STAGES(uint32_t, sc, SS);
 #undef TERNARY_STAGES
+    __shared__ __attribute__((aligned(16))) uint32_t sc00[SS], sc01[NB > 1 ? SS : 1],
+        sc02[NB > 2 ? SS : 1], sc03[NB > 3 ? SS : 1], sc10[SS], sc11[NB > 1 ? SS : 1],
+        sc12[NB > 2 ? SS : 1], sc13[NB > 3 ? SS : 1], scx[SS];
     lds_u4 *const lx[8] = {(lds_u4 *)sx0, (lds_u4 *)sx1, (lds_u4 *)sx2, (lds_u4 *)sx3,
                            (lds_u4 *)sx4, (lds_u4 *)sx5, (lds_u4 *)sx6, (lds_u4 *)sx7};
     lds_u32 *const lw[8] = {(lds_u32 *)sw0, (lds_u32 *)sw1, (lds_u32 *)sw2, (lds_u32 *)sw3,
                             (lds_u32 *)sw4, (lds_u32 *)sw5, (lds_u32 *)sw6, (lds_u32 *)sw7};
-    lds_u32 *const lsc[8] = {(lds_u32 *)sc0, (lds_u32 *)sc1, (lds_u32 *)sc2, (lds_u32 *)sc3,
-                             (lds_u32 *)sc4, (lds_u32 *)sc5, (lds_u32 *)sc6, (lds_u32 *)sc7};
+    lds_u32 *const lsc[2][4] = {
+        {(lds_u32 *)sc00, (lds_u32 *)sc01, (lds_u32 *)sc02, (lds_u32 *)sc03},
+        {(lds_u32 *)sc10, (lds_u32 *)sc11, (lds_u32 *)sc12, (lds_u32 *)sc13}};
+    lds_u32 *const lscx = (lds_u32 *)scx;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -442,9 +456,9 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 
     // Every step issues the same number of DMAs, so that one vmcnt value
     // is right everywhere: steps past the end reload the last K step into a
-    // stage that is never read again.
-    auto issue = [&](auto S, int kt) {
-        constexpr int s = decltype(S)::value;
+    // stage that is never read again.  P: the parity of step kt's round.
+    auto issue = [&](auto S, auto P, int kt) {
+        constexpr int s = decltype(S)::value, p = decltype(P)::value;
         const int kc = kbase + (kt < nk ? kt : nk - 1);
 #pragma unroll
         for (int i = 0; i < C::XI; ++i)
@@ -452,8 +466,13 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
         for (int i = 0; i < C::WI; ++i)
             dma_to_lds<4>(wr, (void *)(lw[s] + i * THREADS + wave_chunk), woff[i], kc * wstep);
-        if constexpr (GROUPED)  // the dword holding group kc / SPG
-            dma_to_lds<4>(sr, (void *)(lsc[s] + wave_chunk), soff, ((kc >> GSH) >> 1) * 4);
+        if constexpr (GROUPED) {
+            if constexpr (s % LS == 0)  // the dword holding group kc / SPG
+                dma_to_lds<4>(sr, (void *)(lsc[p][s / LS] + wave_chunk), soff,
+                              ((kc >> GSH) >> 1) * 4);
+            else
+                dma_to_lds<4>(sr, (void *)(lscx + wave_chunk), kOOB, 0);
+        }
     };
 
     f32x4_t acc[FN][FM];
@@ -474,8 +493,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
     const int xa1 = xa0 ^ 1;
     const int wa = (wn * FN * 16 + fr) * 4 + g;
 
-    auto compute = [&](auto S, int kt) {
-        constexpr int s = decltype(S)::value;
+    auto compute = [&](auto S, auto P, int kt) {
+        constexpr int s = decltype(S)::value, p = decltype(P)::value;
         uint32_t wv[FN];
 #pragma unroll
         for (int f = 0; f < FN; ++f)
@@ -521,7 +540,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
         if constexpr (GROUPED) {
             if constexpr (s % SPG == SPG - 1) {
                 // End of a group: fold its sums with the group's scales (low
-                // half of the stage's dwords for an even group, high half for
+                // half of the pair's dwords for an even group, high half for
                 // an odd one; known from s alone when NS spans two groups).
                 int odd;
                 if constexpr (NS % (2 * SPG) == 0)
@@ -531,7 +550,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     const u32x4_t w = *reinterpret_cast<const lds_u4 *>(
-                        lsc[s] + wn * FN * 16 + f * 16 + 4 * g);
+                        lsc[p][s / LS] + wn * FN * 16 + f * 16 + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float sc = f16_bits_to_f32((uint16_t)(odd ? w[r] >> 16 : w[r]));
@@ -546,25 +565,42 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) gemm_dma_kernel(const BigB
 
     // One K step: wait for this wave's DMA of stage kt, barrier (all waves'
     // DMA of stage kt landed, all waves done with stage kt-1), start the DMA
-    // of step kt+NS-1 into the stage kt-1 used, then compute stage kt.
-    auto step = [&](auto S, int kt) {
-        constexpr int s = decltype(S)::value;
+    // of step kt+NS-1 into the stage kt-1 used (the next round's, of the
+    // other parity, unless kt opens its round), then compute stage kt.
+    auto step = [&](auto S, auto P, int kt) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value, p = decltype(P)::value;
         wait_and_barrier<(NS - 2) * VPS>();
-        issue(std::integral_constant<int, (s + NS - 1) % NS>{}, kt + NS - 1);
-        compute(S, kt);
+        issue(std::integral_constant<int, (s + NS - 1) % NS>{},
+              std::integral_constant<int, s == 0 ? p : 1 - p>{}, kt + NS - 1);
+        compute(S, P, kt);
     };
+    auto round = [&](auto P, int kt) __attribute__((always_inline)) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (step(std::integral_constant<int, I>{}, P, kt + I), ...);
+        }(std::make_integer_sequence<int, NS>{});
+    };
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
 
-    // Prologue: stages 0 .. NS-2.
+    // Prologue: stages 0 .. NS-2 of round 0.
     [&]<int... I>(std::integer_sequence<int, I...>) {
-        (issue(std::integral_constant<int, I>{}, I), ...);
+        (issue(std::integral_constant<int, I>{}, Even{}, I), ...);
     }(std::make_integer_sequence<int, NS - 1>{});
 
     // K is a whole number of NS-step rounds (the host checks), so every
-    // stage index below is a constant.
-    for (int kt = 0; kt < nk; kt += NS) {
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-            (step(std::integral_constant<int, I>{}, kt + I), ...);
-        }(std::make_integer_sequence<int, NS>{});
+    // stage index below is a constant; group-scaled kernels run rounds in
+    // pairs so that the parity is one too.
+    if constexpr (GROUPED) {
+        int kt = 0;
+        for (; kt + 2 * NS <= nk; kt += 2 * NS) {
+            round(Even{}, kt);
+            round(Odd{}, kt + NS);
+        }
+        if (kt < nk)
+            round(Even{}, kt);
+    } else {
+        for (int kt = 0; kt < nk; kt += NS)
+            round(Even{}, kt);
     }
     // No DMA may still be writing LDS when the workgroup ends.
     wait_vm<0>();
