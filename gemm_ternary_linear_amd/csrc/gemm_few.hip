@@ -97,6 +97,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_u4 *lds, 
 #endif
 }
 
+// The same with 4 bytes per lane (LDS at lds + 4 * lane).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t *lds, int voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
+#endif
+}
+
 template <bool FP16>
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
 {
@@ -139,7 +148,6 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
     constexpr int XW = (XI + kWaves - 1) / kWaves;    // x DMAs per wave and stage
     constexpr int ZC = KP * MT * 32;                  // chunk index of a stage's zero area
     constexpr int SU4 = ZC + 64;                      // stage: x chunks + 1 KB of zeros
-    constexpr int NSC = GM == 0 ? 0 : 4;              // scale loads per block and slab
     static_assert(MT == 8 || MT == 16 || MT == 32, "tile tokens");
     static_assert(MT <= 16 || GC == 1, "32-token tiles take one B column per token");
     static_assert(KP == 1 || KP == 2 || KP == 4, "parts");
@@ -241,8 +249,17 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
 
     // ---- loads of slab j (x share, then codes and scales) ---------------
     u32x4_t w[kS][FN];
-    uint32_t sc[kS][FN][GM == 0 ? 1 : 4];
-    auto issue = [&](auto SL, int j) {
+    uint32_t sc[GM == 1 ? kS : 1][FN][4];  // groups of 256: per slot, C rows 4 g + r
+    // Groups of 128: per wave and block, a round's (kS slabs') scales (one
+    // dword: two groups) as [slab][row], DMA'd with the round's first slab
+    // and read into registers (sq, C rows 4 g + r) when the round starts;
+    // sq_shift: slabs by which the DMA started early (see issue()).
+    static_assert(GM != 2 || kS == 4, "a round's scales are four dwords per row");
+    constexpr int SQN = GM == 2 ? kWaves * FN * 64 : 1;
+    __shared__ __attribute__((aligned(16))) uint32_t sqs[SQN];
+    u32x4_t sq[GM == 2 ? FN : 1][4];
+    int sq_shift = 0;
+    auto issue = [&](auto SL, int j) __attribute__((always_inline)) {
         constexpr int s = decltype(SL)::value;
         const bool in = j < L;
 #pragma unroll
@@ -255,26 +272,38 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
         __builtin_amdgcn_sched_barrier(0);
         const int sl = s_lo + j;
         const bool live = in && sl < nslabs;
+        if constexpr (GM == 2 && s == 0) {
+            // The round's slabs sl .. sl+3, before the codes of slab sl (the
+            // wait for those covers it): lane l takes row l & 15's dword of
+            // slab l >> 4, one 256-byte DMA per block.  The start is held at
+            // most 4 slabs before the row's end (K >= 1024) so that no load
+            // leaves the block; rows past N read a real row's scales.
+            // (the last round's reads of the buffer are done)
+            __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));
+            const int lo = min(sl, nslabs - 4);
+            sq_shift = sl - lo;
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int row = min(col, nrows[f] - 1);
+                dma4(sr[f], sqs + (wave * FN + f) * 64, (row * ngroups + 2 * (lo + g)) * 2);
+            }
+        }
 #pragma unroll
         for (int f = 0; f < FN; ++f)
             w[s][f] = load_codes<CP>(wr[f], live ? woff[f] + sl * sstride : kOOB);
-        if constexpr (GM != 0) {
-            // Offsets clamped into the block instead of selected, so that no
-            // lane condition splits a load: rows past N and slabs past the
-            // part read scales that are never used (a dead block's empty
-            // resource reads zeros).
+        // Scale offsets are clamped into the block instead of selected, so
+        // that no lane condition splits a load: rows past N and slabs past
+        // the part read scales that are never used (a dead block's empty
+        // resource reads zeros).
+        if constexpr (GM == 1) {
             const int slc = min(sl, nslabs - 1);
 #pragma unroll
             for (int f = 0; f < FN; ++f)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = min(4 * g + r, nrows[f] - 1);
-                    if constexpr (GM == 2)
-                        sc[s][f][r] = __builtin_amdgcn_raw_buffer_load_b32(
-                            sr[f], (row * ngroups + 2 * slc) * 2, 0, 0);
-                    else
-                        sc[s][f][r] = __builtin_amdgcn_raw_buffer_load_b16(
-                            sr[f], (row * ngroups + slc) * 2, 0, 0);
+                    sc[s][f][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                        sr[f], (row * ngroups + slc) * 2, 0, 0);
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -290,21 +319,40 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
             acc[f][th] = tot[f][th] = zero4;
 
     // Vector memory ops issued after this wave's last code load of slab j
-    // when step j starts: slab j's scale loads, then the x DMAs, code and
+    // (slot s) when step j starts: slab j's scale loads (groups of 256), then
+    // the x DMAs, scale DMAs (groups of 128, a round's first slab), code and
     // scale loads of slabs j+1 .. j+kAhead-1.
-    constexpr int kAfter = FN * NSC + (kAhead - 1) * (XW + FN + FN * NSC);
-    static_assert(kAfter <= 63, "vmcnt range");
+    constexpr auto kAfter = [](int s) constexpr {
+        int n = GM == 1 ? 4 * FN : 0;
+        for (int i = 1; i < kAhead; ++i)
+            n += XW + FN + (GM == 1 ? 4 * FN : (GM == 2 && (s + i) % kS == 0 ? FN : 0));
+        return n;
+    };
+    static_assert(kAfter(0) <= 63 && kAfter(1) <= 63 && kAfter(2) <= 63 && kAfter(3) <= 63,
+                  "vmcnt range");
 
     // One step: slab j from slot / stage s.
-    auto step = [&](auto SL, int j) {
+    auto step = [&](auto SL, int j) __attribute__((always_inline)) {
         constexpr int s = decltype(SL)::value;
         // This wave's codes of slab j have landed, and with them (issued
         // earlier, returned in order) its x DMAs of slab j; after the barrier
         // every wave's have, and every wave is done with stage s - 1.
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<kAfter>();
+        wait_vm<kAfter(s)>();
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GM == 2 && s == 0) {
+            // the round's scales, before the next round's DMA reuses the
+            // buffer: slab i is the DMA's slab i + shift (past the row's end
+            // only for dead slabs, which take the last one's scales)
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = min(i + sq_shift, 3);
+                    sq[f][i] = *(const lds_u4 *)(sqs + (wave * FN + f) * 64 + k * 16 + 4 * g);
+                }
+        }
         issue(std::integral_constant<int, (s + kAhead) % kS>{}, j + kAhead);
 
         f32x4_t part[FN][CF];
@@ -343,17 +391,23 @@ __global__ void __launch_bounds__(kThreads) few_kernel(const FewBatch batch)
                 for (int c = 0; c < CF; ++c)
                     acc[f][c] = part[f][c];
             } else {
+                u32x4_t sv = {0u, 0u, 0u, 0u};
+                if constexpr (GM == 2)
+                    sv = sq[f][s];
 #pragma unroll
                 for (int c = 0; c < CF; ++c)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         uint32_t h;
-                        if constexpr (GM == 1)
+                        if constexpr (GM == 1) {
                             h = sc[s][f][r];
-                        else if constexpr (MT == 16)
-                            h = c ? sc[s][f][r] >> 16 : sc[s][f][r];
-                        else
-                            h = (col >> 3) ? sc[s][f][r] >> 16 : sc[s][f][r];
+                        } else {
+                            const uint32_t v = sv[r];
+                            if constexpr (MT == 16)
+                                h = c ? v >> 16 : v;
+                            else
+                                h = (col >> 3) ? v >> 16 : v;
+                        }
                         tot[f][GC == 1 ? c : 0][r] += f16_bits_to_f32((uint16_t)h) * part[f][c][r];
                     }
             }
@@ -581,8 +635,10 @@ hipError_t launch_policy(int gm, int mt, int kp, unsigned grid, hipStream_t stre
 bool gemm_few_takes(int64_t M, int64_t N, int64_t K, int group, const void *scale)
 {
     // 32-token tiles take one B column per token: per-channel scales and
-    // groups of 256; groups of 128 (two columns per token) stop at 16
-    return M >= 1 && M <= (group == 128 ? 16 : kFewMaxM) && N >= 1 && K >= 256 &&
+    // groups of 256; groups of 128 (two columns per token) stop at 16, and
+    // need four slabs per row (a round's scales are one 16-byte load)
+    return M >= 1 && M <= (group == 128 ? 16 : kFewMaxM) && N >= 1 &&
+           K >= (group == 128 ? 1024 : 256) &&
            K % 256 == 0 && K <= kGemvMaxK &&
            (group == 0 || group == 256 || (group == 128 && ((uintptr_t)scale & 3) == 0));
 }

@@ -100,7 +100,7 @@ bool gemv_valu_takes(int64_t M, int64_t K, int group, bool tiled);
 hipError_t launch_gemv_valu(const GemvArgs &a, bool fp16, hipStream_t stream);
 // Few-token streaming GEMM (gemm_few.hip): 1 <= M <= kFewMaxM (16 for groups
 // of 128), K % 256 == 0, K <= kGemvMaxK, per-channel scales or groups of 128
-// (4-byte aligned scale array) or 256; row-major and tiled codes.  One launch
+// (4-byte aligned scale array, K >= 1024) or 256; row-major and tiled codes.  One launch
 // for up to kGemvMaxBatch problems that share the scale mode and the token
 // tile (few_tile(M): 8, 16 or 32 tokens).
 constexpr int kFewMaxM = 32;

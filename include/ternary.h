@@ -117,8 +117,8 @@ typedef enum {
                                   only.  Never chosen by AUTO (measured slower); kept
                                   for comparison                                        */
     TERNARY_PATH_FEW = 7,      /* few-token streaming GEMM: 1 <= M <= 32 (16 for groups
-                                  of 128), K % 256 == 0, K <= 65536, per channel or
-                                  groups of 128 / 256; x
+                                  of 128), K % 256 == 0, K <= 65536 (groups of 128:
+                                  K >= 1024), per channel or groups of 128 / 256; x
                                   shared in LDS by the eight 16-channel blocks of a
                                   workgroup, codes streamed into registers             */
     TERNARY_PATH_GEMM_ZSKIP = 8 /* the pipelined GEMM skipping all-zero code blocks

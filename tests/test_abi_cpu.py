@@ -125,7 +125,8 @@ def _lin(tl, x=FAKE, dtype=0, M=1, N=16, K=128, p=FAKE * 2, s=FAKE * 3, g=128, y
     (dict(M=64, K=512, g=32, path=8), -8),    # the pipelined kernel's group sizes only
     (dict(M=64, K=512, g=128, s=FAKE * 3 + 2, path=8), -8),
     (dict(M=33, K=256, g=-1, path=7), -8),    # M <= 32
-    (dict(M=17, K=256, g=128, path=7), -8),   # group-128 scales: M <= 16
+    (dict(M=17, K=1024, g=128, path=7), -8),  # group-128 scales: M <= 16
+    (dict(M=9, K=768, g=128, path=7), -8),    # and K >= 1024
     (dict(K=256, g=64, path=7), -8),          # per channel, groups of 128 or 256
     (dict(K=256, g=32, path=7), -8),
     (dict(K=256, g=128, s=FAKE * 3 + 2, path=7), -8),  # group-128 scales 4-byte aligned
@@ -189,7 +190,7 @@ def test_quantize_reject(tl):
     # per channel or groups of 256, groups of 128 up to 16 tokens), else the GEMM
     (16, 4096, -1, "few"), (12, 4352, 256, "few"), (17, 4096, -1, "few"),
     (32, 18944, -1, "few"), (24, 4352, 256, "few"), (33, 4096, -1, "gemm"),
-    (16, 4096, 128, "few"), (17, 4096, 128, "gemm"),
+    (16, 4096, 128, "few"), (17, 4096, 128, "gemm"), (12, 768, 128, "gemm"), (12, 1024, 128, "few"),
     (9, 4096, 64, "gemm"), (9, 384, 128, "gemm"), (16, 65792, -1, "gemm"),
     (2048, 18944, -1, "gemm"), (1, 132, -1, "simple"), (64, 100, -1, "simple"),
     # long K up to 65536 stays on the GEMV at every M <= 8 (measured faster)

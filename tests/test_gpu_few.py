@@ -61,7 +61,7 @@ CASES = [
     (8, 33, 18944, -1, "bf16"),
     (8, 100, 4864, 128, "fp16"),
     (9, 200, 2048, -1, "bf16"),
-    (12, 61, 768, 128, "bf16"),
+    (12, 61, 1024, 128, "bf16"),
     (16, 1024, 5120, 128, "bf16"),
     (16, 96, 1024, -1, "fp16"),
     (16, 50, 7936, 256, "bf16"),
