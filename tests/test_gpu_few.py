@@ -65,6 +65,12 @@ CASES = [
     (16, 1024, 5120, 128, "bf16"),
     (16, 96, 1024, -1, "fp16"),
     (16, 50, 7936, 256, "bf16"),
+    # groups of 128, whose scales come a round of four slabs at a time: K
+    # ranges that end inside a round (the last round's DMA starts early),
+    # one block split over K parts and slices
+    (10, 40, 1792, 128, "fp16"),
+    (16, 16, 6400, 128, "bf16"),
+    (4, 23, 25600, 128, "bf16"),
     # 32-token tiles (one K part; per channel and groups of 256): ragged M
     # and N, a K long enough to slice over workgroups
     (17, 300, 2048, -1, "bf16"),
