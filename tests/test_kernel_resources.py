@@ -48,3 +48,16 @@ def test_decode_kernels_use_no_scratch():
     assert any("few_kernel" in k for k in kernels)
     spills = {k: v.get("ScratchSize") for k, v in kernels.items() if v.get("ScratchSize", 0) != 0}
     assert not spills, f"kernel instances with scratch: {spills}"
+
+
+@pytest.mark.skipif(not Path(HIPCC).exists(), reason="hipcc not available")
+def test_pipelined_gemm_uses_no_scratch():
+    # every instance the automatic choice can run (the zero-block-skipping
+    # ones, a forced path kept for measurement, are allowed to spill: their
+    # group-scaled instances do)
+    with tempfile.TemporaryDirectory() as d:
+        res = _resources("gemm.hip", d)
+    plain = {k: v for k, v in res.items() if "gemm_dma_kernel" in k and k.endswith("Lb0EEEvNS1_8BigBatchE")}
+    assert len(plain) >= 26, sorted(plain)
+    spills = {k: v.get("ScratchSize") for k, v in plain.items() if v.get("ScratchSize", 0) != 0}
+    assert not spills, f"pipelined GEMM instances with scratch: {spills}"
