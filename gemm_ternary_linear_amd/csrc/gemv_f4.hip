@@ -359,6 +359,9 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
     // group scales: this wave's staging area and this lane's row offset
     uint16_t *const gsb = reinterpret_cast<uint16_t *>(smem + L.gs_base) + wave * (kSP * G::GPS * 16);
     const int ngroups = GROUPED ? (K >> G::GLOG) : 1;
+    // groups of 128 or smaller come two to a 4-byte load when every such
+    // load is aligned and holds two groups of one row (a wave-uniform choice)
+    const bool pair_loads = GROUPED && (ngroups & 1) == 0 && ((uintptr_t)P.scale & 3) == 0;
     // group scales: the resource starts at the block's first row (64-bit
     // pointer arithmetic), so offsets stay below 16 rows of scales
     const __amdgpu_buffer_rsrc_t gsr =
@@ -394,12 +397,28 @@ __global__ void __launch_bounds__(kThreads) gemv_f4_kernel(const F4Batch batch)
             // stage the chunk's group scales: [local group][16 rows]
             constexpr int NG = kSP * G::GPS;
             const int g_first = ((s_begin + c0) * 256) >> G::GLOG;
+            if (G::GPS >= 2 && pair_loads) {
+                // two groups per 4-byte load: lane l takes row l & 15's pair
+                // (l >> 4) + 4 i, so a row's 16 lanes-worth of groups come in
+                // half the requests (g_first is even: a chunk is whole slabs)
 #pragma unroll
-            for (int i = 0; i < NG / 4; ++i) {
-                const int lg = (lane >> 4) + 4 * i, row = lane & 15;
-                const int gi = g_first + lg;
-                const int off = row < nrows && gi < ngroups ? (row * ngroups + gi) * 2 : kOOB;
-                gsb[lg * 16 + row] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(gsr, off, 0, 0);
+                for (int i = 0; i < NG / 8; ++i) {
+                    const int pr = (lane >> 4) + 4 * i, row = lane & 15;
+                    const int gi = g_first + 2 * pr;
+                    const int off = row < nrows && gi < ngroups ? (row * ngroups + gi) * 2 : kOOB;
+                    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(gsr, off, 0, 0);
+                    gsb[2 * pr * 16 + row] = (uint16_t)v;
+                    gsb[(2 * pr + 1) * 16 + row] = (uint16_t)(v >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NG / 4; ++i) {
+                    const int lg = (lane >> 4) + 4 * i, row = lane & 15;
+                    const int gi = g_first + lg;
+                    const int off = row < nrows && gi < ngroups ? (row * ngroups + gi) * 2 : kOOB;
+                    gsb[lg * 16 + row] =
+                        (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(gsr, off, 0, 0);
+                }
             }
             __builtin_amdgcn_wave_barrier();
         }

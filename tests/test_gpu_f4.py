@@ -157,3 +157,29 @@ def test_agrees_with_16bit_kernel_within_bound(tl):
                       to_dev(case.scale, torch.float16), -1, path=path)
         torch.cuda.synchronize()
         check_within(widen(bits_of(y), "bf16"), y_ref, bound, path)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_group_scales_any_alignment(tl, g, offset):
+    """Group scales are staged two to a 4-byte load when the scale array is
+    4-byte aligned, one per 2-byte load otherwise: both against the oracle,
+    with tiled and row-major codes, on a ragged block and more than one
+    chunk of slabs."""
+    import torch
+    say(f"f4 group scales g={g} offset={offset}")
+    M, N, K = 1, 45, 3072
+    rng = np.random.default_rng(977 + g + offset)
+    packed, _ = oracle.pack(synth.draw_codes(rng, N, K, 0.3, 0.3))
+    scale = synth.draw_scales(rng, N, K, g)
+    x = synth.draw_x(rng, M, K, "bf16")
+    y_ref, bound = oracle.linear(x, packed, scale, g, dtype="bf16")
+    sbuf = torch.zeros(scale.size + 8, dtype=torch.float16, device="cuda:0")
+    sd = sbuf[offset:offset + scale.size].view(scale.shape)
+    sd.copy_(to_dev(scale, torch.float16))
+    xd = to_dev(x, torch.bfloat16)
+    pd = to_dev(packed, None)
+    for lay, codes in (("rows", pd), ("tiled", tl.tile(pd))):
+        y = tl.linear(xd, codes, sd, g, path=PATH, layout=lay)
+        torch.cuda.synchronize()
+        check_within(widen(bits_of(y), "bf16"), y_ref, bound, f"f4 g={g} offset={offset} {lay}")
